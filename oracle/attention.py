@@ -1,0 +1,217 @@
+"""MXFP8 attention, forward and backward (CPU oracle, test infrastructure only).
+
+Per (batch, head), as the pages describe it:
+  * [Blog], "1. End-to-End Block-Scaled GEMM Fusion": both S = Q K^T and P V
+    are products of MX-quantized operands.
+  * [Blog], "2. Synchronized Online Softmax with Dynamic Scaling": the softmax
+    runs in FP32 with the logits scaled by 1/sqrt(d_k) (the caller's
+    softmax_scale, sigma).
+  * [News], forward/backward paragraph: the FP32 softmax result P is converted
+    to MXFP8 before P V, its block scales computed from the row maximum that
+    the softmax already found; the backward quantizes Q, K and dO in square
+    [32, 32] blocks, recomputes P, and re-quantizes the gradient dS online in
+    transpose-invariant square blocks ([News], contributions paragraph);
+    dQ is reduced in FP16 under a static power-of-two scale.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * Log2-domain softmax with c = fl32(fl32(sigma) * fl32(log2 e)) and an
+    integer row frame M = ceil(fl32(max_j S_ij * c)); p = fl32(exp2(fl32(S c - M))).
+    A power-of-two frame leaves P's E4M3 codes independent of how a kernel
+    tiles the key axis (MX quantization commutes with scaling by 2**k), so
+    "reusing the max" gives a unique P-hat.
+  * P-hat: blocks of 32 keys per query, aligned at key 0.  Normalizer l is the
+    sum of the unquantized fp32 p.  O = (P-hat V-hat) / l.  LSE = ln2 (M + log2 l).
+  * V enters P V with its blocks along the key axis (the contraction axis).
+  * Backward: p = fl32(exp2(fl32(S' c - fl32(LSE * fl32(log2 e))))) from the
+    forward's LSE; D_i = fl32(sum_d dO_id O_id) from the unquantized dO and O;
+    dS = fl32(p * fl32(dP - D)); dS-hat in [32 queries x 32 keys] blocks;
+    P-hat for dV = P^T dO in blocks of 32 queries per key; dK, dQ carry sigma.
+  * Causal masking keeps keys j <= i (queries and keys have equal length).
+fl32 marks one rounding to float32; every sum is float64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import mx
+
+LOG2E32 = float(np.float32(math.log2(math.e)))
+
+
+def fl32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def log2_scale(sigma: float) -> float:
+    """c = fl32(fl32(sigma) * fl32(log2 e))."""
+    return float(fl32(float(np.float32(sigma)) * LOG2E32))
+
+
+def visible(Lq: int, Lk: int, causal: bool) -> np.ndarray:
+    if not causal:
+        return np.ones((Lq, Lk), dtype=bool)
+    return np.arange(Lk)[None, :] <= np.arange(Lq)[:, None]
+
+
+# ----------------------------------------------------------------- forward
+def forward_head(q, k, v, sigma, causal, quantize=True, exact=False):
+    """One (batch, head): q, k, v are [L, D] source values (fp32 or bf16 upcast).
+
+    Returns a dict with O [L, D] (float64, before the output cast), LSE [L]
+    (float64), the integer frame M, the normalizer l and the P-hat codes.
+    ``quantize=False`` skips every MX step; ``exact=True`` skips every fp32
+    rounding (used only to pin the oracle to textbook attention).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
+    if quantize:
+        qh = mx.dequantize_row32(*mx.quantize_row32(q))
+        kh = mx.dequantize_row32(*mx.quantize_row32(k))
+        vh = mx.dequantize_col32(*mx.quantize_col32(v, axis=0), axis=0)
+    else:
+        qh, kh, vh = q, k, v
+    c = sigma * math.log2(math.e) if exact else log2_scale(sigma)
+    S = r(qh @ kh.T)
+    vis = visible(q.shape[0], k.shape[0], causal)
+    Smax = np.max(np.where(vis, S, -np.inf), axis=1)
+    M = np.ceil(r(Smax * c))
+    p = r(np.exp2(r(S * c - M[:, None])))
+    p = np.where(vis, p, 0.0)
+    l = p.sum(axis=1)
+    if quantize:
+        pc, pk = mx.quantize_col32(p, axis=1)           # 32 keys per block, per query
+        ph = mx.dequantize_col32(pc, pk, axis=1)
+    else:
+        pc, pk, ph = None, None, p
+    O = (ph @ vh) / l[:, None]
+    LSE = math.log(2.0) * (M + np.log2(l))
+    return {"O": O, "LSE": LSE, "M": M, "l": l, "P_codes": pc, "P_scales": pk, "S": S}
+
+
+# ---------------------------------------------------------------- backward
+def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False):
+    """One (batch, head) backward.  o, do: [L, D] (the forward output as the
+    caller holds it, and the incoming gradient); lse: [L] (fp32 values).
+
+    Returns float64 dQ, dK, dV [L, D] and the internals (p, dS, D).
+    """
+    q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
+    if quantize:
+        qs = mx.dequantize_sq32(*mx.quantize_sq32(q, 0), 0)
+        ks = mx.dequantize_sq32(*mx.quantize_sq32(k, 0), 0)
+        dos = mx.dequantize_sq32(*mx.quantize_sq32(do, 0), 0)
+        vr = mx.dequantize_row32(*mx.quantize_row32(v))
+    else:
+        qs, ks, dos, vr = q, k, do, v
+    if exact:
+        c, L2 = sigma * math.log2(math.e), lse * math.log2(math.e)
+    else:
+        c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
+    vis = visible(q.shape[0], k.shape[0], causal)
+    S = r(qs @ ks.T)
+    p = np.where(vis, r(np.exp2(r(S * c - L2[:, None]))), 0.0)
+    dP = r(dos @ vr.T)
+    Dv = r(np.sum(do * o, axis=1))
+    dS = np.where(vis, r(p * r(dP - Dv[:, None])), 0.0)
+    if quantize:
+        dSh = mx.dequantize_sq32(*mx.quantize_sq32(dS, 0), 0)   # [32 q x 32 k] blocks
+        pb = mx.dequantize_col32(*mx.quantize_col32(p, axis=0), axis=0)  # 32 queries per key
+    else:
+        dSh, pb = dS, p
+    dV = pb.T @ dos
+    dK = sigma * (dSh.T @ qs)
+    dQ = sigma * (dSh @ ks)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "p": p, "dS": dS, "D": Dv, "S": S, "dP": dP}
+
+
+# -------------------------------------------------------- textbook, float64
+def attention_fp64(q, k, v, sigma, causal):
+    """softmax(sigma q k^T) v in float64, no quantization; returns (O, LSE)."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    S = sigma * (q @ k.T)
+    S = np.where(visible(q.shape[0], k.shape[0], causal), S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    e = np.exp(S - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e / l) @ v, (m + np.log(l))[:, 0]
+
+
+def attention_fp64_backward(q, k, v, do, sigma, causal):
+    """Analytic gradients of attention_fp64 with respect to q, k, v."""
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    S = sigma * (q @ k.T)
+    S = np.where(visible(q.shape[0], k.shape[0], causal), S, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P = P / P.sum(axis=1, keepdims=True)
+    dV = P.T @ do
+    dP = do @ v.T
+    dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+    return sigma * (dS @ k), sigma * (dS.T @ q), dV
+
+
+# ------------------------------------------------------- whole-tensor views
+def _heads(x, cu_seqlens):
+    """Yield (key, [L, D] view) per (batch, head) or (sequence, head)."""
+    if cu_seqlens is None:
+        B, S, H, D = x.shape
+        for b in range(B):
+            for h in range(H):
+                yield (b, h), x[b, :, h, :]
+    else:
+        T, H, D = x.shape
+        for s in range(len(cu_seqlens) - 1):
+            for h in range(H):
+                yield (s, h), x[cu_seqlens[s]:cu_seqlens[s + 1], h, :]
+
+
+def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None):
+    """Forward over [B, S, H, D] (or packed [T, H, D] with cu_seqlens).
+
+    Returns O (float64, q's shape) and LSE ([B, H, S] or [H, T], float64).
+    """
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    O = np.zeros_like(q)
+    if cu_seqlens is None:
+        LSE = np.zeros((q.shape[0], q.shape[2], q.shape[1]))
+    else:
+        LSE = np.zeros((q.shape[1], q.shape[0]))
+    ks, vs = dict(_heads(k, cu_seqlens)), dict(_heads(v, cu_seqlens))
+    for key, qh in _heads(q, cu_seqlens):
+        if qh.shape[0] == 0:
+            continue
+        res = forward_head(qh, ks[key], vs[key], sigma, causal)
+        a, h = key
+        if cu_seqlens is None:
+            O[a, :, h, :] = res["O"]
+            LSE[a, h, :] = res["LSE"]
+        else:
+            O[cu_seqlens[a]:cu_seqlens[a + 1], h, :] = res["O"]
+            LSE[h, cu_seqlens[a]:cu_seqlens[a + 1]] = res["LSE"]
+    return O, LSE
+
+
+def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None):
+    """Backward over whole tensors; lse is [B, H, S] (or [H, T]).  Returns float64 dQ, dK, dV."""
+    q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    K, V, Oh, DOh = (dict(_heads(t, cu_seqlens)) for t in (k, v, o, do))
+    for key, qh in _heads(q, cu_seqlens):
+        if qh.shape[0] == 0:
+            continue
+        a, h = key
+        if cu_seqlens is None:
+            lh = lse[a, h, :]
+            sl = (a, slice(None), h, slice(None))
+        else:
+            lh = lse[h, cu_seqlens[a]:cu_seqlens[a + 1]]
+            sl = (slice(cu_seqlens[a], cu_seqlens[a + 1]), h, slice(None))
+        res = backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal)
+        dQ[sl], dK[sl], dV[sl] = res["dQ"], res["dK"], res["dV"]
+    return dQ, dK, dV
