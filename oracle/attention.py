@@ -27,7 +27,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
     dS = fl32(p * fl32(dP - D)); dS-hat in [32 queries x 32 keys] blocks;
     P-hat for dV = P^T dO in blocks of 32 queries per key; dK, dQ carry sigma.
   * Causal masking keeps keys j <= i (queries and keys have equal length).
-fl32 marks one rounding to float32; every sum is float64.
+  * The products whose values decide MX codes (S in the forward; S' and dP
+    in the backward) accumulate as gfx950's block-scaled fp8 instruction
+    does (``gemm="mfma"``, see oracle/gemm.py): the pages leave the MMA's
+    internal precision open, and a code decided from S must be decided in
+    the kernel's precision.  ``gemm="exact"`` gives the plain fl32(exact sum).
+fl32 marks one rounding to float32; every other sum is float64.
 """
 from __future__ import annotations
 
@@ -35,6 +40,7 @@ import math
 
 import numpy as np
 
+from . import gemm as gm
 from . import mx
 
 LOG2E32 = float(np.float32(math.log2(math.e)))
@@ -56,27 +62,38 @@ def visible(Lq: int, Lk: int, causal: bool) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- forward
-def forward_head(q, k, v, sigma, causal, quantize=True, exact=False):
+def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None, gemm="mfma"):
     """One (batch, head): q, k, v are [L, D] source values (fp32 or bf16 upcast).
 
     Returns a dict with O [L, D] (float64, before the output cast), LSE [L]
     (float64), the integer frame M, the normalizer l and the P-hat codes.
     ``quantize=False`` skips every MX step; ``exact=True`` skips every fp32
     rounding (used only to pin the oracle to textbook attention).
+    ``q_rows`` (optional index array) computes only those query rows; every
+    step is row-wise, so each returned row equals the full computation's.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
     if quantize:
-        qh = mx.dequantize_row32(*mx.quantize_row32(q))
-        kh = mx.dequantize_row32(*mx.quantize_row32(k))
+        qc, qk = mx.quantize_row32(q)
+        kc, kk = mx.quantize_row32(k)
+        qh, kh = mx.dequantize_row32(qc, qk), mx.dequantize_row32(kc, kk)
+        qe, ke = mx.element_exponent_row32(qc, qk), mx.element_exponent_row32(kc, kk)
         vh = mx.dequantize_col32(*mx.quantize_col32(v, axis=0), axis=0)
     else:
         qh, kh, vh = q, k, v
     c = sigma * math.log2(math.e) if exact else log2_scale(sigma)
-    S = r(qh @ kh.T)
     vis = visible(q.shape[0], k.shape[0], causal)
+    if q_rows is not None:
+        qh, vis = qh[q_rows], vis[q_rows]
+        if quantize:
+            qe = qe[q_rows]
+    if quantize and not exact and gemm == "mfma":
+        S = gm.matmul_mfma(qh, qe, kh, ke)
+    else:
+        S = r(qh @ kh.T)
     Smax = np.max(np.where(vis, S, -np.inf), axis=1)
     M = np.ceil(r(Smax * c))
     p = r(np.exp2(r(S * c - M[:, None])))
@@ -93,7 +110,7 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False):
 
 
 # ---------------------------------------------------------------- backward
-def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False):
+def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False, gemm="mfma"):
     """One (batch, head) backward.  o, do: [L, D] (the forward output as the
     caller holds it, and the incoming gradient); lse: [L] (fp32 values).
 
@@ -103,20 +120,23 @@ def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False
     lse = np.asarray(lse, np.float64)
     r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
     if quantize:
-        qs = mx.dequantize_sq32(*mx.quantize_sq32(q, 0), 0)
-        ks = mx.dequantize_sq32(*mx.quantize_sq32(k, 0), 0)
-        dos = mx.dequantize_sq32(*mx.quantize_sq32(do, 0), 0)
-        vr = mx.dequantize_row32(*mx.quantize_row32(v))
+        (qc, qk), (kc, kk), (dc, dk_) = mx.quantize_sq32(q, 0), mx.quantize_sq32(k, 0), mx.quantize_sq32(do, 0)
+        vc, vk = mx.quantize_row32(v)
+        qs, ks, dos = mx.dequantize_sq32(qc, qk, 0), mx.dequantize_sq32(kc, kk, 0), mx.dequantize_sq32(dc, dk_, 0)
+        vr = mx.dequantize_row32(vc, vk)
+        qe, ke, de = (mx.element_exponent_sq32(c_, k_, 0) for c_, k_ in ((qc, qk), (kc, kk), (dc, dk_)))
+        ve = mx.element_exponent_row32(vc, vk)
     else:
         qs, ks, dos, vr = q, k, do, v
+    use_mfma = quantize and not exact and gemm == "mfma"
     if exact:
         c, L2 = sigma * math.log2(math.e), lse * math.log2(math.e)
     else:
         c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
     vis = visible(q.shape[0], k.shape[0], causal)
-    S = r(qs @ ks.T)
+    S = gm.matmul_mfma(qs, qe, ks, ke) if use_mfma else r(qs @ ks.T)
     p = np.where(vis, r(np.exp2(r(S * c - L2[:, None]))), 0.0)
-    dP = r(dos @ vr.T)
+    dP = gm.matmul_mfma(dos, de, vr, ve) if use_mfma else r(dos @ vr.T)
     Dv = r(np.sum(do * o, axis=1))
     dS = np.where(vis, r(p * r(dP - Dv[:, None])), 0.0)
     if quantize:

@@ -69,6 +69,13 @@ def e4m3_encode(y) -> np.ndarray:
     return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
+def e4m3_exponent(codes) -> np.ndarray:
+    """Binary exponent of an E4M3FN code's significand: E - 7 for normals, -6 for
+    subnormals and zero (the format's fixed subnormal exponent)."""
+    E = (np.asarray(codes).astype(np.int64) >> 3) & 0xF
+    return np.where(E == 0, -6, E - 7)
+
+
 def e8m0_value(k) -> np.ndarray:
     """E8M0 byte -> 2**(k - 127) (255 is NaN)."""
     k = np.asarray(k).astype(np.int64)
@@ -103,6 +110,28 @@ def quantize_blocks(x) -> tuple[np.ndarray, np.ndarray]:
 
 def dequantize_blocks(codes, k) -> np.ndarray:
     return e4m3_decode(codes) * e8m0_value(k)[..., None]
+
+
+def element_exponent_row32(codes, k):
+    """Per-element exponent (E4M3 exponent + scale exponent) for ROW32 codes."""
+    codes = np.asarray(codes)
+    e = e4m3_exponent(codes)
+    D = codes.shape[-1]
+    ks = np.repeat(np.asarray(k).astype(np.int64) - E8M0_BIAS, BLOCK, axis=-1)[..., :D]
+    return e + ks
+
+
+def element_exponent_col32(codes, k, axis: int):
+    ks = np.repeat(np.asarray(k).astype(np.int64) - E8M0_BIAS, BLOCK, axis=axis)
+    ks = np.take(ks, np.arange(np.asarray(codes).shape[axis]), axis=axis)
+    return e4m3_exponent(codes) + ks
+
+
+def element_exponent_sq32(codes, k, axis_pos: int):
+    ks = np.repeat(np.repeat(np.asarray(k).astype(np.int64) - E8M0_BIAS, BLOCK, axis=axis_pos), BLOCK, axis=-1)
+    ks = np.take(ks, np.arange(np.asarray(codes).shape[axis_pos]), axis=axis_pos)
+    ks = np.take(ks, np.arange(np.asarray(codes).shape[-1]), axis=-1)
+    return e4m3_exponent(codes) + ks
 
 
 def _pad_to(x: np.ndarray, axis: int, mult: int) -> np.ndarray:
