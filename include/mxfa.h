@@ -1,0 +1,235 @@
+/*
+ * mxfa.h -- MXFP8 block-scaled attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels: MX quantization, the fused MXFP8
+ * attention forward, and the fused MXFP8 attention backward, each with a
+ * fixed-length and a jagged (varlen) form.
+ *
+ * Pages cited (by title):
+ *   [News]  "Low Precision Flash Attention 4: End-to-End Block-Scaled
+ *           Attention for Blackwell"
+ *   [Blog]  "Low-Precision FlashAttention-4: End-to-End Block-Scaled
+ *           Attention for NVIDIA Blackwell"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * MX format ([Blog], "Understanding OCP MXFP8 Microscaling on Blackwell"):
+ *   blocks of 32 elements share one E8M0 scale byte k (value 2^(k-127));
+ *   each element is one OCP E4M3FN byte (bias 7, max 448, 0x7F/0xFF NaN).
+ *   The scale of a block is k = clamp(floor(log2(amax)) - 8 + 127, 0, 254)
+ *   (OCP MX rule; k = 0 for an all-zero block); elements are encoded as
+ *   E4M3(x * 2^(127-k)) rounded to nearest even and saturated to +-448.
+ *
+ * Tensors are dense and row-major.  Fixed-length activations are
+ *   [B, S, H, D] (D contiguous), the shape of the pages' attention call
+ *   ([Blog], "PyTorch Integration & Implementation Example").  Jagged
+ *   activations are packed [T, H, D]; sequence s occupies tokens
+ *   cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ *
+ * An MX tensor is a payload (uint8, same shape and index as the source
+ * element: the FP8 data stays at its unpadded position, [News],
+ * contributions paragraph) plus a scale tensor in one of three layouts:
+ *   MX_ROW32  blocks of 32 consecutive features of one token.
+ *             scales [B, S, H, D/32]        (varlen: [Tpad, H, D/32])
+ *   MX_COL32  blocks of 32 consecutive tokens of one feature (blocked from
+ *             the sequence start; the last block may be short).
+ *             scales [B, ceil(S/32), H, D]  (varlen: [Tpad/32, H, D])
+ *   MX_SQ32   square blocks of 32 tokens x 32 features.  The payload is the
+ *             same whichever axis is contracted ([News], forward/backward
+ *             paragraph).
+ *             scales [B, ceil(S/32), H, D/32] (varlen: [Tpad/32, H, D/32])
+ * Varlen scale tensors are padded per sequence to 128-row boundaries
+ * ([News], contributions paragraph: only the scales are scattered and
+ * padded, to 128-aligned addresses): sequence s owns scale rows
+ * cu_scale_rows[s] .. cu_scale_rows[s+1]-1 (ROW32) or
+ * cu_scale_rows[s]/32 .. (COL32, SQ32), where cu_scale_rows is the prefix
+ * sum of roundup(L_s, 128) (see mx_varlen_scale_offsets).  Pad slots are
+ * written as 0.
+ *
+ * Memory and streams: every pointer argument is device memory owned by the
+ * caller unless stated otherwise; the library never allocates or frees and
+ * keeps no pointer after the call returns (kernels queued on `stream` still
+ * use them).  Every call is asynchronous on `stream` (0 = the null stream)
+ * and does not synchronise the host.  Device pointers must be 16-byte
+ * aligned.  The library holds no state and may be called from any thread.
+ *
+ * Errors: arguments are validated on the host before anything is launched;
+ * an invalid call returns MX_EINVAL (or MX_EWORKSPACE) and launches nothing.
+ * A device that is not gfx950 gives MX_EUNSUPPORTED; a failed launch gives
+ * MX_EHIP.  Non-finite inputs are outside the contract: results are then
+ * unspecified, but no call faults.  Integer device inputs (cu_seqlens,
+ * cu_scale_rows) must be consistent with the host sizes passed beside them;
+ * this is the caller's responsibility (the device does not validate them).
+ */
+#ifndef MXFA_H
+#define MXFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFA_ABI_VERSION 1
+
+typedef enum {
+  MX_OK = 0,
+  MX_EINVAL = 1,        /* bad argument (shape, pointer, alignment, dtype) */
+  MX_EUNSUPPORTED = 2,  /* device is not gfx950, or an unsupported combination */
+  MX_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+  MX_EWORKSPACE = 4     /* workspace pointer null or too small */
+} mx_status;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1, MX_F16 = 2 } mx_dtype;
+
+enum { MX_ROW32 = 1, MX_COL32 = 2, MX_SQ32 = 4 };
+
+/* ABI version (MXFA_ABI_VERSION) and a static string for a status code. */
+int mx_abi_version(void);
+const char* mx_status_str(mx_status s);
+
+/*
+ * mx_quantize -- MX quantization of a [B, S, H, D] tensor in one pass.
+ * Defines: the MX block format of [Blog], "Understanding OCP MXFP8
+ * Microscaling on Blackwell", with the dual/multiple scale layouts written
+ * in one pass of [News], contributions paragraph.
+ *   x          input, x_dtype MX_BF16 or MX_F32, [B, S, H, D]
+ *   D          64 or 128; S >= 0 (any value; COL32/SQ32 tail blocks short)
+ *   layouts    nonzero bitmask of MX_ROW32 | MX_COL32 | MX_SQ32
+ *   *_data     payload [B, S, H, D] uint8 for each requested layout
+ *   *_scale    scales in that layout's shape (see above)
+ * Buffers of layouts not requested are ignored and may be NULL.
+ */
+mx_status mx_quantize(const void* x, mx_dtype x_dtype, int B, int S, int H, int D,
+                      unsigned layouts,
+                      uint8_t* row32_data, uint8_t* row32_scale,
+                      uint8_t* col32_data, uint8_t* col32_scale,
+                      uint8_t* sq32_data, uint8_t* sq32_scale,
+                      hipStream_t stream);
+
+/*
+ * mx_varlen_scale_offsets -- cu_scale_rows[s] = sum_{u<s} roundup(L_u, 128)
+ * from cu_seqlens (both device int32 arrays of nseq+1 entries).
+ * Defines: the 128-aligned scale placement of jagged tensors, [News],
+ * contributions paragraph.  One tiny kernel; nseq >= 1.
+ */
+mx_status mx_varlen_scale_offsets(const int32_t* cu_seqlens, int nseq, int32_t* cu_scale_rows,
+                                  hipStream_t stream);
+
+/*
+ * mx_quantize_varlen -- mx_quantize for a packed [T, H, D] tensor.
+ *   cu_seqlens, cu_scale_rows   device int32 [nseq+1]
+ *   total_tokens                T = cu_seqlens[nseq]
+ *   total_scale_rows            Tpad = cu_scale_rows[nseq] (a multiple of 128)
+ * Blocks along tokens start at each sequence's first token; pad scale
+ * slots are written as 0.
+ */
+mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype,
+                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                             int total_tokens, int total_scale_rows, int H, int D,
+                             unsigned layouts,
+                             uint8_t* row32_data, uint8_t* row32_scale,
+                             uint8_t* col32_data, uint8_t* col32_scale,
+                             uint8_t* sq32_data, uint8_t* sq32_scale,
+                             hipStream_t stream);
+
+/*
+ * mx_attn_fwd -- fused MXFP8 attention forward.
+ * Defines: [Blog], "1. End-to-End Block-Scaled GEMM Fusion" (S = Q K^T and
+ * P V both on block-scaled operands, nothing written to HBM in between) and
+ * "2. Synchronized Online Softmax with Dynamic Scaling" (FP32 online
+ * softmax, logits scaled by softmax_scale); [News], forward/backward
+ * paragraph (P converted to MXFP8, its scales taken from the max the
+ * softmax already computed).
+ * Computation per (b, h), with c = fl32(softmax_scale * log2(e)):
+ *   S = Q^ K^T (Q^, K^ ROW32, exact-ish fp32 MFMA accumulation);
+ *   M_i = ceil(fl32(max_j S_ij * c)) (an integer frame);
+ *   p_ij = 2^(S_ij c - M_i) (fp32), l_i = sum_j p_ij;
+ *   P^ = MX(p) in blocks of 32 keys per query (aligned at key 0);
+ *   O = (P^ V^) / l  with V^ in COL32;  LSE_i = ln2 * (M_i + log2 l_i).
+ *   q_data, q_scale, k_data, k_scale   ROW32 payload + scales
+ *   v_data, v_scale                    COL32 payload + scales
+ *   D 64 or 128; S >= 1; causal keeps keys j <= i
+ *   o        [B, S, H, D], o_dtype MX_BF16 or MX_F32 (rounded to nearest even)
+ *   lse      [B, H, S] fp32, natural log; may be NULL
+ */
+mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale,
+                      const uint8_t* k_data, const uint8_t* k_scale,
+                      const uint8_t* v_data, const uint8_t* v_scale,
+                      int B, int S, int H, int D, float softmax_scale, int causal,
+                      void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * mx_attn_fwd_varlen -- mx_attn_fwd over packed sequences ([T, H, D]
+ * payloads, varlen scale layouts).  Causality is within each sequence.
+ * lse is [H, T].  max_seqlen bounds every L_s (host int).
+ */
+mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
+                             const uint8_t* k_data, const uint8_t* k_scale,
+                             const uint8_t* v_data, const uint8_t* v_scale,
+                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                             int total_tokens, int max_seqlen, int H, int D,
+                             float softmax_scale, int causal,
+                             void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * mx_attn_bwd_workspace_bytes -- device scratch mx_attn_bwd needs:
+ * an fp16 dQ accumulator [B, S, H, D] (or [T, H, D]) and D_i [B, H, S]
+ * fp32 (or [H, T]), each 256-byte aligned.  tokens = B*S or T.
+ */
+size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D);
+
+/*
+ * mx_attn_bwd -- fused MXFP8 attention backward.
+ * Defines: [News], forward/backward paragraph (Q, K, dO quantized in
+ * square [32, 32] blocks so one payload feeds both GEMMs; P recomputed;
+ * dQ reduced in FP16 under a static scale) and contributions paragraph
+ * (dS quantized online in transpose-invariant square blocks); [Blog],
+ * "3. Gradient Scale Recomputation in the Backward Pass".
+ * Computation per (b, h):
+ *   S' = Q^ K^T (SQ32 operands); p = 2^(S' c - fl32(LSE * log2 e));
+ *   dP = dO^ V^T (dO^ SQ32, V^ ROW32); D_i = sum_d dO_id O_id (fp32, from
+ *   the unquantized dout and o); dS = p (dP - D);
+ *   dS^ = MX(dS) in [32 query x 32 key] blocks; P^ = MX(p) in blocks of 32
+ *   queries per key;
+ *   dV = P^T dO^;  dK = softmax_scale * dS^T Q^;
+ *   dQ = softmax_scale * dS^ K^, reduced in fp16 as dQ * 2^dq_scale_log2
+ *   and written as acc * 2^-dq_scale_log2.
+ *   q_*, k_*, do_*   SQ32 payload + scales; v_* ROW32 payload + scales
+ *   o, dout          [B, S, H, D] in io_dtype (MX_BF16 or MX_F32)
+ *   lse              [B, H, S] fp32 from the forward
+ *   dq_scale_log2    in [-15, 15]
+ *   dq, dk, dv       [B, S, H, D] in grad_dtype (MX_BF16 or MX_F32)
+ *   workspace        >= mx_attn_bwd_workspace_bytes(B*S, H, D) bytes
+ */
+mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale,
+                      const uint8_t* k_data, const uint8_t* k_scale,
+                      const uint8_t* v_data, const uint8_t* v_scale,
+                      const uint8_t* do_data, const uint8_t* do_scale,
+                      const void* o, const void* dout, mx_dtype io_dtype, const float* lse,
+                      int B, int S, int H, int D, float softmax_scale, int causal,
+                      int dq_scale_log2,
+                      void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_attn_bwd_varlen -- mx_attn_bwd over packed sequences (lse [H, T]).
+ */
+mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
+                             const uint8_t* k_data, const uint8_t* k_scale,
+                             const uint8_t* v_data, const uint8_t* v_scale,
+                             const uint8_t* do_data, const uint8_t* do_scale,
+                             const void* o, const void* dout, mx_dtype io_dtype, const float* lse,
+                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                             int total_tokens, int max_seqlen, int H, int D,
+                             float softmax_scale, int causal, int dq_scale_log2,
+                             void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFA_H */

@@ -1,0 +1,254 @@
+"""Python binding of libmxfa (MXFP8 block-scaled attention for MI355X).
+
+Argument marshalling only: each ``mx_*`` function below has the name and the
+argument order of the C entry point in ``include/mxfa.h``, takes torch
+tensors where the C call takes device pointers, passes the current HIP stream,
+and raises :class:`MXError` on a non-zero status.  Every step of the
+computation runs in the HIP kernels of ``libmxfa.so``; there is no fallback.
+The ``alloc_*`` helpers only allocate output tensors of the documented shapes
+(PyTorch supplies device memory and streams).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+ROW32, COL32, SQ32 = 1, 2, 4
+F32, BF16, F16 = 0, 1, 2
+LAYOUT_NAMES = {ROW32: "row32", COL32: "col32", SQ32: "sq32"}
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfa.so")
+_lib = None
+
+_c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+_SIGS = {
+    "mx_abi_version": ([], _c_int),
+    "mx_status_str": ([_c_int], ctypes.c_char_p),
+    "mx_quantize": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
+    "mx_varlen_scale_offsets": ([_vp, _c_int, _vp, _vp], _c_int),
+    "mx_quantize_varlen": ([_vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint]
+                           + [_vp] * 6 + [_vp], _c_int),
+    "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
+    "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
+                           _c_int),
+    "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
+    "mx_attn_bwd": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
+                    + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
+    "mx_attn_bwd_varlen": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_vp, _vp] + [_c_int] * 5
+                           + [_c_float, _c_int, _c_int] + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
+}
+
+
+class MXError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfa.so (built by ``python -m mxfp8_block_scaled_flash_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m mxfp8_block_scaled_flash_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGS)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().mx_status_str(status).decode()
+        raise MXError(f"{what}: {msg}")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float16:
+        return F16
+    raise MXError(f"unsupported dtype {dt}")
+
+
+# --------------------------------------------------------------- raw entry points
+def mx_abi_version() -> int:
+    return lib().mx_abi_version()
+
+
+def mx_quantize(x, B, S, H, D, layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale,
+                stream=None):
+    _check(lib().mx_quantize(_ptr(x), _dtype_code(x.dtype), B, S, H, D, layouts, _ptr(row32_data),
+                             _ptr(row32_scale), _ptr(col32_data), _ptr(col32_scale), _ptr(sq32_data),
+                             _ptr(sq32_scale), _stream(stream)), "mx_quantize")
+
+
+def mx_varlen_scale_offsets(cu_seqlens, nseq, cu_scale_rows, stream=None):
+    _check(lib().mx_varlen_scale_offsets(_ptr(cu_seqlens), nseq, _ptr(cu_scale_rows), _stream(stream)),
+           "mx_varlen_scale_offsets")
+
+
+def mx_quantize_varlen(x, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows, H, D, layouts,
+                       row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale, stream=None):
+    _check(lib().mx_quantize_varlen(_ptr(x), _dtype_code(x.dtype), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq,
+                                    total_tokens, total_scale_rows, H, D, layouts, _ptr(row32_data),
+                                    _ptr(row32_scale), _ptr(col32_data), _ptr(col32_scale), _ptr(sq32_data),
+                                    _ptr(sq32_scale), _stream(stream)), "mx_quantize_varlen")
+
+
+def mx_attn_fwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal, o, lse,
+                stream=None):
+    _check(lib().mx_attn_fwd(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                             _ptr(v_scale), B, S, H, D, float(softmax_scale), int(bool(causal)), _ptr(o),
+                             _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd")
+
+
+def mx_attn_fwd_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seqlens, cu_scale_rows, nseq,
+                       total_tokens, max_seqlen, H, D, softmax_scale, causal, o, lse, stream=None):
+    _check(lib().mx_attn_fwd_varlen(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                                    _ptr(v_scale), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq, total_tokens,
+                                    max_seqlen, H, D, float(softmax_scale), int(bool(causal)), _ptr(o),
+                                    _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_varlen")
+
+
+def mx_attn_bwd_workspace_bytes(tokens, H, D) -> int:
+    return lib().mx_attn_bwd_workspace_bytes(tokens, H, D)
+
+
+def mx_attn_bwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse, B, S, H, D,
+                softmax_scale, causal, dq_scale_log2, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data), _ptr(v_scale),
+                             _ptr(do_data), _ptr(do_scale), _ptr(o), _ptr(dout), _dtype_code(o.dtype), _ptr(lse),
+                             B, S, H, D, float(softmax_scale), int(bool(causal)), int(dq_scale_log2), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _dtype_code(dq.dtype), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)), "mx_attn_bwd")
+
+
+def mx_attn_bwd_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse,
+                       cu_seqlens, cu_scale_rows, nseq, total_tokens, max_seqlen, H, D, softmax_scale, causal,
+                       dq_scale_log2, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd_varlen(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                                    _ptr(v_scale), _ptr(do_data), _ptr(do_scale), _ptr(o), _ptr(dout),
+                                    _dtype_code(o.dtype), _ptr(lse), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq,
+                                    total_tokens, max_seqlen, H, D, float(softmax_scale), int(bool(causal)),
+                                    int(dq_scale_log2), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq.dtype),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "mx_attn_bwd_varlen")
+
+
+# ------------------------------------------------------------ allocation helpers
+def scale_shape(layout: int, shape, total_scale_rows=None):
+    """Scale tensor shape for a payload of ``shape`` ([B,S,H,D] or varlen [T,H,D])."""
+    if len(shape) == 4:
+        B, S, H, D = shape
+        nb = (S + 31) // 32
+        return {ROW32: (B, S, H, D // 32), COL32: (B, nb, H, D), SQ32: (B, nb, H, D // 32)}[layout]
+    T, H, D = shape
+    Tp = total_scale_rows
+    return {ROW32: (Tp, H, D // 32), COL32: (Tp // 32, H, D), SQ32: (Tp // 32, H, D // 32)}[layout]
+
+
+def alloc_quantized(shape, layouts, device, total_scale_rows=None):
+    """Empty payload/scale tensors for every requested layout: {layout: (data, scale)}."""
+    out = {}
+    for lay in (ROW32, COL32, SQ32):
+        if layouts & lay:
+            data = torch.empty(shape, dtype=torch.uint8, device=device)
+            scale = torch.empty(scale_shape(lay, shape, total_scale_rows), dtype=torch.uint8, device=device)
+            out[lay] = (data, scale)
+    return out
+
+
+def quantize(x, layouts=ROW32 | COL32 | SQ32):
+    """One-pass MX quantization of a [B, S, H, D] tensor; returns {layout: (data, scale)}."""
+    B, S, H, D = x.shape
+    out = alloc_quantized(x.shape, layouts, x.device)
+    g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
+    mx_quantize(x, B, S, H, D, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0), g(COL32, 1), g(SQ32, 0),
+                g(SQ32, 1))
+    return out
+
+
+def padded_scale_rows(seqlens) -> int:
+    return int(sum((int(L) + 127) // 128 * 128 for L in seqlens))
+
+
+def quantize_varlen(x, cu_seqlens, seqlens, layouts=ROW32 | COL32 | SQ32):
+    """MX quantization of a packed [T, H, D] tensor; returns ({layout: (data, scale)}, cu_scale_rows)."""
+    T, H, D = x.shape
+    nseq = len(seqlens)
+    Tp = padded_scale_rows(seqlens)
+    csr = torch.empty(nseq + 1, dtype=torch.int32, device=x.device)
+    mx_varlen_scale_offsets(cu_seqlens, nseq, csr)
+    out = alloc_quantized(x.shape, layouts, x.device, Tp)
+    g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
+    mx_quantize_varlen(x, cu_seqlens, csr, nseq, T, Tp, H, D, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0),
+                       g(COL32, 1), g(SQ32, 0), g(SQ32, 1))
+    return out, csr
+
+
+def attn_fwd(q, k, v, softmax_scale, causal, out_dtype=torch.bfloat16, with_lse=True):
+    """q, k: (data, scale) ROW32; v: (data, scale) COL32.  Returns (O, LSE)."""
+    B, S, H, D = q[0].shape
+    o = torch.empty((B, S, H, D), dtype=out_dtype, device=q[0].device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q[0].device) if with_lse else None
+    mx_attn_fwd(q[0], q[1], k[0], k[1], v[0], v[1], B, S, H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal,
+                    out_dtype=torch.bfloat16, with_lse=True):
+    T, H, D = q[0].shape
+    o = torch.empty((T, H, D), dtype=out_dtype, device=q[0].device)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q[0].device) if with_lse else None
+    mx_attn_fwd_varlen(q[0], q[1], k[0], k[1], v[0], v[1], cu_seqlens, cu_scale_rows, len(seqlens), T,
+                       max(seqlens), H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, o, dout, lse, softmax_scale, causal, dq_scale_log2, grad_dtype=torch.bfloat16):
+    """q, k, do: (data, scale) SQ32; v: (data, scale) ROW32; o, dout: [B,S,H,D]; lse [B,H,S].
+    Returns (dQ, dK, dV)."""
+    B, S, H, D = q[0].shape
+    dev = q[0].device
+    dq, dk, dv = (torch.empty((B, S, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_workspace_bytes(B * S, H, D), dtype=torch.uint8, device=dev)
+    mx_attn_bwd(q[0], q[1], k[0], k[1], v[0], v[1], do[0], do[1], o, dout, lse, B, S, H, D, softmax_scale, causal,
+                dq_scale_log2, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q, k, v, do, o, dout, lse, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal,
+                    dq_scale_log2, grad_dtype=torch.bfloat16):
+    T, H, D = q[0].shape
+    dev = q[0].device
+    dq, dk, dv = (torch.empty((T, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_workspace_bytes(T, H, D), dtype=torch.uint8, device=dev)
+    mx_attn_bwd_varlen(q[0], q[1], k[0], k[1], v[0], v[1], do[0], do[1], o, dout, lse, cu_seqlens, cu_scale_rows,
+                       len(seqlens), T, max(seqlens), H, D, softmax_scale, causal, dq_scale_log2, dq, dk, dv, ws)
+    return dq, dk, dv

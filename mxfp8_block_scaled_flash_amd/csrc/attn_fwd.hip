@@ -1,0 +1,290 @@
+// Fused MXFP8 attention forward for gfx950.
+//
+// What is computed follows "Low-Precision FlashAttention-4: End-to-End
+// Block-Scaled Attention for NVIDIA Blackwell", sections "1. End-to-End
+// Block-Scaled GEMM Fusion" (S = Q K^T and P V on block-scaled operands, no
+// HBM round trip in between) and "2. Synchronized Online Softmax with Dynamic
+// Scaling" (FP32 running max and sum), and "Low Precision Flash Attention 4:
+// End-to-End Block-Scaled Attention for Blackwell", forward/backward
+// paragraph (the FP32 softmax result is converted to MXFP8, its block scales
+// taken from the maximum the softmax already holds).
+//
+// gfx950 design (not the pages' Blackwell design):
+//  * Each wavefront owns 32 queries and computes S^T = K Q^T with
+//    v_mfma_scale_f32_32x32x64_f8f6f4, so every lane holds one query and 16
+//    keys of each 32-key block: the row max needs one cross-lane step and the
+//    block scale of P is set per lane.
+//  * Softmax runs in the log2 domain under an integer frame M = ceil(max t),
+//    so rescaling O and l is an exact power of two and P's codes do not depend
+//    on how keys are tiled.
+//  * P's block amax is exp2(block max of t - M): one exp per block from the
+//    maxima already reduced for M.  The fp32->fp8 convert (which divides by
+//    the E8M0 scale) does not saturate, so values are clamped to 448*scale.
+//  * P is re-packed between lane halves with v_permlane32_swap so each lane
+//    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
+//    through ds_read_b64_tr_b8, in the same key order.
+//  * K and V tiles of 64 keys are staged in LDS and shared by the
+//    workgroup's waves.  Workgroups are ordered so that each XCD works
+//    through whole heads, longest (causal) query tiles first, keeping a
+//    head's K/V in that XCD's L2.
+#include "mx_common.h"
+#include "mx_launch.h"
+
+namespace mxk {
+
+template <int OA, int OB>
+MX_DEV v16f mfma32(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+
+MX_DEV v8i pack8(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+MX_DEV v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
+}
+
+template <int D, int NW, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+  constexpr int BM = 32 * NW;   // queries per workgroup
+  constexpr int BN = 64;        // keys per tile
+  constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
+  constexpr int ND = D / 32;    // 32-feature chunks of O
+  constexpr int KST = D + 16;   // LDS row stride of the K and V tiles
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
+  __shared__ uint32_t sKs[BN];   // K ROW32 scale bytes of each key
+  __shared__ uint32_t sVs[64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+
+  // ---- work decode: XCD x = id % 8 takes (sequence, head) units x, x+8, ...;
+  // within a unit, the longest query tile first.
+  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int u = (j / a.nqt) * 8 + xcd;
+  if (u >= a.nseq * a.H) return;
+  const int qt = a.nqt - 1 - (j % a.nqt);
+  const int h = u % a.H, s = u / a.H;
+  int tok0, L, srow0, sblk0;
+  a.seq.get(s, tok0, L, srow0, sblk0);
+  const int qbase = qt * BM;
+  if (qbase >= L) return;
+  const int q0 = qbase + 32 * w;
+  const int qi = q0 + n;
+  const long rowH = (long)a.H * D;
+
+  // ---- Q as the B operand (resident for the whole key loop)
+  v8i qa[NC];
+  uint32_t qsc = 0;
+  if (qi < L) {
+    const uint8_t* qp = a.q + (long)(tok0 + qi) * rowH + (long)h * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qa[c] = pack8(*(const uint4*)(qp + 64 * c + 16 * g), *(const uint4*)(qp + 64 * c + 32 + 16 * g));
+    const long srow = ((long)(srow0 + qi) * a.H + h);
+    uint32_t wq = (D == 128) ? *(const uint32_t*)(a.qs + srow * 4) : *(const uint16_t*)(a.qs + srow * 2);
+    qsc = wq >> (8 * g);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qa[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const int kend = CAUSAL ? min(L, qbase + BM) : L;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  v16f o[ND];
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc) o[dc] = v16f{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.c;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    // ---- stage K and V (payload rows of D bytes) and their scales
+    for (int ch = tid; ch < BN * D / 16; ch += NT) {
+      const int r = ch / (D / 16), cx = ch % (D / 16);
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (k0 + r < L) {
+        const long off = (long)(tok0 + k0 + r) * rowH + (long)h * D + cx * 16;
+        kv = *(const uint4*)(a.k + off);
+        vv = *(const uint4*)(a.v + off);
+      }
+      *(uint4*)(sK + r * KST + cx * 16) = kv;
+      *(uint4*)(sV + r * KST + cx * 16) = vv;
+    }
+    for (int r = tid; r < BN; r += NT) {
+      uint32_t wk = 0;
+      if (k0 + r < L) {
+        const long srow = ((long)(srow0 + k0 + r) * a.H + h);
+        wk = (D == 128) ? *(const uint32_t*)(a.ks + srow * 4) : *(const uint16_t*)(a.ks + srow * 2);
+      }
+      sKs[r] = wk;
+    }
+    for (int x = tid; x < 64; x += NT) {
+      const int b = x >> 5, rr = x & 31;
+      uint32_t wv = 0;
+      if ((2 * t + b) * 32 < L) {
+        const uint8_t* vp = a.vs + ((long)(sblk0 + 2 * t + b) * a.H + h) * D + rr;
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) wv |= (uint32_t)vp[32 * dc] << (8 * dc);
+      }
+      sVs[x] = wv;
+    }
+    __syncthreads();
+    if (q0 >= L) continue;
+    if (CAUSAL && k0 > q0 + 31) continue;   // tile entirely above this wave's diagonal
+
+    // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
+    v16f st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint8_t* kp = sK + (kb * 32 + n) * KST + 16 * g;
+      const uint32_t ksc = sKs[kb * 32 + n] >> (8 * g);
+      v16f acc = v16f{};
+      acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc, qsc);
+      if constexpr (NC > 1)
+        acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc, qsc);
+      st[kb] = acc;
+    }
+    const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= L || (CAUSAL && key > qi)) st[kb][i] = -INFINITY;
+        }
+    }
+    // ---- block maxima, frame update
+    float bm[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float m = st[kb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
+      bm[kb] = wave_max_xor(m, 32);
+    }
+    const float m_new = fmaxf(m_run, ceilf(fmaxf(bm[0], bm[1]) * c));
+    if (m_new > m_run) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_new));
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc) o[dc] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float negM = -m_run;
+    // ---- p = 2^(S c - M), running sum, P block scales from the block maxima
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
+        st[kb][i] = p;
+        psum += p;
+      }
+    l_run += psum;
+    int kc[2];
+    float sc[2], lim[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float amax = __builtin_amdgcn_exp2f(fmaf(bm[kb], c, negM));
+      kc[kb] = max(scale_code(amax), 1);
+      sc[kb] = e8m0_f32(kc[kb]);
+      lim[kb] = 448.f * sc[kb];
+    }
+    // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
+    uint32_t dw[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v2s z = {0, 0};
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q], lim[kb]), fminf(st[kb][4 * q + 1], lim[kb]),
+                                                     sc[kb], false);
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q + 2], lim[kb]), fminf(st[kb][4 * q + 3], lim[kb]),
+                                                     sc[kb], true);
+        dw[kb][q] = __builtin_bit_cast(uint32_t, z);
+      }
+    // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order
+    v8i pb;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
+      auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
+      pb[4 * kb + 0] = s02[0];
+      pb[4 * kb + 1] = s02[1];
+      pb[4 * kb + 2] = s13[0];
+      pb[4 * kb + 3] = s13[1];
+    }
+    const int psc = g ? kc[1] : kc[0];
+    const uint32_t vsc = sVs[lane];
+    // ---- O^T += V^T P^T, V^T rows d = 32 dc + lane%32, through LDS transpose reads
+    {
+      const int G = lane >> 4, i16 = lane & 15;
+      const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
+      const int rowofs = 16 * (G >> 1) + (i16 >> 1);
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc) {
+        const uint8_t* vp = sV + rowofs * KST + 32 * dc + colofs;
+        v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * KST), r2 = lds_tr8(vp + 32 * KST), r3 = lds_tr8(vp + 40 * KST);
+        v8i va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        if (dc == 0) o[0] = mfma32<0, 0>(va, pb, o[0], vsc, psc);
+        if (dc == 1) o[1] = mfma32<1, 0>(va, pb, o[1], vsc, psc);
+        if constexpr (ND > 2) {
+          if (dc == 2) o[2] = mfma32<2, 0>(va, pb, o[2], vsc, psc);
+          if (dc == 3) o[3] = mfma32<3, 0>(va, pb, o[3], vsc, psc);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, LSE = ln2 (M + log2 l).  Each lane half summed
+  // p over its 16 keys of every block: the row sum adds both halves.
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (qi >= L) return;
+  const float inv = 1.f / l_run;
+  const long orow = (long)(tok0 + qi) * rowH + (long)h * D;
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * dc + 8 * q + 4 * g;
+      const float v0 = o[dc][4 * q] * inv, v1 = o[dc][4 * q + 1] * inv, v2 = o[dc][4 * q + 2] * inv,
+                  v3 = o[dc][4 * q + 3] * inv;
+      if constexpr (OUT_BF16) {
+        uint2 pk = make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
+        *(uint2*)((uint16_t*)a.o + orow + d) = pk;
+      } else {
+        *(float4*)((float*)a.o + orow + d) = make_float4(v0, v1, v2, v3);
+      }
+    }
+  if (g == 0 && a.lse) {
+    const long li = a.seq.cu ? (long)h * a.T + tok0 + qi : ((long)s * a.H + h) * a.seq.S + qi;
+    a.lse[li] = 0.69314718055994531f * (m_run + log2f(l_run));
+  }
+}
+
+hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st) {
+  constexpr int NW = 4;
+  a.nqt = (max_len + 32 * NW - 1) / (32 * NW);
+  const long units = (long)a.nseq * a.H;
+  const long grid = ((units + 7) / 8) * 8 * a.nqt;
+  if (grid == 0) return hipSuccess;
+  dim3 g((unsigned)grid), b(NW * 64);
+#define MX_FWD_CASE(DD, CC, OB) \
+  if (D == DD && causal == CC && out_bf16 == OB) { attn_fwd_kernel<DD, NW, CC, OB><<<g, b, 0, st>>>(a); return hipGetLastError(); }
+  MX_FWD_CASE(64, false, false) MX_FWD_CASE(64, false, true) MX_FWD_CASE(64, true, false) MX_FWD_CASE(64, true, true)
+  MX_FWD_CASE(128, false, false) MX_FWD_CASE(128, false, true) MX_FWD_CASE(128, true, false) MX_FWD_CASE(128, true, true)
+#undef MX_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mxk

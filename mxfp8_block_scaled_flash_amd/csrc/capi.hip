@@ -1,0 +1,214 @@
+// Host side of the C ABI declared in include/mxfa.h: argument validation,
+// launch geometry and status codes.  Nothing here allocates device memory or
+// synchronises the host; every kernel goes onto the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/mxfa.h"
+#include "mx_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// gfx950 check, cached per device ordinal (0 unknown, 1 gfx950, 2 other).
+std::atomic<int> g_dev_ok[64];
+
+mx_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MX_EHIP;
+  if (dev < 0 || dev >= 64) return MX_EUNSUPPORTED;
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MX_EHIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MX_OK : MX_EUNSUPPORTED;
+}
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
+
+bool valid_layouts(unsigned layouts) { return layouts != 0 && (layouts & ~7u) == 0; }
+
+bool layout_ptrs_ok(unsigned layouts, uint8_t* rd, uint8_t* rs, uint8_t* cd, uint8_t* cs, uint8_t* sd,
+                    uint8_t* ss) {
+  if ((layouts & MX_ROW32) && !(rd && rs && aligned16(rd) && aligned16(rs))) return false;
+  if ((layouts & MX_COL32) && !(cd && cs && aligned16(cd) && aligned16(cs))) return false;
+  if ((layouts & MX_SQ32) && !(sd && ss && aligned16(sd) && aligned16(ss))) return false;
+  return true;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return false;
+  return true;
+}
+
+float log2_scale(float softmax_scale) { return softmax_scale * 1.44269504088896340736f; }
+
+constexpr long kMaxElems = 1L << 40;
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MXFA_ABI_VERSION; }
+
+const char* mx_status_str(mx_status s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_EINVAL: return "MX_EINVAL: invalid argument";
+    case MX_EUNSUPPORTED: return "MX_EUNSUPPORTED: unsupported device or combination";
+    case MX_EHIP: return "MX_EHIP: HIP runtime error";
+    case MX_EWORKSPACE: return "MX_EWORKSPACE: workspace missing or too small";
+  }
+  return "unknown mx_status";
+}
+
+mx_status mx_quantize(const void* x, mx_dtype x_dtype, int B, int S, int H, int D, unsigned layouts,
+                      uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
+                      uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+  if (B < 0 || S < 0 || H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  if (!valid_layouts(layouts)) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  if (!x || !aligned16(x)) return MX_EINVAL;
+  if (!layout_ptrs_ok(layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale))
+    return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  mxk::QuantArgs a{};
+  a.seq.cu = nullptr;
+  a.seq.csr = nullptr;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.H = H;
+  a.nseq = B;
+  a.nwaves = (long)B * a.seq.nblk * H;
+  a.layouts = layouts;
+  a.row_data = row32_data; a.row_scale = row32_scale;
+  a.col_data = col32_data; a.col_scale = col32_scale;
+  a.sq_data = sq32_data; a.sq_scale = sq32_scale;
+  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, a, stream));
+}
+
+mx_status mx_varlen_scale_offsets(const int32_t* cu_seqlens, int nseq, int32_t* cu_scale_rows, hipStream_t stream) {
+  if (nseq < 1 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_scale_offsets(cu_seqlens, nseq, cu_scale_rows, stream));
+}
+
+mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens, const int32_t* cu_scale_rows,
+                             int nseq, int total_tokens, int total_scale_rows, int H, int D, unsigned layouts,
+                             uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
+                             uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || total_scale_rows < 0 || total_scale_rows % 128 != 0) return MX_EINVAL;
+  if (total_scale_rows < total_tokens) return MX_EINVAL;
+  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  if (!valid_layouts(layouts)) return MX_EINVAL;
+  if (!cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if ((long)total_scale_rows * H * D > kMaxElems) return MX_EINVAL;
+  if (total_scale_rows == 0) return MX_OK;
+  if (total_tokens > 0 && (!x || !aligned16(x))) return MX_EINVAL;
+  if (!layout_ptrs_ok(layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale))
+    return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  mxk::QuantArgs a{};
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_scale_rows;
+  a.seq.S = 0;
+  a.seq.nblk = 0;
+  a.H = H;
+  a.nseq = nseq;
+  a.nwaves = (long)(total_scale_rows / 32) * H;
+  a.layouts = layouts;
+  a.row_data = row32_data; a.row_scale = row32_scale;
+  a.col_data = col32_data; a.col_scale = col32_scale;
+  a.sq_data = sq32_data; a.sq_scale = sq32_scale;
+  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, a, stream));
+}
+
+static mx_status fwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                            const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale, int H, int D,
+                            float softmax_scale, void* o, mx_dtype o_dtype, mxk::FwdArgs& a) {
+  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (o_dtype != MX_BF16 && o_dtype != MX_F32) return MX_EINVAL;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
+  if (!all_aligned({q_data, q_scale, k_data, k_scale, v_data, v_scale, o})) return MX_EINVAL;
+  a.q = q_data; a.qs = q_scale; a.k = k_data; a.ks = k_scale; a.v = v_data; a.vs = v_scale;
+  a.H = H;
+  a.c = log2_scale(softmax_scale);
+  a.o = o;
+  return MX_OK;
+}
+
+mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data, const uint8_t* k_scale,
+                      const uint8_t* v_data, const uint8_t* v_scale, int B, int S, int H, int D,
+                      float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  mxk::FwdArgs a{};
+  if (mx_status st = fwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, H, D, softmax_scale, o, o_dtype, a))
+    return st;
+  if (lse && !aligned16(lse)) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = nullptr;
+  a.seq.csr = nullptr;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.nseq = B;
+  a.T = B * S;
+  a.lse = lse;
+  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, a, S, stream));
+}
+
+mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                             int max_seqlen, int H, int D, float softmax_scale, int causal, void* o,
+                             mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
+  mxk::FwdArgs a{};
+  if (mx_status st = fwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, H, D, softmax_scale, o, o_dtype, a))
+    return st;
+  if (lse && !aligned16(lse)) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_scale_rows;
+  a.seq.S = 0;
+  a.seq.nblk = 0;
+  a.nseq = nseq;
+  a.T = total_tokens;
+  a.lse = lse;
+  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, a, max_seqlen, stream));
+}
+
+size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D) {
+  if (tokens < 0 || H < 1 || D < 1) return 0;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  return up((size_t)tokens * H * D * 2) + up((size_t)tokens * H * 4);
+}
+
+mx_status mx_attn_bwd(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*,
+                      const uint8_t*, const uint8_t*, const void*, const void*, mx_dtype, const float*, int, int, int,
+                      int, float, int, int, void*, void*, void*, mx_dtype, void*, size_t, hipStream_t) {
+  return MX_EUNSUPPORTED;
+}
+
+mx_status mx_attn_bwd_varlen(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*,
+                             const uint8_t*, const uint8_t*, const uint8_t*, const void*, const void*, mx_dtype,
+                             const float*, const int32_t*, const int32_t*, int, int, int, int, int, float, int, int,
+                             void*, void*, void*, mx_dtype, void*, size_t, hipStream_t) {
+  return MX_EUNSUPPORTED;
+}
+
+}  // extern "C"

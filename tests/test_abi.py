@@ -1,0 +1,88 @@
+"""The C-ABI library: it loads, exports every entry point the header
+declares, and rejects invalid arguments on the host before launching
+anything (these calls need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_flash_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfa.h")
+EINVAL, EWORKSPACE = 1, 4
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == mx.exported_symbols()
+
+
+def test_library_exports_every_declared_symbol():
+    L = mx.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.mx_abi_version() == 1
+    for s in range(5):
+        assert L.mx_status_str(s).decode().startswith("MX_")
+
+
+def _quant(**kw):
+    args = dict(x=16, dt=mx.BF16, B=1, S=32, H=1, D=128, lay=mx.ROW32, rd=16, rs=16, cd=None, cs=None, sd=None,
+                ss=None)
+    args.update(kw)
+    return mx.lib().mx_quantize(args["x"], args["dt"], args["B"], args["S"], args["H"], args["D"], args["lay"],
+                                args["rd"], args["rs"], args["cd"], args["cs"], args["sd"], args["ss"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(D=96), dict(D=0), dict(H=0), dict(B=-1), dict(S=-3), dict(lay=0),
+                                 dict(lay=8), dict(dt=mx.F16), dict(x=None), dict(x=24), dict(rd=None),
+                                 dict(rs=8), dict(lay=mx.COL32), dict(lay=mx.SQ32 | mx.ROW32)])
+def test_quantize_rejects_invalid_arguments(bad):
+    assert _quant(**bad) == EINVAL
+
+
+def test_empty_quantize_is_a_no_op():
+    assert _quant(B=0) == 0 and _quant(S=0) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=16, qs=16, k=16, ks=16, v=16, vs=16, B=1, S=64, H=1, D=128, sc=0.1, causal=1, o=16, odt=mx.BF16,
+             lse=None)
+    a.update(kw)
+    return mx.lib().mx_attn_fwd(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["B"], a["S"], a["H"], a["D"],
+                                a["sc"], a["causal"], a["o"], a["odt"], a["lse"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(D=32), dict(H=0), dict(S=-1), dict(sc=0.0), dict(sc=-1.0),
+                                 dict(sc=float("nan")), dict(sc=float("inf")), dict(odt=mx.F16), dict(o=None),
+                                 dict(q=None), dict(vs=4), dict(lse=4)])
+def test_forward_rejects_invalid_arguments(bad):
+    assert _fwd(**bad) == EINVAL
+
+
+def test_varlen_rejects_invalid_arguments():
+    L = mx.lib()
+    # total_scale_rows not a multiple of 128, and smaller than the token count
+    assert L.mx_quantize_varlen(16, mx.BF16, 16, 16, 1, 10, 100, 1, 128, 1, 16, 16, None, None, None, None,
+                                None) == EINVAL
+    assert L.mx_quantize_varlen(16, mx.BF16, 16, 16, 1, 300, 256, 1, 128, 1, 16, 16, None, None, None, None,
+                                None) == EINVAL
+    assert L.mx_quantize_varlen(16, mx.BF16, None, 16, 1, 10, 128, 1, 128, 1, 16, 16, None, None, None, None,
+                                None) == EINVAL
+    assert L.mx_varlen_scale_offsets(None, 1, 16, None) == EINVAL
+    assert L.mx_varlen_scale_offsets(16, 0, 16, None) == EINVAL
+    assert L.mx_attn_fwd_varlen(*([16] * 6), 16, 16, 0, 10, 10, 1, 128, ctypes.c_float(0.1), 1, 16, mx.BF16,
+                                None, None) == EINVAL
+
+
+def test_workspace_size():
+    n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
+    assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
+    assert mx.lib().mx_attn_bwd_workspace_bytes(-1, 3, 128) == 0
