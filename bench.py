@@ -1,0 +1,195 @@
+"""Benchmark of the MXFP8 attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = MX quantization of Q, K, V, dO in every layout the forward and
+backward consume, the fused forward, and the fused backward, on the
+synthetic LLM-shaped workload (B8 H32 S8192 D128, causal, bf16 N(0,1)
+inputs already resident in HBM).  Prints one JSON line.  Kernel durations
+come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MXFP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 / MXFP8 MFMA peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llm")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="time only quantize + forward")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, sigma):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the forward for 1024 query rows at the end of one (batch, head) (rows with
+    the most visible keys)."""
+    import numpy as np
+    import synth
+    from oracle import attention as at
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    b, h = synth.draw_sample_pairs(w.seed, w.B, w.H, 1)[0]
+    q, k, v = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v"))
+    rows = np.arange(w.S - 1024, w.S)
+    t0 = time.perf_counter()
+    at.forward_head(q, k, v, sigma, True, q_rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * float(np.sum(rows + 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"forward of 1024 query rows (S-1024..S-1) of (b={b}, h={h}) of the B8 H32 S8192 D128 causal "
+                      f"workload, {dt:.1f} s; numpy, elementwise work on 1 thread, BLAS on {threads}"}
+
+
+def _bwd_available(mx) -> bool:
+    """mx_attn_bwd returns MX_EUNSUPPORTED (2) in builds without the backward."""
+    st = mx.lib().mx_attn_bwd(*([None] * 12), 1, 32, 1, 128, 0.1, 1, 0, *([None] * 3), 1, None, 0, None)
+    return st != 2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the workload shards by "
+              "(batch, head) with no exchange, so N GPUs would each run this same kernel on B*H/N heads.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp8_block_scaled_flash_amd as mx
+    import synth
+
+    w = synth.workload(args.workload)
+    dev = "cuda"
+    if not args.no_bwd and mx.mx_attn_bwd_workspace_bytes(1, 1, 128) and not _bwd_available(mx):
+        print("note: this build's mx_attn_bwd is not available; timing quantize + forward only", file=sys.stderr)
+        args.no_bwd = True
+    B, S, H, D = w.B, w.S, w.H, w.D
+    sigma = 1.0 / math.sqrt(D)
+    x = {t: synth.tensor_torch(w, t, dev) for t in ("q", "k", "v", "do")}
+    do_bwd = not args.no_bwd
+    ROW, COL, SQ = mx.ROW32, mx.COL32, mx.SQ32
+    lay = {"q": ROW | SQ, "k": ROW | SQ, "v": COL | ROW, "do": SQ} if do_bwd else {"q": ROW, "k": ROW, "v": COL}
+    qz = {t: mx.alloc_quantized(x[t].shape, lay[t], dev) for t in lay}
+    o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    if do_bwd:
+        dq, dk, dv = (torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        ws = torch.empty(mx.mx_attn_bwd_workspace_bytes(B * S, H, D), dtype=torch.uint8, device=dev)
+
+    def g(t, l, i):
+        return qz[t][l][i] if l in qz[t] else None
+
+    def quantize_all():
+        for t in lay:
+            mx.mx_quantize(x[t], B, S, H, D, lay[t], g(t, ROW, 0), g(t, ROW, 1), g(t, COL, 0), g(t, COL, 1),
+                           g(t, SQ, 0), g(t, SQ, 1))
+
+    def forward():
+        mx.mx_attn_fwd(qz["q"][ROW][0], qz["q"][ROW][1], qz["k"][ROW][0], qz["k"][ROW][1], qz["v"][COL][0],
+                       qz["v"][COL][1], B, S, H, D, sigma, True, o, lse)
+
+    def backward():
+        mx.mx_attn_bwd(qz["q"][SQ][0], qz["q"][SQ][1], qz["k"][SQ][0], qz["k"][SQ][1], qz["v"][ROW][0],
+                       qz["v"][ROW][1], qz["do"][SQ][0], qz["do"][SQ][1], o, x["do"], lse, B, S, H, D, sigma, True,
+                       8, dq, dk, dv, ws)
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec):
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        quantize_all()
+        e[1].record(stream)
+        forward()
+        e[2].record(stream)
+        if do_bwd:
+            backward()
+        e[3].record(stream)
+        if rec is not None:
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t_start, t_end = ev(), ev()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(recs)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    q_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / len(recs)
+    f_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / len(recs)
+    b_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / len(recs) if do_bwd else 0.0
+    ms_step = total_ms / args.steps
+
+    pairs = B * H * S * (S + 1) / 2
+    f_flop = 4.0 * D * pairs
+    b_flop = 10.0 * D * pairs if do_bwd else 0.0
+    f_tflops = f_flop / (f_ms * 1e-3) / 1e12
+    b_tflops = b_flop / (b_ms * 1e-3) / 1e12 if do_bwd else None
+    value = (f_flop + b_flop) / (ms_step * 1e-3) / 1e12
+    # quantize: algorithmic bytes = bf16 read + per layout (payload + scales)
+    elems = B * S * H * D
+    per_layout = {ROW: 1 + 1 / 32, COL: 1 + 1 / 32, SQ: 1 + 1 / 1024}
+    q_bytes = sum(elems * (2 + sum(per_layout[l] for l in (ROW, COL, SQ) if lay[t] & l)) for t in lay)
+
+    if do_bwd:
+        dom = {"kernel": "mx_attn_bwd (all kernels of the call)", "ms": b_ms, "flop": b_flop}
+    else:
+        dom = {"kernel": "attn_fwd_kernel", "ms": f_ms, "flop": f_flop}
+    achieved = dom["flop"] / (dom["ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "MXFP8 attn TFLOP/s fwd & bwd, B8 H32 S8192 D128 causal; % of MXFP8 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"mxfp8 attention fwd+bwd B{B} H{H} S{S} D{D} causal bf16 N(0,1)",
+                   "B": B, "H": H, "S": S, "D": D, "causal": True},
+        "fwd_tflops": round(f_tflops, 2),
+        "fwd_pct_peak": round(100 * f_tflops / MXFP8_PEAK_TFLOPS, 2),
+        "bwd_tflops": round(b_tflops, 2) if b_tflops else None,
+        "bwd_pct_peak": round(100 * b_tflops / MXFP8_PEAK_TFLOPS, 2) if b_tflops else None,
+        "quantize_ms": round(q_ms, 4),
+        "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "fwd_ms": round(f_ms, 4),
+        "bwd_ms": round(b_ms, 4) if do_bwd else None,
+        "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),
+                     "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, sigma)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
