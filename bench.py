@@ -61,7 +61,7 @@ def cpu_baseline(w, sigma):
 
 def _bwd_available(mx) -> bool:
     """mx_attn_bwd returns MX_EUNSUPPORTED (2) in builds without the backward."""
-    st = mx.lib().mx_attn_bwd(*([None] * 12), 1, 32, 1, 128, 0.1, 1, 0, *([None] * 3), 1, None, 0, None)
+    st = mx.lib().mx_attn_bwd(*([None] * 10), 1, None, 1, 32, 1, 128, 0.1, 1, 0, None, None, None, 1, None, 0, None)
     return st != 2
 
 
