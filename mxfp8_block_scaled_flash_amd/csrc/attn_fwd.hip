@@ -17,8 +17,9 @@
 //  * Softmax runs in the log2 domain under an integer frame M = ceil(max t),
 //    so rescaling O and l is an exact power of two and P's codes do not depend
 //    on how keys are tiled.
-//  * P's block amax is exp2(block max of t - M): one exp per block from the
-//    maxima already reduced for M.  The fp32->fp8 convert (which divides by
+//  * P's block amax is 2^(block max of t - M), so its E8M0 scale follows
+//    from the maxima already reduced for M, with no extra exp (and no
+//    dependence on the accuracy of the hardware exp2).  The fp32->fp8 convert (which divides by
 //    the E8M0 scale) does not saturate, so values are clamped to 448*scale.
 //  * P is re-packed between lane halves with v_permlane32_swap so each lane
 //    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
@@ -102,6 +103,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   for (int dc = 0; dc < ND; ++dc) o[dc] = v16f{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.c;
+  uint32_t vsc_prev = 0;   // scale operands of the last P V products, pinned until they finish
+  int psc_prev = 0;
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
@@ -142,14 +145,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 
     // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
     v16f st[2];
+    uint32_t ksc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint8_t* kp = sK + (kb * 32 + n) * KST + 16 * g;
-      const uint32_t ksc = sKs[kb * 32 + n] >> (8 * g);
+      ksc[kb] = sKs[kb * 32 + n] >> (8 * g);
       v16f acc = v16f{};
-      acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc, qsc);
+      acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc[kb], qsc);
       if constexpr (NC > 1)
-        acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc, qsc);
+        acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc[kb], qsc);
       st[kb] = acc;
     }
     const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
@@ -171,6 +175,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
       bm[kb] = wave_max_xor(m, 32);
     }
+    // S has been read: this tile's S products and the previous tile's P V products are done
+    keep(ksc[0]);
+    keep(ksc[1]);
+    keep(vsc_prev);
+    keep(psc_prev);
     const float m_new = fmaxf(m_run, ceilf(fmaxf(bm[0], bm[1]) * c));
     if (m_new > m_run) {
       const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_new));
@@ -195,8 +204,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     float sc[2], lim[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const float amax = __builtin_amdgcn_exp2f(fmaf(bm[kb], c, negM));
-      kc[kb] = max(scale_code(amax), 1);
+      // block amax of p is 2^(block max of t - M): its scale straight from that exponent
+      kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
       sc[kb] = e8m0_f32(kc[kb]);
       lim[kb] = 448.f * sc[kb];
     }
@@ -244,11 +253,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
       }
     }
+    vsc_prev = vsc;
+    psc_prev = psc;
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (M + log2 l).  Each lane half summed
   // p over its 16 keys of every block: the row sum adds both halves.
   l_run += __shfl_xor(l_run, 32, 64);
+  keep(o[ND - 1][0]);
+  keep(vsc_prev);
+  keep(psc_prev);
   if (qi >= L) return;
   const float inv = 1.f / l_run;
   const long orow = (long)(tok0 + qi) * rowH + (long)h * D;

@@ -198,17 +198,82 @@ size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D) {
   return up((size_t)tokens * H * D * 2) + up((size_t)tokens * H * 4);
 }
 
-mx_status mx_attn_bwd(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*,
-                      const uint8_t*, const uint8_t*, const void*, const void*, mx_dtype, const float*, int, int, int,
-                      int, float, int, int, void*, void*, void*, mx_dtype, void*, size_t, hipStream_t) {
-  return MX_EUNSUPPORTED;
+static mx_status bwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                            const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                            const uint8_t* do_data, const uint8_t* do_scale, const void* o, const void* dout,
+                            mx_dtype io_dtype, const float* lse, int H, int D, float softmax_scale, int dq_scale_log2,
+                            void* dq, void* dk, void* dv, mx_dtype grad_dtype, void* workspace,
+                            size_t workspace_bytes, int tokens, mxk::BwdArgs& a) {
+  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if ((io_dtype != MX_BF16 && io_dtype != MX_F32) || (grad_dtype != MX_BF16 && grad_dtype != MX_F32)) return MX_EINVAL;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
+  if (dq_scale_log2 < -15 || dq_scale_log2 > 15) return MX_EINVAL;
+  if (!all_aligned({q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse, dq, dk, dv}))
+    return MX_EINVAL;
+  if (!workspace || !aligned16(workspace)) return MX_EWORKSPACE;
+  if (workspace_bytes < mx_attn_bwd_workspace_bytes(tokens, H, D)) return MX_EWORKSPACE;
+  a.q = q_data; a.qs = q_scale; a.k = k_data; a.ks = k_scale; a.v = v_data; a.vs = v_scale;
+  a.dob = do_data; a.dos = do_scale;
+  a.o = o; a.dout = dout; a.lse = lse;
+  a.H = H;
+  a.c = log2_scale(softmax_scale);
+  a.sigma = softmax_scale;
+  a.dq_mult = softmax_scale * std::ldexp(1.0f, dq_scale_log2);
+  a.dq_unscale = std::ldexp(1.0f, -dq_scale_log2);
+  a.grad_f32 = grad_dtype == MX_F32;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  const size_t acc_bytes = ((size_t)tokens * H * D * 2 + 255) / 256 * 256;
+  a.acc = workspace;
+  a.Dbuf = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes);
+  return MX_OK;
 }
 
-mx_status mx_attn_bwd_varlen(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*,
-                             const uint8_t*, const uint8_t*, const uint8_t*, const void*, const void*, mx_dtype,
-                             const float*, const int32_t*, const int32_t*, int, int, int, int, int, float, int, int,
-                             void*, void*, void*, mx_dtype, void*, size_t, hipStream_t) {
-  return MX_EUNSUPPORTED;
+mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data, const uint8_t* k_scale,
+                      const uint8_t* v_data, const uint8_t* v_scale, const uint8_t* do_data, const uint8_t* do_scale,
+                      const void* o, const void* dout, mx_dtype io_dtype, const float* lse, int B, int S, int H, int D,
+                      float softmax_scale, int causal, int dq_scale_log2, void* dq, void* dk, void* dv,
+                      mx_dtype grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                                io_dtype, lse, H, D, softmax_scale, dq_scale_log2, dq, dk, dv, grad_dtype, workspace,
+                                workspace_bytes, B * S, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = nullptr;
+  a.seq.csr = nullptr;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.nseq = B;
+  a.T = B * S;
+  return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, S, stream));
+}
+
+mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                             const uint8_t* do_data, const uint8_t* do_scale, const void* o, const void* dout,
+                             mx_dtype io_dtype, const float* lse, const int32_t* cu_seqlens,
+                             const int32_t* cu_scale_rows, int nseq, int total_tokens, int max_seqlen, int H, int D,
+                             float softmax_scale, int causal, int dq_scale_log2, void* dq, void* dk, void* dv,
+                             mx_dtype grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                                io_dtype, lse, H, D, softmax_scale, dq_scale_log2, dq, dk, dv, grad_dtype, workspace,
+                                workspace_bytes, total_tokens, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_scale_rows;
+  a.seq.S = 0;
+  a.seq.nblk = 0;
+  a.nseq = nseq;
+  a.T = total_tokens;
+  return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, max_seqlen, stream));
 }
 
 }  // extern "C"

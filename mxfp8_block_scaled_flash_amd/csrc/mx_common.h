@@ -44,6 +44,20 @@ MX_DEV int scale_code(float amax) {
   return max(e - 8, 0);
 }
 
+// E8M0 code of a block of values p = fl32(2^a), from the block's largest
+// exponent a_max alone: the code clamp(floor(log2 fl32(2^a_max)) + 119, 0, 254)
+// that scale_code() would pick from the rounded maximum.  floor(log2) of the
+// rounded value is floor(a_max), except on [log2(1 - 2^-25), 0), where 2^a
+// rounds up to 1.0 (the fp32 bound below is the smallest float in that
+// interval).  No other fp32 a lies that close below an integer.  This makes
+// the decision independent of the accuracy of the hardware exp2.
+MX_DEV int exp2_scale_code(float a_max) {
+  if (!(a_max > -1.0e30f)) return 0;   // empty or fully masked block
+  float f = floorf(a_max);
+  if (a_max < 0.f && a_max >= __uint_as_float(0xB338AA3Bu)) f = 0.f;
+  return min(max((int)f + 119, 0), 254);
+}
+
 // 2^(k-127) as an fp32 value, for k in [1, 254].
 MX_DEV float e8m0_f32(int k) { return __uint_as_float((uint32_t)k << 23); }
 
@@ -58,5 +72,17 @@ MX_DEV uint32_t f32_to_bf16(float f) {
 }
 
 MX_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+// The scaled MFMA reads its operand registers (data and E8M0 scales) over the
+// passes of the instruction, and the compiler may hand those registers to
+// other values as soon as the instruction has issued.  keep() pins values in
+// their registers up to a point placed after something that consumes the
+// MFMA's result (which waits for the instruction to finish).
+template <typename T>
+MX_DEV void keep(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
 
 }  // namespace mxk

@@ -28,8 +28,29 @@ struct FwdArgs {
   float* lse;
 };
 
+struct BwdArgs {
+  const uint8_t *q, *qs, *k, *ks, *v, *vs, *dob, *dos;   // SQ32 Q, K, dO; ROW32 V
+  const void* o;        // forward output [tokens, H, D]
+  const void* dout;     // incoming gradient [tokens, H, D]
+  const float* lse;     // [B, H, S] or [H, T]
+  SeqMap seq;
+  int H;
+  int nseq;
+  int nkt;              // key tiles per sequence
+  int T;                // total tokens
+  float c;              // fl32(softmax_scale * log2 e)
+  float sigma;          // softmax_scale
+  float dq_mult;        // softmax_scale * 2^s
+  float dq_unscale;     // 2^-s
+  int grad_f32;
+  void *dq, *dk, *dv;
+  void* acc;            // fp16 dQ accumulator [tokens, H, D] (workspace)
+  float* Dbuf;          // D_i (workspace), indexed like lse
+};
+
 hipError_t launch_quantize(const void* x, bool fp32, int D, const QuantArgs& a, hipStream_t st);
 hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipStream_t st);
 hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
+hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);
 
 }  // namespace mxk

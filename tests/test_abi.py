@@ -86,3 +86,10 @@ def test_workspace_size():
     n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
     assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
     assert mx.lib().mx_attn_bwd_workspace_bytes(-1, 3, 128) == 0
+
+
+def test_library_has_no_unresolved_kernel_stubs():
+    import subprocess
+    out = subprocess.run(["nm", "-D", mx._LIB_PATH], capture_output=True, text=True).stdout
+    missing = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not missing, missing
