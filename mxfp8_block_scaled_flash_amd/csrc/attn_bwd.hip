@@ -19,9 +19,10 @@
 //     dS = p (dP - D), then MX codes of P (32 queries per key) and of dS
 //     (square 32 x 32 blocks, wave-wide amax), and accumulates dV^T and
 //     dK^T in registers.  The dS codes go to LDS, and the workgroup's waves
-//     then form dQ^T = K^T dS^T for the tile (128 keys of contraction) and
-//     add it, scaled by softmax_scale * 2^s, into the fp16 accumulator with
-//     packed fp16 atomics.  Q^ and dO^ are read from LDS in both
+//     then form dQ = dS K for the tile (128 keys of contraction) and add it,
+//     scaled by softmax_scale * 2^s, into the fp16 accumulator with packed
+//     fp16 atomics laid along contiguous features (neighbouring lanes pair
+//     up), so each atomic instruction touches four 64-byte row segments.  Q^ and dO^ are read from LDS in both
 //     orientations: rows as MFMA operands, columns through
 //     ds_read_b64_tr_b8 (one payload, both GEMMs).
 //  3. bwd_dq_kernel: dQ = acc * 2^-s in the output type.
@@ -352,7 +353,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- dQ^T for (query block t, feature chunk dc) pairs, shared out among the waves
+    // ---- dQ for (query block t, feature chunk dc) pairs, shared out among the waves.
+    // Output element i of lane l: query 32t + 8(i/4) + 4g + i%4, feature 32 dc + l%32, so a
+    // wave's atomics run along contiguous features of a few query rows.
     for (int cb = w; cb < 2 * ND; cb += NW) {
       const int t = cb / ND, dc = cb % ND;
       if (q0 + 32 * t >= L) continue;
@@ -361,12 +364,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
       int kscale[BN / 64], sscale[BN / 64];
 #pragma unroll
       for (int kk = 0; kk < BN / 64; ++kk) {
-        ka[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);
-        sb[kk] = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);
-        kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
+        sb[kk] = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+        ka[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features, K: keys
         sscale[kk] = (int)sDSs[t][2 * kk + g];
+        kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
         if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-        acc = mfma32b<0, 0>(ka[kk], sb[kk], acc, kscale[kk], sscale[kk]);
+        acc = mfma32b<0, 0>(sb[kk], ka[kk], acc, sscale[kk], kscale[kk]);
       }
       keep(acc[0]);
 #pragma unroll
@@ -374,13 +377,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
         keep(kscale[kk]);
         keep(sscale[kk]);
       }
-      const int qi = q0 + 32 * t + n;
-      if (qi < L) {
-        _Float16* ap = (_Float16*)a.acc + (long)(tok0 + qi) * rowH + (long)h * D + 32 * dc + 4 * g;
+      // pair neighbouring lanes: the even lane of a pair adds (row, f..f+1) of element i, the
+      // odd lane (row + 1, f-1..f) of element i + 1
+      const bool odd = lane & 1;
+      const int fcol = 32 * dc + n - (odd ? 1 : 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          atomic_add_h2(ap + 8 * q, acc[4 * q] * a.dq_mult, acc[4 * q + 1] * a.dq_mult);
-          atomic_add_h2(ap + 8 * q + 2, acc[4 * q + 2] * a.dq_mult, acc[4 * q + 3] * a.dq_mult);
+      for (int i = 0; i < 16; i += 2) {
+        const float mine = odd ? acc[i + 1] : acc[i];
+        const float send = odd ? acc[i] : acc[i + 1];
+        const float got = __shfl_xor(send, 1, 64);
+        const int ql = 32 * t + 8 * (i >> 2) + 4 * g + (i & 3) + (odd ? 1 : 0);
+        const int qi = q0 + ql;
+        if (qi < L) {
+          _Float16* ap = (_Float16*)a.acc + (long)(tok0 + qi) * rowH + (long)h * D + fcol;
+          if (odd) atomic_add_h2(ap, got * a.dq_mult, mine * a.dq_mult);
+          else atomic_add_h2(ap, mine * a.dq_mult, got * a.dq_mult);
         }
       }
     }
