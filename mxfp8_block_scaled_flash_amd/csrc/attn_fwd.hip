@@ -25,7 +25,9 @@
 //    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
 //    through ds_read_b64_tr_b8, in the same key order.
 //  * K and V tiles of 64 keys are staged in LDS and shared by the
-//    workgroup's waves.  Workgroups are ordered so that each XCD works
+//    workgroup's waves; two LDS buffers, the next tile's global loads in
+//    flight while the current one is computed, one barrier per tile, and
+//    two workgroups per CU so one's softmax overlaps the other's MFMAs.  Workgroups are ordered so that each XCD works
 //    through whole heads, longest (causal) query tiles first, keeping a
 //    head's K/V in that XCD's L2.
 #include "mx_common.h"
@@ -49,18 +51,29 @@ MX_DEV v2i lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
 
+// One 64-key tile of K and V in flight between HBM and LDS.
+template <int D, int NT>
+struct KVStage {
+  static constexpr int CH = 64 * D / 16 / NT;   // 16-byte chunks per thread per tensor
+  uint4 k[CH], v[CH];
+  uint32_t ks;
+  uint32_t vb[D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
+};
+
 template <int D, int NW, bool CAUSAL, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;   // queries per workgroup
   constexpr int BN = 64;        // keys per tile
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
   constexpr int KST = D + 16;   // LDS row stride of the K and V tiles
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
-  __shared__ uint32_t sKs[BN];   // K ROW32 scale bytes of each key
-  __shared__ uint32_t sVs[64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
+  static_assert(BN * D / 16 % NT == 0, "tile chunks must divide among the threads");
+  // two buffers: the tile being computed and the next one, written while it is computed
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][BN * KST];
+  __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
+  __shared__ uint32_t sVs[2][64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
 
@@ -78,6 +91,49 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int q0 = qbase + 32 * w;
   const int qi = q0 + n;
   const long rowH = (long)a.H * D;
+
+  // ---- staging of one K/V tile: global loads into registers, then LDS stores
+  // Loads are branch-free (rows past the end are clamped to the last key and
+  // zeroed when stored), so no wait on them is forced before the tile that is
+  // being computed needs it.  Every wave fetches the scales of key `lane`;
+  // wave 0 stores the K ones, wave 1 the V ones.
+  auto load_tile = [&](int t, KVStage<D, NT>& st) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
+      const int ch = tid + c * NT;
+      const int r = ch / (D / 16), cx = ch % (D / 16);
+      const long off = (long)(tok0 + min(k0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
+      st.k[c] = *(const uint4*)(a.k + off);
+      st.v[c] = *(const uint4*)(a.v + off);
+    }
+    const long srow = ((long)(srow0 + min(k0 + lane, L - 1)) * a.H + h);
+    st.ks = (D == 128) ? *(const uint32_t*)(a.ks + srow * 4) : *(const uint16_t*)(a.ks + srow * 2);
+    const int vblk = min(2 * t + (lane >> 5), (L - 1) >> 5);
+    const uint8_t* vp = a.vs + ((long)(sblk0 + vblk) * a.H + h) * D + (lane & 31);
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) st.vb[dc] = vp[32 * dc];
+  };
+  auto store_tile = [&](int t, int buf, const KVStage<D, NT>& st) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
+      const int ch = tid + c * NT;
+      const int r = ch / (D / 16), cx = ch % (D / 16);
+      const uint32_t m = (k0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
+      const uint4 kk = st.k[c], vv = st.v[c];
+      *(uint4*)(&sK[buf][r * KST + cx * 16]) = make_uint4(kk.x & m, kk.y & m, kk.z & m, kk.w & m);
+      *(uint4*)(&sV[buf][r * KST + cx * 16]) = make_uint4(vv.x & m, vv.y & m, vv.z & m, vv.w & m);
+    }
+    if (w == 0) {
+      sKs[buf][lane] = (k0 + lane < L) ? st.ks : 0u;
+    } else if (w == 1) {
+      uint32_t vs = 0;
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc) vs |= st.vb[dc] << (8 * dc);
+      sVs[buf][lane] = ((2 * t + (lane >> 5)) * 32 < L) ? vs : 0u;
+    }
+  };
 
   // ---- Q as the B operand (resident for the whole key loop)
   v8i qa[NC];
@@ -106,155 +162,142 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   uint32_t vsc_prev = 0;   // scale operands of the last P V products, pinned until they finish
   int psc_prev = 0;
 
+  {
+    KVStage<D, NT> st0;
+    load_tile(0, st0);
+    store_tile(0, 0, st0);
+  }
+  __syncthreads();
+
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    __syncthreads();
-    // ---- stage K and V (payload rows of D bytes) and their scales
-    for (int ch = tid; ch < BN * D / 16; ch += NT) {
-      const int r = ch / (D / 16), cx = ch % (D / 16);
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (k0 + r < L) {
-        const long off = (long)(tok0 + k0 + r) * rowH + (long)h * D + cx * 16;
-        kv = *(const uint4*)(a.k + off);
-        vv = *(const uint4*)(a.v + off);
-      }
-      *(uint4*)(sK + r * KST + cx * 16) = kv;
-      *(uint4*)(sV + r * KST + cx * 16) = vv;
-    }
-    for (int r = tid; r < BN; r += NT) {
-      uint32_t wk = 0;
-      if (k0 + r < L) {
-        const long srow = ((long)(srow0 + k0 + r) * a.H + h);
-        wk = (D == 128) ? *(const uint32_t*)(a.ks + srow * 4) : *(const uint16_t*)(a.ks + srow * 2);
-      }
-      sKs[r] = wk;
-    }
-    for (int x = tid; x < 64; x += NT) {
-      const int b = x >> 5, rr = x & 31;
-      uint32_t wv = 0;
-      if ((2 * t + b) * 32 < L) {
-        const uint8_t* vp = a.vs + ((long)(sblk0 + 2 * t + b) * a.H + h) * D + rr;
-#pragma unroll
-        for (int dc = 0; dc < ND; ++dc) wv |= (uint32_t)vp[32 * dc] << (8 * dc);
-      }
-      sVs[x] = wv;
-    }
-    __syncthreads();
-    if (q0 >= L) continue;
-    if (CAUSAL && k0 > q0 + 31) continue;   // tile entirely above this wave's diagonal
+    const int cur = t & 1;
+    // the next tile's loads are in flight while this one is computed (past
+    // the last tile the last one is fetched again and its buffer rewritten
+    // with the same bytes, which keeps the loop free of branches around them)
+    KVStage<D, NT> nxt;
+    const int tn = min(t + 1, ntiles - 1);
+    load_tile(tn, nxt);
 
-    // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
-    v16f st[2];
-    uint32_t ksc[2];
+    const bool compute = q0 < L && !(CAUSAL && k0 > q0 + 31);   // skip tiles above this wave's diagonal
+    if (compute) {
+      const uint8_t* sKc = sK[cur];
+      const uint8_t* sVc = sV[cur];
+      // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
+      v16f st[2];
+      uint32_t ksc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* kp = sK + (kb * 32 + n) * KST + 16 * g;
-      ksc[kb] = sKs[kb * 32 + n] >> (8 * g);
-      v16f acc = v16f{};
-      acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc[kb], qsc);
-      if constexpr (NC > 1)
-        acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc[kb], qsc);
-      st[kb] = acc;
-    }
-    const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
-    if (need_mask) {
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* kp = sKc + (kb * 32 + n) * KST + 16 * g;
+        ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
+        v16f acc = v16f{};
+        acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc[kb], qsc);
+        if constexpr (NC > 1)
+          acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc[kb], qsc);
+        st[kb] = acc;
+      }
+      const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key >= L || (CAUSAL && key > qi)) st[kb][i] = -INFINITY;
+          }
+      }
+      // ---- block maxima, frame update
+      float bm[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float m = st[kb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
+        bm[kb] = wave_max_xor(m, 32);
+      }
+      // S has been read: this tile's S products and the previous tile's P V products are done
+      keep(ksc[0]);
+      keep(ksc[1]);
+      keep(vsc_prev);
+      keep(psc_prev);
+      const float m_new = fmaxf(m_run, ceilf(fmaxf(bm[0], bm[1]) * c));
+      if (m_new > m_run) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_new));
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) o[dc] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float negM = -m_run;
+      // ---- p = 2^(S c - M), running sum
+      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= L || (CAUSAL && key > qi)) st[kb][i] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
+          st[kb][i] = p;
+          psum += p;
         }
-    }
-    // ---- block maxima, frame update
-    float bm[2];
+      l_run += psum;
+      int kc[2];
+      float sc[2], lim[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float m = st[kb][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
-      bm[kb] = wave_max_xor(m, 32);
-    }
-    // S has been read: this tile's S products and the previous tile's P V products are done
-    keep(ksc[0]);
-    keep(ksc[1]);
-    keep(vsc_prev);
-    keep(psc_prev);
-    const float m_new = fmaxf(m_run, ceilf(fmaxf(bm[0], bm[1]) * c));
-    if (m_new > m_run) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_new));
-#pragma unroll
-      for (int dc = 0; dc < ND; ++dc) o[dc] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float negM = -m_run;
-    // ---- p = 2^(S c - M), running sum, P block scales from the block maxima
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
-        st[kb][i] = p;
-        psum += p;
+      for (int kb = 0; kb < 2; ++kb) {
+        // block amax of p is 2^(block max of t - M): its scale straight from that exponent
+        kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
+        sc[kb] = e8m0_f32(kc[kb]);
+        lim[kb] = 448.f * sc[kb];
       }
-    l_run += psum;
-    int kc[2];
-    float sc[2], lim[2];
+      // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
+      uint32_t dw[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // block amax of p is 2^(block max of t - M): its scale straight from that exponent
-      kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
-      sc[kb] = e8m0_f32(kc[kb]);
-      lim[kb] = 448.f * sc[kb];
-    }
-    // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
-    uint32_t dw[2][4];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int q = 0; q < 4; ++q) {
+          v2s z = {0, 0};
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q], lim[kb]), fminf(st[kb][4 * q + 1], lim[kb]),
+                                                       sc[kb], false);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q + 2], lim[kb]),
+                                                       fminf(st[kb][4 * q + 3], lim[kb]), sc[kb], true);
+          dw[kb][q] = __builtin_bit_cast(uint32_t, z);
+        }
+      // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order
+      v8i pb;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v2s z = {0, 0};
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q], lim[kb]), fminf(st[kb][4 * q + 1], lim[kb]),
-                                                     sc[kb], false);
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q + 2], lim[kb]), fminf(st[kb][4 * q + 3], lim[kb]),
-                                                     sc[kb], true);
-        dw[kb][q] = __builtin_bit_cast(uint32_t, z);
+      for (int kb = 0; kb < 2; ++kb) {
+        auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
+        auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
+        pb[4 * kb + 0] = s02[0];
+        pb[4 * kb + 1] = s02[1];
+        pb[4 * kb + 2] = s13[0];
+        pb[4 * kb + 3] = s13[1];
       }
-    // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order
-    v8i pb;
+      const int psc = g ? kc[1] : kc[0];
+      const uint32_t vsc = sVs[cur][lane];
+      // ---- O^T += V^T P^T, V^T rows d = 32 dc + lane%32, through LDS transpose reads
+      {
+        const int G = lane >> 4, i16 = lane & 15;
+        const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
+        const int rowofs = 16 * (G >> 1) + (i16 >> 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
-      auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
-      pb[4 * kb + 0] = s02[0];
-      pb[4 * kb + 1] = s02[1];
-      pb[4 * kb + 2] = s13[0];
-      pb[4 * kb + 3] = s13[1];
-    }
-    const int psc = g ? kc[1] : kc[0];
-    const uint32_t vsc = sVs[lane];
-    // ---- O^T += V^T P^T, V^T rows d = 32 dc + lane%32, through LDS transpose reads
-    {
-      const int G = lane >> 4, i16 = lane & 15;
-      const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
-      const int rowofs = 16 * (G >> 1) + (i16 >> 1);
-#pragma unroll
-      for (int dc = 0; dc < ND; ++dc) {
-        const uint8_t* vp = sV + rowofs * KST + 32 * dc + colofs;
-        v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * KST), r2 = lds_tr8(vp + 32 * KST), r3 = lds_tr8(vp + 40 * KST);
-        v8i va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-        if (dc == 0) o[0] = mfma32<0, 0>(va, pb, o[0], vsc, psc);
-        if (dc == 1) o[1] = mfma32<1, 0>(va, pb, o[1], vsc, psc);
-        if constexpr (ND > 2) {
-          if (dc == 2) o[2] = mfma32<2, 0>(va, pb, o[2], vsc, psc);
-          if (dc == 3) o[3] = mfma32<3, 0>(va, pb, o[3], vsc, psc);
+        for (int dc = 0; dc < ND; ++dc) {
+          const uint8_t* vp = sVc + rowofs * KST + 32 * dc + colofs;
+          v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * KST), r2 = lds_tr8(vp + 32 * KST), r3 = lds_tr8(vp + 40 * KST);
+          v8i va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+          if (dc == 0) o[0] = mfma32<0, 0>(va, pb, o[0], vsc, psc);
+          if (dc == 1) o[1] = mfma32<1, 0>(va, pb, o[1], vsc, psc);
+          if constexpr (ND > 2) {
+            if (dc == 2) o[2] = mfma32<2, 0>(va, pb, o[2], vsc, psc);
+            if (dc == 3) o[3] = mfma32<3, 0>(va, pb, o[3], vsc, psc);
+          }
         }
       }
+      vsc_prev = vsc;
+      psc_prev = psc;
     }
-    vsc_prev = vsc;
-    psc_prev = psc;
+    store_tile(tn, cur ^ 1, nxt);
+    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (M + log2 l).  Each lane half summed
