@@ -121,24 +121,46 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ main kernel
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
-  constexpr int BN = 32 * NW;   // keys per workgroup
+// One workgroup of eight waves per (sequence, head, 128-key tile), walking
+// 64-query steps.  Per step:
+//   A. wave w computes S and dP for key block w%4 and query block w/4
+//      (32 x 32), p and dS, their MX codes (P: one scale per key and 32
+//      queries; dS: one scale per square block), stored in LDS as [key][query];
+//   B. wave w accumulates dV^T and dK^T (all 64 queries of contraction) for
+//      key block w%4 and D/64 of the 32-feature chunks, reading the codes back;
+//   C. wave w < 2D/32 forms dQ for one (query block, feature chunk) from all
+//      128 keys and adds it to the fp16 accumulator with packed atomics.
+// The next step's Q / dO tiles, scales, LSE and D are loaded into registers
+// while this step computes and written to the other LDS buffer at its end:
+// two barriers per step.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int BN = 128;       // keys per workgroup
   constexpr int BQ = 64;        // queries per step
   constexpr int NC = D / 64;    // 64-feature chunks of the S / dP contraction
   constexpr int ND = D / 32;    // 32-feature chunks of dK, dV, dQ
+  constexpr int CPW = ND / 2;   // dV / dK chunks per wave
   constexpr int NB = D / 32;    // scale bytes per SQ32 / ROW32 scale word
   constexpr int KST = D + 16;   // LDS row stride of K, Q, dO tiles
-  constexpr int SST = BQ + 16;  // LDS row stride of the dS code tile [key][query]
+  constexpr int SST = BQ + 16;  // LDS row stride of the P and dS code tiles [key][query]
   constexpr int NT = NW * 64;
+  constexpr int QCH = BQ * D / 16;    // 16-byte chunks of one Q (or dO) tile
+  constexpr int CPT = 2 * QCH / NT;   // chunks of Q and dO per thread per step
+  static_assert(2 * QCH % NT == 0, "chunks must divide among the threads");
   __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[BN * SST];
   __shared__ __attribute__((aligned(16))) uint8_t sDS[BN * SST];
-  __shared__ uint32_t sKs[NW];       // K SQ32 scale word (bytes = feature blocks) per key block
-  __shared__ uint32_t sQs[2], sDOs[2];
-  __shared__ uint32_t sDSs[2][NW];   // dS scale of (query block t, key block)
-  __shared__ float sL[BQ], sDv[BQ];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
+  __shared__ uint32_t sKs[4];
+  __shared__ uint32_t sVs[BN];             // V ROW32 scale word per key              // K SQ32 scale word (bytes = feature blocks) per key block
+  __shared__ uint32_t sQs[2][2], sDOs[2][2];   // [buffer][query block]
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];    // LSE log2(e)
+  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];   // D
+  __shared__ int sPs[2][BN];               // P scale code of (query block, key)
+  __shared__ int sDSs[2][4];               // dS scale code of (query block, key block)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
   const int id = blockIdx.x, xcd = id & 7, jj = id >> 3;
@@ -151,8 +173,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
   const int kbase = kt * BN;
   if (kbase >= L) return;
   const long rowH = (long)a.H * D;
-  const int kw0 = kbase + 32 * w;
-  const int kj = kw0 + n;
+  const int kb = w & 3;               // key block of phases A and B
+  const int ta = w >> 2;              // query block of phase A
+  const int kw0 = kbase + 32 * kb;
+  const int kj = kw0 + n;             // this lane's key in phases A and B
 
   // ---- K tile (all keys of the workgroup) for the dQ products, and scales
   for (int ch = tid; ch < BN * D / 16; ch += NT) {
@@ -161,256 +185,267 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_kernel(BwdArgs a) {
     if (kbase + r < L) kv = *(const uint4*)(a.k + (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16);
     *(uint4*)(sK + r * KST + cx * 16) = kv;
   }
-  if (tid < NW) {
+  if (tid < 4) {
     uint32_t wk = 0;
-    if (kbase + 32 * tid < L)
-      wk = ld_scale_word(a.ks + ((long)(sblk0 + kbase / 32 + tid) * a.H + h) * NB, NB);
+    if (kbase + 32 * tid < L) wk = ld_scale_word(a.ks + ((long)(sblk0 + kbase / 32 + tid) * a.H + h) * NB, NB);
     sKs[tid] = wk;
   }
-  // ---- this wave's keys as the column operand of S = Q K^T and dP = dO V^T
-  v8i kb[NC], vb[NC];
-  uint32_t ksc = 0, vsc = 0;
-  if (kj < L) {
-    const uint8_t* kp = a.k + (long)(tok0 + kj) * rowH + (long)h * D;
-    const uint8_t* vp = a.v + (long)(tok0 + kj) * rowH + (long)h * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kb[c] = pack8b(*(const uint4*)(kp + 64 * c + 16 * g), *(const uint4*)(kp + 64 * c + 32 + 16 * g));
-      vb[c] = pack8b(*(const uint4*)(vp + 64 * c + 16 * g), *(const uint4*)(vp + 64 * c + 32 + 16 * g));
-    }
-    ksc = ld_scale_word(a.ks + ((long)(sblk0 + kw0 / 32) * a.H + h) * NB, NB) >> (8 * g);
-    vsc = ld_scale_word(a.vs + ((long)(srow0 + kj) * a.H + h) * NB, NB) >> (8 * g);
-  } else {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kb[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      vb[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+  // ---- V tile for the dP products (K comes from the tile above), and V's scales
+  for (int ch = tid; ch < BN * D / 16; ch += NT) {
+    const int r = ch / (D / 16), cx = ch % (D / 16);
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (kbase + r < L) vv = *(const uint4*)(a.v + (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16);
+    *(uint4*)(sV + r * KST + cx * 16) = vv;
   }
-  v16f dvt[ND], dkt[ND];   // dV^T, dK^T: element i = feature 32 dc + 8(i/4) + 4g + i%4, key kj
+  if (tid < BN) sVs[tid] = (kbase + tid < L) ? ld_scale_word(a.vs + ((long)(srow0 + kbase + tid) * a.H + h) * NB, NB) : 0u;
+
+  // ---- staging of one query step.  Loads are branch-free: rows past the end
+  // are clamped to the last query and zeroed (or masked later) when stored.
+  struct Stage {
+    uint4 x[CPT];
+    float l, d;
+    uint32_t qs, dos;
+  };
+  auto lse_index = [&](int q) -> long {
+    return a.seq.cu ? (long)h * a.T + tok0 + q : ((long)s * a.H + h) * a.seq.S + q;
+  };
+  auto load_step = [&](int q0, Stage& st) {
 #pragma unroll
-  for (int dc = 0; dc < ND; ++dc) {
-    dvt[dc] = v16f{};
-    dkt[dc] = v16f{};
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * NT;
+      const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
+      const long off = (long)(tok0 + min(q0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
+      st.x[c] = *(const uint4*)((ch < QCH ? a.q : a.dob) + off);
+    }
+    const long li = lse_index(min(q0 + lane, L - 1));
+    st.l = a.lse[li];
+    st.d = a.Dbuf[li];
+    const long so = ((long)(sblk0 + min(q0 / 32 + (lane & 1), (L - 1) / 32)) * a.H + h) * NB;
+    st.qs = ld_scale_word(a.qs + so, NB);
+    st.dos = ld_scale_word(a.dos + so, NB);
+  };
+  auto store_step = [&](int q0, int buf, const Stage& st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * NT;
+      const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
+      const uint32_t m = (q0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
+      const uint4 x = st.x[c];
+      uint8_t* dst = (ch < QCH ? sQ[buf] : sDO[buf]) + r * KST + cx * 16;
+      *(uint4*)dst = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+    }
+    if (w == 0) {
+      sL[buf][lane] = st.l * 1.44269504088896340736f;
+      sDv[buf][lane] = st.d;
+    } else if (w == 1 && lane < 2) {
+      const bool ok = q0 + 32 * lane < L;
+      sQs[buf][lane] = ok ? st.qs : 0u;
+      sDOs[buf][lane] = ok ? st.dos : 0u;
+    }
+  };
+
+  v16f dvt[CPW], dkt[CPW];   // dV^T, dK^T: element i = feature 32 dc + 8(i/4) + 4g + i%4, key kj
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    dvt[c] = v16f{};
+    dkt[c] = v16f{};
   }
-  const float c = a.c;
+  const float cl = a.c;
   const int qstart = CAUSAL ? (kbase / BQ) * BQ : 0;
+  const int nsteps = (L - qstart + BQ - 1) / BQ;
   // scale operands of the last dV / dK products, pinned until those products finish
   uint32_t dosw_prev = 0, qsw_prev = 0;
   int psc_prev = 0, ssc_prev = 0;
 
-  for (int q0 = qstart; q0 < L; q0 += BQ) {
-    __syncthreads();
-    // ---- stage the Q and dO tiles, their scales, LSE*log2(e) and D
-    for (int ch = tid; ch < BQ * D / 16; ch += NT) {
-      const int r = ch / (D / 16), cx = ch % (D / 16);
-      uint4 qv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
-      if (q0 + r < L) {
-        const long off = (long)(tok0 + q0 + r) * rowH + (long)h * D + cx * 16;
-        qv = *(const uint4*)(a.q + off);
-        dv = *(const uint4*)(a.dob + off);
-      }
-      *(uint4*)(sQ + r * KST + cx * 16) = qv;
-      *(uint4*)(sDO + r * KST + cx * 16) = dv;
-    }
-    if (tid < 2) {
-      uint32_t wq = 0, wd = 0;
-      if (q0 + 32 * tid < L) {
-        const long so = ((long)(sblk0 + q0 / 32 + tid) * a.H + h) * NB;
-        wq = ld_scale_word(a.qs + so, NB);
-        wd = ld_scale_word(a.dos + so, NB);
-      }
-      sQs[tid] = wq;
-      sDOs[tid] = wd;
-    }
-    for (int r = tid; r < BQ; r += NT) {
-      float l2 = 0.f, dd = 0.f;
-      if (q0 + r < L) {
-        const long li = a.seq.cu ? (long)h * a.T + tok0 + q0 + r : ((long)s * a.H + h) * a.seq.S + q0 + r;
-        l2 = a.lse[li] * 1.44269504088896340736f;
-        dd = a.Dbuf[li];
-      }
-      sL[r] = l2;
-      sDv[r] = dd;
-    }
-    __syncthreads();
+  {
+    Stage st0;
+    load_step(qstart, st0);
+    store_step(qstart, 0, st0);
+  }
+  __syncthreads();
 
-    const bool active = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);
-    if (active) {
-      // ---- S and dP for two 32-query blocks: element i = query q0 + 32t + 8(i/4) + 4g + i%4, key kj
-      v16f st[2], dpt[2];
-      uint32_t qsa[2], dsa[2];
+  for (int j = 0; j < nsteps; ++j) {
+    const int q0 = qstart + j * BQ, buf = j & 1;
+    const uint8_t* sQb = sQ[buf];
+    const uint8_t* sDOb = sDO[buf];
+    // the next step's operands are in flight while this one is computed (after
+    // the last step, the last one is fetched again and its buffer rewritten)
+    const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
+    Stage nx;
+    load_step(qn, nx);
+
+    // ---- A. S and dP for (key block kb, query block ta): element i = query qa0 + 8(i/4) + 4g + i%4, key kj
+    const int qa0 = q0 + 32 * ta;
+    uint8_t* prow = sP + (32 * kb + n) * SST + 32 * ta + 16 * g;
+    uint8_t* srow = sDS + (32 * kb + n) * SST + 32 * ta + 16 * g;
+    if (kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31)) {
+      const uint8_t* qp = sQb + (32 * ta + n) * KST + 16 * g;
+      const uint8_t* op = sDOb + (32 * ta + n) * KST + 16 * g;
+      const uint32_t qsa = sQs[buf][ta] >> (8 * g), dsa = sDOs[buf][ta] >> (8 * g);
+      v16f st = v16f{}, dpt = v16f{};
+      const uint8_t* kr = sK + (32 * kb + n) * KST + 16 * g;
+      const uint8_t* vr = sV + (32 * kb + n) * KST + 16 * g;
+      const uint32_t ksc = sKs[kb] >> (8 * g), vsc = sVs[32 * kb + n] >> (8 * g);
+      st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
+                         pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), st, qsa, ksc);
+      dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
+                          pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), dpt, dsa, vsc);
+      if constexpr (NC > 1) {
+        st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
+                           pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
+        dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
+                            pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
+      }
+      float lv[16], dv[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint8_t* qp = sQ + (32 * t + n) * KST + 16 * g;
-        const uint8_t* op = sDO + (32 * t + n) * KST + 16 * g;
-        qsa[t] = sQs[t] >> (8 * g);
-        dsa[t] = sDOs[t] >> (8 * g);
-        v16f sa = v16f{}, da = v16f{};
-        sa = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)), kb[0], sa, qsa[t], ksc);
-        da = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), vb[0], da, dsa[t], vsc);
-        if constexpr (NC > 1) {
-          sa = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)), kb[NC - 1], sa, qsa[t], ksc);
-          da = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)), vb[NC - 1], da, dsa[t], vsc);
-        }
-        st[t] = sa;
-        dpt[t] = da;
+      for (int q = 0; q < 4; ++q) {
+        const float4 l4 = *(const float4*)(&sL[buf][32 * ta + 8 * q + 4 * g]);
+        const float4 d4 = *(const float4*)(&sDv[buf][32 * ta + 8 * q + 4 * g]);
+        lv[4 * q] = l4.x; lv[4 * q + 1] = l4.y; lv[4 * q + 2] = l4.z; lv[4 * q + 3] = l4.w;
+        dv[4 * q] = d4.x; dv[4 * q + 1] = d4.y; dv[4 * q + 2] = d4.z; dv[4 * q + 3] = d4.w;
       }
       // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D)
-      float amax[2], smax[2];   // largest exp2 argument of each P block; |dS| max of each dS block
+      const bool need_mask = qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+      float am = -INFINITY, sm = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float am = -INFINITY, sm = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
-          const int qi = q0 + ql;
-          const bool masked = qi >= L || kj >= L || (CAUSAL && kj > qi);
-          const float arg = masked ? -INFINITY : fmaf(st[t][i], c, -sL[ql]);
-          const float p = __builtin_amdgcn_exp2f(arg);
-          const float ds = p * (dpt[t][i] - sDv[ql]);
-          st[t][i] = p;
-          dpt[t][i] = ds;
-          am = fmaxf(am, arg);
-          sm = fmaxf(sm, fabsf(ds));
+      for (int i = 0; i < 16; ++i) {
+        float arg = fmaf(st[i], cl, -lv[i]);
+        if (need_mask) {
+          const int qi = qa0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (qi >= L || kj >= L || (CAUSAL && kj > qi)) arg = -INFINITY;
         }
-        amax[t] = fmaxf(am, __shfl_xor(am, 32, 64));   // 32 queries of this key
-        smax[t] = wave_max_all(sm);                      // 32 queries x 32 keys
+        const float p = __builtin_amdgcn_exp2f(arg);
+        const float ds = p * (dpt[i] - dv[i]);
+        st[i] = p;
+        dpt[i] = ds;
+        am = fmaxf(am, arg);
+        sm = fmaxf(sm, fabsf(ds));
       }
+      const float amax = fmaxf(am, __shfl_xor(am, 32, 64));   // 32 queries of this key
+      const float smax = wave_max_all(sm);                      // 32 queries x 32 keys
       // S and dP have been read: their products and the previous step's dV, dK products are done
-      keep(qsa[0]); keep(qsa[1]); keep(dsa[0]); keep(dsa[1]);
+      keep(qsa); keep(dsa); keep(ksc); keep(vsc);
       keep(dosw_prev); keep(qsw_prev); keep(psc_prev); keep(ssc_prev);
-      // ---- MX codes: dword q of block t holds queries 8q + 4g + 0..3
-      uint32_t pw[2][4], sw[2][4];
-      int kp[2], ks2[2];
+      // ---- MX codes: dword q holds queries 8q + 4g + 0..3
+      const int kp = max(exp2_scale_code(amax), 1);
+      const int ks2 = max(scale_code(smax), 1);
+      const float psc = e8m0_f32(kp), plim = 448.f * psc;
+      const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
+      uint32_t pw[4], sw[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        kp[t] = max(exp2_scale_code(amax[t]), 1);
-        ks2[t] = max(scale_code(smax[t]), 1);
-        const float psc = e8m0_f32(kp[t]), plim = 448.f * psc;
-        const float ssc = e8m0_f32(ks2[t]), slim = 448.f * ssc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v2s z = {0, 0};
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[t][4 * q], plim), fminf(st[t][4 * q + 1], plim), psc,
-                                                       false);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[t][4 * q + 2], plim), fminf(st[t][4 * q + 3], plim),
-                                                       psc, true);
-          pw[t][q] = __builtin_bit_cast(uint32_t, z);
-          v2s y = {0, 0};
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q], -slim, slim),
-                                                       __builtin_amdgcn_fmed3f(dpt[t][4 * q + 1], -slim, slim), ssc,
-                                                       false);
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q + 2], -slim, slim),
-                                                       __builtin_amdgcn_fmed3f(dpt[t][4 * q + 3], -slim, slim), ssc,
-                                                       true);
-          sw[t][q] = __builtin_bit_cast(uint32_t, y);
-          // dS codes to LDS as [key][query] for the dQ products
-          *(uint32_t*)(sDS + (32 * w + n) * SST + 32 * t + 8 * q + 4 * g) = sw[t][q];
-        }
+      for (int q = 0; q < 4; ++q) {
+        v2s z = {0, 0};
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[4 * q], plim), fminf(st[4 * q + 1], plim), psc, false);
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[4 * q + 2], plim), fminf(st[4 * q + 3], plim), psc, true);
+        pw[q] = __builtin_bit_cast(uint32_t, z);
+        v2s y = {0, 0};
+        y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
+                                                     __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc, false);
+        y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
+                                                     __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc, true);
+        sw[q] = __builtin_bit_cast(uint32_t, y);
       }
-      if (lane == 0) {
-        sDSs[0][w] = ks2[0];
-        sDSs[1][w] = ks2[1];
-      }
-      // ---- swap lane halves: half g then holds queries 16g + 0..15 of each block, in order
-      v8i pP, pS;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        auto a02 = __builtin_amdgcn_permlane32_swap(pw[t][0], pw[t][2], false, false);
-        auto a13 = __builtin_amdgcn_permlane32_swap(pw[t][1], pw[t][3], false, false);
-        pP[4 * t + 0] = a02[0]; pP[4 * t + 1] = a02[1]; pP[4 * t + 2] = a13[0]; pP[4 * t + 3] = a13[1];
-        auto b02 = __builtin_amdgcn_permlane32_swap(sw[t][0], sw[t][2], false, false);
-        auto b13 = __builtin_amdgcn_permlane32_swap(sw[t][1], sw[t][3], false, false);
-        pS[4 * t + 0] = b02[0]; pS[4 * t + 1] = b02[1]; pS[4 * t + 2] = b13[0]; pS[4 * t + 3] = b13[1];
-      }
-      const int pscale = g ? kp[1] : kp[0];
-      const int sscale = g ? ks2[1] : ks2[0];
-      const uint32_t dosw = sDOs[g], qsw = sQs[g];
-      dosw_prev = dosw; qsw_prev = qsw; psc_prev = pscale; ssc_prev = sscale;
-      // ---- dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries)
-#pragma unroll
-      for (int dc = 0; dc < ND; ++dc) {
-        const v8i oa = tr_operand(sDO + 32 * dc, KST, lane);
-        const v8i qa = tr_operand(sQ + 32 * dc, KST, lane);
-        if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pP, dvt[0], dosw, pscale); dkt[0] = mfma32b<0, 0>(qa, pS, dkt[0], qsw, sscale); }
-        if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pP, dvt[1], dosw, pscale); dkt[1] = mfma32b<1, 0>(qa, pS, dkt[1], qsw, sscale); }
-        if constexpr (ND > 2) {
-          if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pP, dvt[2], dosw, pscale); dkt[2] = mfma32b<2, 0>(qa, pS, dkt[2], qsw, sscale); }
-          if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pP, dvt[3], dosw, pscale); dkt[3] = mfma32b<3, 0>(qa, pS, dkt[3], qsw, sscale); }
-        }
-      }
+      // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
+      auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+      auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+      auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+      auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+      *(uint4*)prow = make_uint4(a02[0], a02[1], a13[0], a13[1]);
+      *(uint4*)srow = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+      if (g == 0) sPs[ta][32 * kb + n] = kp;
+      if (lane == 0) sDSs[ta][kb] = ks2;
     } else {
-      // keys entirely after this query tile (or past the sequence): their dS is zero
+      // keys entirely after these queries (or past either end): P and dS are zero
       const uint4 z = make_uint4(0, 0, 0, 0);
-      uint8_t* rowp = sDS + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
-      *(uint4*)rowp = z;
-      *(uint4*)(rowp + 16) = z;
-      if (lane == 0) {
-        sDSs[0][w] = 0;
-        sDSs[1][w] = 0;
-      }
+      *(uint4*)prow = z;
+      *(uint4*)srow = z;
+      if (g == 0) sPs[ta][32 * kb + n] = 1;
+      if (lane == 0) sDSs[ta][kb] = 1;
     }
     __syncthreads();
 
-    // ---- dQ for (query block t, feature chunk dc) pairs, shared out among the waves.
+    // ---- B. dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries)
+    if (kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1)) {
+      const uint8_t* pr = sP + (32 * kb + n) * SST + 16 * g;
+      const uint8_t* sr = sDS + (32 * kb + n) * SST + 16 * g;
+      const v8i pP = pack8b(*(const uint4*)pr, *(const uint4*)(pr + 32));
+      const v8i pS = pack8b(*(const uint4*)sr, *(const uint4*)(sr + 32));
+      const int pscale = sPs[g][32 * kb + n];
+      const int sscale = sDSs[g][kb];
+      const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int dc = ta * CPW + c;
+        const uint32_t dosw = dow >> (8 * dc), qsw = qw >> (8 * dc);
+        const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
+        const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
+        dvt[c] = mfma32b<0, 0>(oa, pP, dvt[c], dosw, pscale);
+        dkt[c] = mfma32b<0, 0>(qa, pS, dkt[c], qsw, sscale);
+        dosw_prev = dosw;
+        qsw_prev = qsw;
+      }
+      psc_prev = pscale;
+      ssc_prev = sscale;
+    }
+
+    // ---- C. dQ for (query block t, feature chunk dc) = (w / ND, w % ND).
     // Output element i of lane l: query 32t + 8(i/4) + 4g + i%4, feature 32 dc + l%32, so a
     // wave's atomics run along contiguous features of a few query rows.
-    for (int cb = w; cb < 2 * ND; cb += NW) {
-      const int t = cb / ND, dc = cb % ND;
-      if (q0 + 32 * t >= L) continue;
-      v16f acc = v16f{};
-      v8i ka[BN / 64], sb[BN / 64];
-      int kscale[BN / 64], sscale[BN / 64];
+    if (w < 2 * ND) {
+      const int t = w / ND, dc = w % ND;
+      if (q0 + 32 * t < L) {
+        v16f acc = v16f{};
+        int kscale[2], sscale[2];
 #pragma unroll
-      for (int kk = 0; kk < BN / 64; ++kk) {
-        sb[kk] = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-        ka[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features, K: keys
-        sscale[kk] = (int)sDSs[t][2 * kk + g];
-        kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-        if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-        acc = mfma32b<0, 0>(sb[kk], ka[kk], acc, sscale[kk], kscale[kk]);
-      }
-      keep(acc[0]);
+        for (int kk = 0; kk < 2; ++kk) {
+          sscale[kk] = sDSs[t][2 * kk + g];
+          kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
+          if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
+          const v8i sb = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+          const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features, K: keys
+          acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
+        }
+        keep(acc[0]);
+        keep(kscale[0]); keep(kscale[1]); keep(sscale[0]); keep(sscale[1]);
+        // pair neighbouring lanes: the even lane of a pair adds (row, f..f+1) of element i, the
+        // odd lane (row + 1, f-1..f) of element i + 1
+        const bool odd = lane & 1;
+        const uint32_t om = odd ? ~0u : 0u;   // bit selects (a select of vector elements becomes indexing)
+        const int fcol = 32 * dc + n - (odd ? 1 : 0);
 #pragma unroll
-      for (int kk = 0; kk < BN / 64; ++kk) {
-        keep(kscale[kk]);
-        keep(sscale[kk]);
-      }
-      // pair neighbouring lanes: the even lane of a pair adds (row, f..f+1) of element i, the
-      // odd lane (row + 1, f-1..f) of element i + 1
-      const bool odd = lane & 1;
-      const int fcol = 32 * dc + n - (odd ? 1 : 0);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float mine = odd ? acc[i + 1] : acc[i];
-        const float send = odd ? acc[i] : acc[i + 1];
-        const float got = __shfl_xor(send, 1, 64);
-        const int ql = 32 * t + 8 * (i >> 2) + 4 * g + (i & 3) + (odd ? 1 : 0);
-        const int qi = q0 + ql;
-        if (qi < L) {
-          _Float16* ap = (_Float16*)a.acc + (long)(tok0 + qi) * rowH + (long)h * D + fcol;
-          if (odd) atomic_add_h2(ap, got * a.dq_mult, mine * a.dq_mult);
-          else atomic_add_h2(ap, mine * a.dq_mult, got * a.dq_mult);
+        for (int i = 0; i < 16; i += 2) {
+          const uint32_t x0 = __float_as_uint(acc[i]), x1 = __float_as_uint(acc[i + 1]);
+          const float mine = __uint_as_float((x1 & om) | (x0 & ~om));
+          const float send = __uint_as_float((x0 & om) | (x1 & ~om));
+          const float got = __shfl_xor(send, 1, 64);
+          const int qi = q0 + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3) + (odd ? 1 : 0);
+          if (qi < L) {
+            _Float16* ap = (_Float16*)a.acc + (long)(tok0 + qi) * rowH + (long)h * D + fcol;
+            if (odd) atomic_add_h2(ap, got * a.dq_mult, mine * a.dq_mult);
+            else atomic_add_h2(ap, mine * a.dq_mult, got * a.dq_mult);
+          }
         }
       }
     }
+
+    store_step(qn, buf ^ 1, nx);
+    __syncthreads();
   }
 
   // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
-  keep(dvt[ND - 1][0]);
-  keep(dkt[ND - 1][0]);
+  keep(dvt[CPW - 1][0]);
+  keep(dkt[CPW - 1][0]);
   keep(dosw_prev); keep(qsw_prev); keep(psc_prev); keep(ssc_prev);
   if (kj >= L) return;
   const long orow = (long)(tok0 + kj) * rowH + (long)h * D;
 #pragma unroll
-  for (int dc = 0; dc < ND; ++dc)
+  for (int c = 0; c < CPW; ++c)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int d = 32 * dc + 8 * q + 4 * g;
-      const float k0 = dkt[dc][4 * q] * a.sigma, k1 = dkt[dc][4 * q + 1] * a.sigma, k2 = dkt[dc][4 * q + 2] * a.sigma,
-                  k3 = dkt[dc][4 * q + 3] * a.sigma;
-      const float v0 = dvt[dc][4 * q], v1 = dvt[dc][4 * q + 1], v2 = dvt[dc][4 * q + 2], v3 = dvt[dc][4 * q + 3];
+      const int d = 32 * (ta * CPW + c) + 8 * q + 4 * g;
+      const float k0 = dkt[c][4 * q] * a.sigma, k1 = dkt[c][4 * q + 1] * a.sigma, k2 = dkt[c][4 * q + 2] * a.sigma,
+                  k3 = dkt[c][4 * q + 3] * a.sigma;
+      const float v0 = dvt[c][4 * q], v1 = dvt[c][4 * q + 1], v2 = dvt[c][4 * q + 2], v3 = dvt[c][4 * q + 3];
       if (a.grad_f32) {
         *(float4*)((float*)a.dk + orow + d) = make_float4(k0, k1, k2, k3);
         *(float4*)((float*)a.dv + orow + d) = make_float4(v0, v1, v2, v3);
@@ -446,13 +481,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n8) {
   }
 }
 
-template __global__ void attn_bwd_kernel<64, 4, true>(BwdArgs);
-template __global__ void attn_bwd_kernel<64, 4, false>(BwdArgs);
-template __global__ void attn_bwd_kernel<128, 4, true>(BwdArgs);
-template __global__ void attn_bwd_kernel<128, 4, false>(BwdArgs);
+template __global__ void attn_bwd_kernel<64, true>(BwdArgs);
+template __global__ void attn_bwd_kernel<64, false>(BwdArgs);
+template __global__ void attn_bwd_kernel<128, true>(BwdArgs);
+template __global__ void attn_bwd_kernel<128, false>(BwdArgs);
 
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st) {
-  constexpr int NW = 4;
   const long rows = (long)a.T * a.H;
   if (rows == 0) return hipSuccess;
   // 1. D_i and zeroed accumulator
@@ -470,14 +504,15 @@ hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_l
   }
   // 2. main
   {
-    a.nkt = (max_len + 32 * NW - 1) / (32 * NW);
+    constexpr int BN = 128;
+    a.nkt = (max_len + BN - 1) / BN;
     const long units = (long)a.nseq * a.H;
     const long grid = ((units + 7) / 8) * 8 * a.nkt;
-    dim3 g((unsigned)grid), b(NW * 64);
-    if (D == 64 && causal) attn_bwd_kernel<64, NW, true><<<g, b, 0, st>>>(a);
-    else if (D == 64) attn_bwd_kernel<64, NW, false><<<g, b, 0, st>>>(a);
-    else if (causal) attn_bwd_kernel<128, NW, true><<<g, b, 0, st>>>(a);
-    else attn_bwd_kernel<128, NW, false><<<g, b, 0, st>>>(a);
+    dim3 g((unsigned)grid), b(512);
+    if (D == 64 && causal) attn_bwd_kernel<64, true><<<g, b, 0, st>>>(a);
+    else if (D == 64) attn_bwd_kernel<64, false><<<g, b, 0, st>>>(a);
+    else if (causal) attn_bwd_kernel<128, true><<<g, b, 0, st>>>(a);
+    else attn_bwd_kernel<128, false><<<g, b, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
