@@ -26,6 +26,8 @@
 //     orientations: rows as MFMA operands, columns through
 //     ds_read_b64_tr_b8 (one payload, both GEMMs).
 //  3. bwd_dq_kernel: dQ = acc * 2^-s in the output type.
+#include <type_traits>
+
 #include "mx_common.h"
 #include "mx_launch.h"
 
@@ -63,11 +65,8 @@ MX_DEV uint32_t ld_scale_word(const uint8_t* p, int nbytes) {
   return nbytes == 4 ? *(const uint32_t*)p : *(const uint16_t*)p;
 }
 
-MX_DEV float wave_max_all(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+// p in [0, inf) clamped to lim (one v_med3; p is never NaN)
+MX_DEV float clampp(float p, float lim) { return __builtin_amdgcn_fmed3f(p, 0.f, lim); }
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
@@ -162,7 +161,8 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   __shared__ int sPs[2][BN];               // P scale code of (query block, key)
   __shared__ int sDSs[2][4];               // dS scale code of (query block, key block)
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int id = blockIdx.x, xcd = id & 7, jj = id >> 3;
   const int u = (jj / a.nkt) * 8 + xcd;
   if (u >= a.nseq * a.H) return;
@@ -306,23 +306,31 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       }
       // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D)
       const bool need_mask = qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+      // element i is query qa0 + 4g + c_i, c_i = 8(i/4) + i%4: visible iff lo <= c_i < hi
+      const int lo = kj >= L ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
+      const int hi = L - qa0 - 4 * g;
       float am = -INFINITY, sm = 0.f;
+      // two copies of the elementwise pass: with the mask (diagonal and edge blocks) and without
+      auto pass = [&](auto masked) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float arg = fmaf(st[i], cl, -lv[i]);
-        if (need_mask) {
-          const int qi = qa0 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (qi >= L || kj >= L || (CAUSAL && kj > qi)) arg = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          float arg = fmaf(st[i], cl, -lv[i]);
+          if constexpr (decltype(masked)::value) {
+            const int ci = 8 * (i >> 2) + (i & 3);
+            arg = (ci >= lo && ci < hi) ? arg : -INFINITY;
+          }
+          const float p = __builtin_amdgcn_exp2f(arg);
+          const float ds = p * (dpt[i] - dv[i]);
+          st[i] = p;
+          dpt[i] = ds;
+          am = fmaxf(am, arg);
+          sm = fmaxf(sm, fabsf(ds));
         }
-        const float p = __builtin_amdgcn_exp2f(arg);
-        const float ds = p * (dpt[i] - dv[i]);
-        st[i] = p;
-        dpt[i] = ds;
-        am = fmaxf(am, arg);
-        sm = fmaxf(sm, fabsf(ds));
-      }
-      const float amax = fmaxf(am, __shfl_xor(am, 32, 64));   // 32 queries of this key
-      const float smax = wave_max_all(sm);                      // 32 queries x 32 keys
+      };
+      if (need_mask) pass(std::true_type{});
+      else pass(std::false_type{});
+      const float amax = half_swap_max(am);   // 32 queries of this key
+      const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
       // S and dP have been read: their products and the previous step's dV, dK products are done
       keep(qsa); keep(dsa); keep(ksc); keep(vsc);
       keep(dosw_prev); keep(qsw_prev); keep(psc_prev); keep(ssc_prev);
@@ -335,8 +343,8 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v2s z = {0, 0};
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[4 * q], plim), fminf(st[4 * q + 1], plim), psc, false);
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[4 * q + 2], plim), fminf(st[4 * q + 3], plim), psc, true);
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc, false);
+        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim), psc, true);
         pw[q] = __builtin_bit_cast(uint32_t, z);
         v2s y = {0, 0};
         y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
@@ -409,22 +417,30 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         keep(kscale[0]); keep(kscale[1]); keep(sscale[0]); keep(sscale[1]);
         // pair neighbouring lanes: the even lane of a pair adds (row, f..f+1) of element i, the
         // odd lane (row + 1, f-1..f) of element i + 1
-        const bool odd = lane & 1;
-        const uint32_t om = odd ? ~0u : 0u;   // bit selects (a select of vector elements becomes indexing)
-        const int fcol = 32 * dc + n - (odd ? 1 : 0);
+        // lanes pair up: the even lane adds (row r, features f, f+1) of element i, the odd lane
+        // (row r + 1, features f-1, f) of element i + 1; each sends the value its partner needs
+        const int odd = lane & 1;
+        // wave-uniform base at (query q0 + 32t, feature 32 dc); 32-bit lane offsets in halves
+        _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc);
+        const uint32_t rh = (uint32_t)rowH;
+        const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
+        const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_i below this are in range
+        const float mult = a.dq_mult;
+        auto add_tile = [&](auto checked) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const uint32_t x0 = __float_as_uint(acc[i]), x1 = __float_as_uint(acc[i + 1]);
-          const float mine = __uint_as_float((x1 & om) | (x0 & ~om));
-          const float send = __uint_as_float((x0 & om) | (x1 & ~om));
-          const float got = __shfl_xor(send, 1, 64);
-          const int qi = q0 + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3) + (odd ? 1 : 0);
-          if (qi < L) {
-            _Float16* ap = (_Float16*)a.acc + (long)(tok0 + qi) * rowH + (long)h * D + fcol;
-            if (odd) atomic_add_h2(ap, got * a.dq_mult, mine * a.dq_mult);
-            else atomic_add_h2(ap, mine * a.dq_mult, got * a.dq_mult);
+          for (int i = 0; i < 16; i += 2) {
+            const float x0 = acc[i], x1 = acc[i + 1];
+            const float send = odd ? x0 : x1;
+            const float got = __int_as_float(
+                __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
+            const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
+            const int ci = 8 * (i >> 2) + (i & 3);
+            if (!decltype(checked)::value || ci < rows_left)
+              atomic_add_h2(abase + (lofs + (uint32_t)ci * rh), lo_v * mult, hi_v * mult);
           }
-        }
+        };
+        if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
+        else add_tile(std::true_type{});
       }
     }
 

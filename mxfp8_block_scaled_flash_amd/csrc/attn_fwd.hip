@@ -47,6 +47,9 @@ MX_DEV v8i pack8(uint4 lo, uint4 hi) {
   return r;
 }
 
+// p in [0, inf) clamped to lim (one v_med3; p is never NaN)
+MX_DEV float clampp(float p, float lim) { return __builtin_amdgcn_fmed3f(p, 0.f, lim); }
+
 MX_DEV v2i lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
   __shared__ uint32_t sVs[2][64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
   // ---- work decode: XCD x = id % 8 takes (sequence, head) units x, x+8, ...;
   // within a unit, the longest query tile first.
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         float m = st[kb][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
-        bm[kb] = wave_max_xor(m, 32);
+        bm[kb] = half_swap_max(m);
       }
       // S has been read: this tile's S products and the previous tile's P V products are done
       keep(ksc[0]);
@@ -256,10 +260,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v2s z = {0, 0};
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q], lim[kb]), fminf(st[kb][4 * q + 1], lim[kb]),
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q], lim[kb]), clampp(st[kb][4 * q + 1], lim[kb]),
                                                        sc[kb], false);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, fminf(st[kb][4 * q + 2], lim[kb]),
-                                                       fminf(st[kb][4 * q + 3], lim[kb]), sc[kb], true);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q + 2], lim[kb]),
+                                                       clampp(st[kb][4 * q + 3], lim[kb]), sc[kb], true);
           dw[kb][q] = __builtin_bit_cast(uint32_t, z);
         }
       // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order

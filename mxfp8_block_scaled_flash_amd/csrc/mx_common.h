@@ -73,6 +73,33 @@ MX_DEV uint32_t f32_to_bf16(float f) {
 
 MX_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
+// max of v and the value of the lane 32 apart (v_permlane32_swap exchanges the wave's halves)
+MX_DEV float half_swap_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int CTRL>
+MX_DEV int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide max of non-negative floats.  Their bit patterns order like the
+// values, so the reduction runs on integers: DPP within rows of 16 lanes
+// (quad swaps, half-row and row mirrors), then v_permlane16_swap and
+// v_permlane32_swap across rows.
+MX_DEV float wave_max_nonneg(float f) {
+  int v = __float_as_int(f);
+  v = max(v, dpp_i32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_i32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_i32<0x141>(v));   // row_half_mirror
+  v = max(v, dpp_i32<0x140>(v));   // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return __int_as_float(max((int)b[0], (int)b[1]));
+}
+
 // The scaled MFMA reads its operand registers (data and E8M0 scales) over the
 // passes of the instruction, and the compiler may hand those registers to
 // other values as soon as the instruction has issued.  keep() pins values in
