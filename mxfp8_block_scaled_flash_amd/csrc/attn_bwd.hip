@@ -121,17 +121,22 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ main kernel
 // One workgroup of eight waves per (sequence, head, 128-key tile), walking
-// 64-query steps.  Per step:
-//   A. wave w computes S and dP for key block w%4 and query block w/4
-//      (32 x 32), p and dS, their MX codes (P: one scale per key and 32
-//      queries; dS: one scale per square block), stored in LDS as [key][query];
-//   B. wave w accumulates dV^T and dK^T (all 64 queries of contraction) for
-//      key block w%4 and D/64 of the 32-feature chunks, reading the codes back;
-//   C. wave w < 2D/32 forms dQ for one (query block, feature chunk) from all
-//      128 keys and adds it to the fp16 accumulator with packed atomics.
-// The next step's Q / dO tiles, scales, LSE and D are loaded into registers
-// while this step computes and written to the other LDS buffer at its end:
-// two barriers per step.
+// 64-query steps as a two-stage pipeline, one barrier per stage interval:
+//  * producer waves 0-3 (wave w owns key block w, K^ and V^ rows in registers)
+//    compute, for step i, S and dP for their 32 keys x 64 queries (keys as the
+//    output columns: lane = one key), p and dS, and their MX codes (P: one
+//    scale per key and 32 queries; dS: one scale per square 32 x 32 block),
+//    stored in LDS as [key][query] with the scales;
+//  * consumer waves 4-7 take step i - 1 meanwhile: wave 4 + b accumulates
+//    dV^T and dK^T for key block b (all D features, 64 queries of
+//    contraction, codes read back from LDS, Q^T and dO^T through transpose
+//    reads), then forms D/64 of the 32 x 32 (query block, feature chunk)
+//    tiles of dQ = dS^ K^ over the 128 keys and adds them to the fp16
+//    accumulator with packed atomics.
+// A producer and a consumer share each SIMD, so one's softmax work overlaps
+// the other's MFMAs.  Q^ / dO^ tiles, scales, LSE and D rotate through three
+// LDS buffers (step being produced, step being consumed, step being loaded
+// from HBM by the producers), the codes through two.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int NW = 8;
@@ -139,27 +144,26 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int BQ = 64;        // queries per step
   constexpr int NC = D / 64;    // 64-feature chunks of the S / dP contraction
   constexpr int ND = D / 32;    // 32-feature chunks of dK, dV, dQ
-  constexpr int CPW = ND / 2;   // dV / dK chunks per wave
+  constexpr int TPW = ND / 2;   // dQ tiles per consumer wave (2 ND tiles over 4 waves)
   constexpr int NB = D / 32;    // scale bytes per SQ32 / ROW32 scale word
   constexpr int KST = D + 16;   // LDS row stride of K, Q, dO tiles
   constexpr int SST = BQ + 16;  // LDS row stride of the P and dS code tiles [key][query]
   constexpr int NT = NW * 64;
+  constexpr int NTP = 256;            // producer threads: they alone load and stage the query steps
   constexpr int QCH = BQ * D / 16;    // 16-byte chunks of one Q (or dO) tile
-  constexpr int CPT = 2 * QCH / NT;   // chunks of Q and dO per thread per step
-  static_assert(2 * QCH % NT == 0, "chunks must divide among the threads");
+  constexpr int CPT = 2 * QCH / NTP;  // chunks of Q and dO per producer thread per step
+  static_assert(2 * QCH % NTP == 0, "chunks must divide among the threads");
   __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sP[BN * SST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDS[BN * SST];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
-  __shared__ uint32_t sKs[4];
-  __shared__ uint32_t sVs[BN];             // V ROW32 scale word per key              // K SQ32 scale word (bytes = feature blocks) per key block
-  __shared__ uint32_t sQs[2][2], sDOs[2][2];   // [buffer][query block]
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];    // LSE log2(e)
-  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];   // D
-  __shared__ int sPs[2][BN];               // P scale code of (query block, key)
-  __shared__ int sDSs[2][4];               // dS scale code of (query block, key block)
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[3][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sDO[3][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[2][BN * SST];
+  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * SST];
+  __shared__ uint32_t sKs[4];                  // K SQ32 scale word (bytes = feature blocks) per key block
+  __shared__ uint32_t sQs[3][2], sDOs[3][2];   // [buffer][query block]
+  __shared__ __attribute__((aligned(16))) float sL[3][BQ];    // LSE log2(e)
+  __shared__ __attribute__((aligned(16))) float sDv[3][BQ];   // D
+  __shared__ int sPs[2][2][BN];                // P scale code of (query block, key)
+  __shared__ int sDSs[2][2][4];                // dS scale code of (query block, key block)
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -173,10 +177,9 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int kbase = kt * BN;
   if (kbase >= L) return;
   const long rowH = (long)a.H * D;
-  const int kb = w & 3;               // key block of phases A and B
-  const int ta = w >> 2;              // query block of phase A
+  const int kb = w & 3;               // this wave's key block (both roles)
   const int kw0 = kbase + 32 * kb;
-  const int kj = kw0 + n;             // this lane's key in phases A and B
+  const int kj = kw0 + n;             // this lane's key
 
   // ---- K tile (all keys of the workgroup) for the dQ products, and scales
   for (int ch = tid; ch < BN * D / 16; ch += NT) {
@@ -190,17 +193,11 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     if (kbase + 32 * tid < L) wk = ld_scale_word(a.ks + ((long)(sblk0 + kbase / 32 + tid) * a.H + h) * NB, NB);
     sKs[tid] = wk;
   }
-  // ---- V tile for the dP products (K comes from the tile above), and V's scales
-  for (int ch = tid; ch < BN * D / 16; ch += NT) {
-    const int r = ch / (D / 16), cx = ch % (D / 16);
-    uint4 vv = make_uint4(0, 0, 0, 0);
-    if (kbase + r < L) vv = *(const uint4*)(a.v + (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16);
-    *(uint4*)(sV + r * KST + cx * 16) = vv;
-  }
-  if (tid < BN) sVs[tid] = (kbase + tid < L) ? ld_scale_word(a.vs + ((long)(srow0 + kbase + tid) * a.H + h) * NB, NB) : 0u;
 
-  // ---- staging of one query step.  Loads are branch-free: rows past the end
-  // are clamped to the last query and zeroed (or masked later) when stored.
+  // ---- staging of one query step, by the producer waves (the consumers issue
+  // the dQ atomics; a wait for staged loads there would also wait for those).
+  // Loads are branch-free: rows past the end are clamped to the last query and
+  // zeroed (or masked later) when stored.
   struct Stage {
     uint4 x[CPT];
     float l, d;
@@ -212,7 +209,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   auto load_step = [&](int q0, Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
+      const int ch = tid + c * NTP;
       const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
       const long off = (long)(tok0 + min(q0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
       st.x[c] = *(const uint4*)((ch < QCH ? a.q : a.dob) + off);
@@ -227,7 +224,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   auto store_step = [&](int q0, int buf, const Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
+      const int ch = tid + c * NTP;
       const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
       const uint32_t m = (q0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
       const uint4 x = st.x[c];
@@ -244,234 +241,266 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     }
   };
 
-  v16f dvt[CPW], dkt[CPW];   // dV^T, dK^T: element i = feature 32 dc + 8(i/4) + 4g + i%4, key kj
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    dvt[c] = v16f{};
-    dkt[c] = v16f{};
-  }
-  const float cl = a.c;
   const int qstart = CAUSAL ? (kbase / BQ) * BQ : 0;
   const int nsteps = (L - qstart + BQ - 1) / BQ;
-  // scale operands of the last dV / dK products, pinned until those products finish
-  uint32_t dosw_prev = 0, qsw_prev = 0;
-  int psc_prev = 0, ssc_prev = 0;
-
-  {
+  if (w < 4) {
     Stage st0;
     load_step(qstart, st0);
     store_step(qstart, 0, st0);
   }
   __syncthreads();
 
-  for (int j = 0; j < nsteps; ++j) {
-    const int q0 = qstart + j * BQ, buf = j & 1;
-    const uint8_t* sQb = sQ[buf];
-    const uint8_t* sDOb = sDO[buf];
-    // the next step's operands are in flight while this one is computed (after
-    // the last step, the last one is fetched again and its buffer rewritten)
-    const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
-    Stage nx;
-    load_step(qn, nx);
-
-    // ---- A. S and dP for (key block kb, query block ta): element i = query qa0 + 8(i/4) + 4g + i%4, key kj
-    const int qa0 = q0 + 32 * ta;
-    uint8_t* prow = sP + (32 * kb + n) * SST + 32 * ta + 16 * g;
-    uint8_t* srow = sDS + (32 * kb + n) * SST + 32 * ta + 16 * g;
-    if (kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31)) {
-      const uint8_t* qp = sQb + (32 * ta + n) * KST + 16 * g;
-      const uint8_t* op = sDOb + (32 * ta + n) * KST + 16 * g;
-      const uint32_t qsa = sQs[buf][ta] >> (8 * g), dsa = sDOs[buf][ta] >> (8 * g);
-      v16f st = v16f{}, dpt = v16f{};
-      const uint8_t* kr = sK + (32 * kb + n) * KST + 16 * g;
-      const uint8_t* vr = sV + (32 * kb + n) * KST + 16 * g;
-      const uint32_t ksc = sKs[kb] >> (8 * g), vsc = sVs[32 * kb + n] >> (8 * g);
-      st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
-                         pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), st, qsa, ksc);
-      dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
-                          pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), dpt, dsa, vsc);
-      if constexpr (NC > 1) {
-        st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
-                           pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
-        dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
-                            pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
-      }
-      float lv[16], dv[16];
+  // Both roles run nsteps + 1 intervals with one barrier each: interval i
+  // produces step i, consumes step i - 1 and loads step i + 1 (past the last
+  // step, the last one is fetched again and its buffer rewritten with the same
+  // bytes, which keeps the loads free of branches).
+  if (w < 4) {
+    // ================================================================ producer
+    const float cl = a.c;
+    v8i kop[NC], vop[NC];
+    uint32_t ksc = 0, vsc = 0;
+    if (kj < L) {
+      const uint8_t* kp = a.k + (long)(tok0 + kj) * rowH + (long)h * D;
+      const uint8_t* vp = a.v + (long)(tok0 + kj) * rowH + (long)h * D;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 l4 = *(const float4*)(&sL[buf][32 * ta + 8 * q + 4 * g]);
-        const float4 d4 = *(const float4*)(&sDv[buf][32 * ta + 8 * q + 4 * g]);
-        lv[4 * q] = l4.x; lv[4 * q + 1] = l4.y; lv[4 * q + 2] = l4.z; lv[4 * q + 3] = l4.w;
-        dv[4 * q] = d4.x; dv[4 * q + 1] = d4.y; dv[4 * q + 2] = d4.z; dv[4 * q + 3] = d4.w;
+      for (int c = 0; c < NC; ++c) {
+        kop[c] = pack8b(*(const uint4*)(kp + 64 * c + 16 * g), *(const uint4*)(kp + 64 * c + 32 + 16 * g));
+        vop[c] = pack8b(*(const uint4*)(vp + 64 * c + 16 * g), *(const uint4*)(vp + 64 * c + 32 + 16 * g));
       }
-      // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D)
-      const bool need_mask = qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
-      // element i is query qa0 + 4g + c_i, c_i = 8(i/4) + i%4: visible iff lo <= c_i < hi
-      const int lo = kj >= L ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
-      const int hi = L - qa0 - 4 * g;
-      float am = -INFINITY, sm = 0.f;
-      // two copies of the elementwise pass: with the mask (diagonal and edge blocks) and without
-      auto pass = [&](auto masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float arg = fmaf(st[i], cl, -lv[i]);
-          if constexpr (decltype(masked)::value) {
-            const int ci = 8 * (i >> 2) + (i & 3);
-            arg = (ci >= lo && ci < hi) ? arg : -INFINITY;
-          }
-          const float p = __builtin_amdgcn_exp2f(arg);
-          const float ds = p * (dpt[i] - dv[i]);
-          st[i] = p;
-          dpt[i] = ds;
-          am = fmaxf(am, arg);
-          sm = fmaxf(sm, fabsf(ds));
-        }
-      };
-      if (need_mask) pass(std::true_type{});
-      else pass(std::false_type{});
-      const float amax = half_swap_max(am);   // 32 queries of this key
-      const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
-      // S and dP have been read: their products and the previous step's dV, dK products are done
-      keep(qsa); keep(dsa); keep(ksc); keep(vsc);
-      keep(dosw_prev); keep(qsw_prev); keep(psc_prev); keep(ssc_prev);
-      // ---- MX codes: dword q holds queries 8q + 4g + 0..3
-      const int kp = max(exp2_scale_code(amax), 1);
-      const int ks2 = max(scale_code(smax), 1);
-      const float psc = e8m0_f32(kp), plim = 448.f * psc;
-      const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
-      uint32_t pw[4], sw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v2s z = {0, 0};
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc, false);
-        z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim), psc, true);
-        pw[q] = __builtin_bit_cast(uint32_t, z);
-        v2s y = {0, 0};
-        y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
-                                                     __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc, false);
-        y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
-                                                     __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc, true);
-        sw[q] = __builtin_bit_cast(uint32_t, y);
-      }
-      // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
-      auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-      auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-      auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
-      auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
-      *(uint4*)prow = make_uint4(a02[0], a02[1], a13[0], a13[1]);
-      *(uint4*)srow = make_uint4(b02[0], b02[1], b13[0], b13[1]);
-      if (g == 0) sPs[ta][32 * kb + n] = kp;
-      if (lane == 0) sDSs[ta][kb] = ks2;
+      ksc = ld_scale_word(a.ks + ((long)(sblk0 + kw0 / 32) * a.H + h) * NB, NB) >> (8 * g);
+      vsc = ld_scale_word(a.vs + ((long)(srow0 + kj) * a.H + h) * NB, NB) >> (8 * g);
     } else {
-      // keys entirely after these queries (or past either end): P and dS are zero
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      *(uint4*)prow = z;
-      *(uint4*)srow = z;
-      if (g == 0) sPs[ta][32 * kb + n] = 1;
-      if (lane == 0) sDSs[ta][kb] = 1;
-    }
-    __syncthreads();
-
-    // ---- B. dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries)
-    if (kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1)) {
-      const uint8_t* pr = sP + (32 * kb + n) * SST + 16 * g;
-      const uint8_t* sr = sDS + (32 * kb + n) * SST + 16 * g;
-      const v8i pP = pack8b(*(const uint4*)pr, *(const uint4*)(pr + 32));
-      const v8i pS = pack8b(*(const uint4*)sr, *(const uint4*)(sr + 32));
-      const int pscale = sPs[g][32 * kb + n];
-      const int sscale = sDSs[g][kb];
-      const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        const int dc = ta * CPW + c;
-        const uint32_t dosw = dow >> (8 * dc), qsw = qw >> (8 * dc);
-        const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
-        const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
-        dvt[c] = mfma32b<0, 0>(oa, pP, dvt[c], dosw, pscale);
-        dkt[c] = mfma32b<0, 0>(qa, pS, dkt[c], qsw, sscale);
-        dosw_prev = dosw;
-        qsw_prev = qsw;
+      for (int c = 0; c < NC; ++c) {
+        kop[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        vop[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       }
-      psc_prev = pscale;
-      ssc_prev = sscale;
     }
-
-    // ---- C. dQ for (query block t, feature chunk dc) = (w / ND, w % ND).
-    // Output element i of lane l: query 32t + 8(i/4) + 4g + i%4, feature 32 dc + l%32, so a
-    // wave's atomics run along contiguous features of a few query rows.
-    if (w < 2 * ND) {
-      const int t = w / ND, dc = w % ND;
-      if (q0 + 32 * t < L) {
-        v16f acc = v16f{};
-        int kscale[2], sscale[2];
+    for (int i = 0; i <= nsteps; ++i) {
+      const int qn = qstart + min(i + 1, nsteps - 1) * BQ;
+      Stage nx;
+      load_step(qn, nx);
+      if (i < nsteps) {
+        const int q0 = qstart + i * BQ, qb = i % 3, pb = i & 1;
+        const uint8_t* sQb = sQ[qb];
+        const uint8_t* sDOb = sDO[qb];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          sscale[kk] = sDSs[t][2 * kk + g];
-          kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-          if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-          const v8i sb = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-          const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features, K: keys
-          acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
-        }
-        keep(acc[0]);
-        keep(kscale[0]); keep(kscale[1]); keep(sscale[0]); keep(sscale[1]);
-        // pair neighbouring lanes: the even lane of a pair adds (row, f..f+1) of element i, the
-        // odd lane (row + 1, f-1..f) of element i + 1
-        // lanes pair up: the even lane adds (row r, features f, f+1) of element i, the odd lane
-        // (row r + 1, features f-1, f) of element i + 1; each sends the value its partner needs
-        const int odd = lane & 1;
-        // wave-uniform base at (query q0 + 32t, feature 32 dc); 32-bit lane offsets in halves
-        _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc);
-        const uint32_t rh = (uint32_t)rowH;
-        const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
-        const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_i below this are in range
-        const float mult = a.dq_mult;
-        auto add_tile = [&](auto checked) {
+        for (int t = 0; t < 2; ++t) {
+          // ---- S and dP for (key block kb, query block t): element e = query qa0 + 8(e/4) + 4g + e%4, key kj
+          const int qa0 = q0 + 32 * t;
+          uint8_t* prow = sP[pb] + (32 * kb + n) * SST + 32 * t + 16 * g;
+          uint8_t* srow = sDS[pb] + (32 * kb + n) * SST + 32 * t + 16 * g;
+          if (kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31)) {
+            const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
+            const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
+            const uint32_t qsa = sQs[qb][t] >> (8 * g), dsa = sDOs[qb][t] >> (8 * g);
+            v16f st = v16f{}, dpt = v16f{};
+            st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)), kop[0], st, qsa, ksc);
+            dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), vop[0], dpt, dsa, vsc);
+            if constexpr (NC > 1) {
+              st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)), kop[NC - 1], st, qsa,
+                                 ksc);
+              dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)), vop[NC - 1], dpt, dsa,
+                                  vsc);
+            }
+            float lv[16], dv[16];
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            const float x0 = acc[i], x1 = acc[i + 1];
-            const float send = odd ? x0 : x1;
-            const float got = __int_as_float(
-                __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
-            const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
-            const int ci = 8 * (i >> 2) + (i & 3);
-            if (!decltype(checked)::value || ci < rows_left)
-              atomic_add_h2(abase + (lofs + (uint32_t)ci * rh), lo_v * mult, hi_v * mult);
+            for (int q = 0; q < 4; ++q) {
+              const float4 l4 = *(const float4*)(&sL[qb][32 * t + 8 * q + 4 * g]);
+              const float4 d4 = *(const float4*)(&sDv[qb][32 * t + 8 * q + 4 * g]);
+              lv[4 * q] = l4.x; lv[4 * q + 1] = l4.y; lv[4 * q + 2] = l4.z; lv[4 * q + 3] = l4.w;
+              dv[4 * q] = d4.x; dv[4 * q + 1] = d4.y; dv[4 * q + 2] = d4.z; dv[4 * q + 3] = d4.w;
+            }
+            // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D)
+            const bool need_mask = qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+            // element i is query qa0 + 4g + c_i, c_i = 8(i/4) + i%4: visible iff lo <= c_i < hi
+            const int lo = kj >= L ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
+            const int hi = L - qa0 - 4 * g;
+            float am = -INFINITY, sm = 0.f;
+            // two copies of the elementwise pass: with the mask (diagonal and edge blocks) and without
+            auto pass = [&](auto masked) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                float arg = fmaf(st[e], cl, -lv[e]);
+                if constexpr (decltype(masked)::value) {
+                  const int ci = 8 * (e >> 2) + (e & 3);
+                  arg = (ci >= lo && ci < hi) ? arg : -INFINITY;
+                }
+                const float p = __builtin_amdgcn_exp2f(arg);
+                const float ds = p * (dpt[e] - dv[e]);
+                st[e] = p;
+                dpt[e] = ds;
+                am = fmaxf(am, arg);
+                sm = fmaxf(sm, fabsf(ds));
+              }
+            };
+            if (need_mask) pass(std::true_type{});
+            else pass(std::false_type{});
+            const float amax = half_swap_max(am);   // 32 queries of this key
+            const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
+            // S and dP have been read: their products are done
+            keep(qsa); keep(dsa); keep(ksc); keep(vsc);
+            // ---- MX codes: dword q holds queries 8q + 4g + 0..3
+            const int kp = max(exp2_scale_code(amax), 1);
+            const int ks2 = max(scale_code(smax), 1);
+            const float psc = e8m0_f32(kp), plim = 448.f * psc;
+            const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
+            uint32_t pw[4], sw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v2s z = {0, 0};
+              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc,
+                                                           false);
+              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim),
+                                                           psc, true);
+              pw[q] = __builtin_bit_cast(uint32_t, z);
+              v2s y = {0, 0};
+              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
+                                                           __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc,
+                                                           false);
+              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
+                                                           __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc,
+                                                           true);
+              sw[q] = __builtin_bit_cast(uint32_t, y);
+            }
+            // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
+            auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+            auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+            auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+            auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+            *(uint4*)prow = make_uint4(a02[0], a02[1], a13[0], a13[1]);
+            *(uint4*)srow = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+            if (g == 0) sPs[pb][t][32 * kb + n] = kp;
+            if (lane == 0) sDSs[pb][t][kb] = ks2;
+          } else {
+            // keys entirely after these queries (or past either end): P and dS are zero
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            *(uint4*)prow = z;
+            *(uint4*)srow = z;
+            if (g == 0) sPs[pb][t][32 * kb + n] = 1;
+            if (lane == 0) sDSs[pb][t][kb] = 1;
           }
-        };
-        if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
-        else add_tile(std::true_type{});
+        }
       }
+      store_step(qn, (i + 1) % 3, nx);
+      __syncthreads();
+    }
+  } else {
+    // ================================================================ consumer
+    v16f dvt[ND], dkt[ND];   // dV^T, dK^T: element e = feature 32 dc + 8(e/4) + 4g + e%4, key kj
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc) {
+      dvt[dc] = v16f{};
+      dkt[dc] = v16f{};
+    }
+    // scale operands of the last dV / dK products, pinned until those products finish
+    uint32_t dow_prev = 0, qw_prev = 0;
+    int psc_prev = 0, ssc_prev = 0;
+    const int uw = w - 4;
+    for (int i = 0; i <= nsteps; ++i) {
+      if (i > 0) {
+        const int q0 = qstart + (i - 1) * BQ, qb = (i - 1) % 3, pb = (i - 1) & 1;
+        const uint8_t* sQb = sQ[qb];
+        const uint8_t* sDOb = sDO[qb];
+        // ---- dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries)
+        if (kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1)) {
+          const uint8_t* pr = sP[pb] + (32 * kb + n) * SST + 16 * g;
+          const uint8_t* sr = sDS[pb] + (32 * kb + n) * SST + 16 * g;
+          const v8i pP = pack8b(*(const uint4*)pr, *(const uint4*)(pr + 32));
+          const v8i pS = pack8b(*(const uint4*)sr, *(const uint4*)(sr + 32));
+          const int pscale = sPs[pb][g][32 * kb + n];
+          const int sscale = sDSs[pb][g][kb];
+          const uint32_t dow = sDOs[qb][g], qw = sQs[qb][g];
+#pragma unroll
+          for (int dc = 0; dc < ND; ++dc) {
+            const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
+            const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
+            if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pP, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, pS, dkt[0], qw, sscale); }
+            if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pP, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, pS, dkt[1], qw, sscale); }
+            if constexpr (ND > 2) {
+              if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pP, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, pS, dkt[2], qw, sscale); }
+              if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pP, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, pS, dkt[3], qw, sscale); }
+            }
+          }
+          dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
+        }
+        // ---- dQ tiles (t, dc): output element e of lane l is query 32t + 8(e/4) + 4g + e%4,
+        // feature 32 dc + l%32, so a wave's atomics run along contiguous features of a few rows
+#pragma unroll
+        for (int c = 0; c < TPW; ++c) {
+          const int tile = uw * TPW + c;
+          const int t = tile / ND, dc = tile % ND;
+          if (q0 + 32 * t >= L) continue;
+          v16f acc = v16f{};
+          int kscale[2], sscale[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            sscale[kk] = sDSs[pb][t][2 * kk + g];
+            kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
+            if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
+            const v8i sb = tr_operand(sDS[pb] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+            const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);       // columns: features, K: keys
+            acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
+          }
+          keep(acc[0]);
+          keep(kscale[0]); keep(kscale[1]); keep(sscale[0]); keep(sscale[1]);
+          // lanes pair up: the even lane adds (row r, features f, f+1) of element e, the odd lane
+          // (row r + 1, features f-1, f) of element e + 1; each sends the value its partner needs
+          const int odd = lane & 1;
+          // wave-uniform base at (query q0 + 32t, feature 32 dc); 32-bit lane offsets in halves
+          _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc);
+          const uint32_t rh = (uint32_t)rowH;
+          const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
+          const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_e below this are in range
+          const float mult = a.dq_mult;
+          auto add_tile = [&](auto checked) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+              const float x0 = acc[e], x1 = acc[e + 1];
+              const float send = odd ? x0 : x1;
+              const float got = __int_as_float(
+                  __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
+              const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
+              const int ci = 8 * (e >> 2) + (e & 3);
+              if (!decltype(checked)::value || ci < rows_left)
+                atomic_add_h2(abase + (lofs + (uint32_t)ci * rh), lo_v * mult, hi_v * mult);
+            }
+          };
+          if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
+          else add_tile(std::true_type{});
+        }
+        // the dV / dK products have finished once a later result is read
+        keep(dkt[ND - 1][0]);
+        keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
+      }
+      __syncthreads();
     }
 
-    store_step(qn, buf ^ 1, nx);
-    __syncthreads();
+    // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
+    keep(dvt[ND - 1][0]);
+    keep(dkt[ND - 1][0]);
+    keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
+    if (kj >= L) return;
+    const long orow = (long)(tok0 + kj) * rowH + (long)h * D;
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 32 * dc + 8 * q + 4 * g;
+        const float k0 = dkt[dc][4 * q] * a.sigma, k1 = dkt[dc][4 * q + 1] * a.sigma,
+                    k2 = dkt[dc][4 * q + 2] * a.sigma, k3 = dkt[dc][4 * q + 3] * a.sigma;
+        const float v0 = dvt[dc][4 * q], v1 = dvt[dc][4 * q + 1], v2 = dvt[dc][4 * q + 2], v3 = dvt[dc][4 * q + 3];
+        if (a.grad_f32) {
+          *(float4*)((float*)a.dk + orow + d) = make_float4(k0, k1, k2, k3);
+          *(float4*)((float*)a.dv + orow + d) = make_float4(v0, v1, v2, v3);
+        } else {
+          *(uint2*)((uint16_t*)a.dk + orow + d) =
+              make_uint2(f32_to_bf16(k0) | (f32_to_bf16(k1) << 16), f32_to_bf16(k2) | (f32_to_bf16(k3) << 16));
+          *(uint2*)((uint16_t*)a.dv + orow + d) =
+              make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
+        }
+      }
   }
-
-  // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
-  keep(dvt[CPW - 1][0]);
-  keep(dkt[CPW - 1][0]);
-  keep(dosw_prev); keep(qsw_prev); keep(psc_prev); keep(ssc_prev);
-  if (kj >= L) return;
-  const long orow = (long)(tok0 + kj) * rowH + (long)h * D;
-#pragma unroll
-  for (int c = 0; c < CPW; ++c)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = 32 * (ta * CPW + c) + 8 * q + 4 * g;
-      const float k0 = dkt[c][4 * q] * a.sigma, k1 = dkt[c][4 * q + 1] * a.sigma, k2 = dkt[c][4 * q + 2] * a.sigma,
-                  k3 = dkt[c][4 * q + 3] * a.sigma;
-      const float v0 = dvt[c][4 * q], v1 = dvt[c][4 * q + 1], v2 = dvt[c][4 * q + 2], v3 = dvt[c][4 * q + 3];
-      if (a.grad_f32) {
-        *(float4*)((float*)a.dk + orow + d) = make_float4(k0, k1, k2, k3);
-        *(float4*)((float*)a.dv + orow + d) = make_float4(v0, v1, v2, v3);
-      } else {
-        *(uint2*)((uint16_t*)a.dk + orow + d) =
-            make_uint2(f32_to_bf16(k0) | (f32_to_bf16(k1) << 16), f32_to_bf16(k2) | (f32_to_bf16(k3) << 16));
-        *(uint2*)((uint16_t*)a.dv + orow + d) =
-            make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
-      }
-    }
 }
 
 // ------------------------------------------------------------ dQ finalize
