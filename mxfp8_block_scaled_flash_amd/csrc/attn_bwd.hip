@@ -75,6 +75,19 @@ MX_DEV void atomic_add_h2(_Float16* p, float a, float b) {
   __builtin_amdgcn_global_atomic_fadd_v2f16((h2v __attribute__((address_space(1)))*)(p), v);
 }
 
+// Buffer resource over `bytes` bytes from base (raw, untyped accesses; the
+// word-3 value is the gfx9-family default for such buffers).
+MX_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+
+// Packed fp16 atomic add through a buffer resource: a 32-bit byte offset from
+// a scalar base (buffer_atomic_pk_add_f16).
+MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float a, float b) {
+  h2v v = {(_Float16)a, (_Float16)b};
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(v, r, (int)byte_off, 0, 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ preprocess
@@ -284,102 +297,112 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         const int q0 = qstart + i * BQ, qb = i % 3, pb = i & 1;
         const uint8_t* sQb = sQ[qb];
         const uint8_t* sDOb = sDO[qb];
+        // ---- S and dP for (key block kb, query blocks t = 0, 1): element e of st[t], dpt[t] is
+        // query q0 + 32t + 8(e/4) + 4g + e%4, key kj.  Both blocks go through the elementwise
+        // pass, the reductions and the encoding together (independent chains side by side).
+        bool act[2], edge[2];
+        v16f st[2], dpt[2];
+        uint32_t qsa[2], dsa[2];
+        int lo[2], hi[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          // ---- S and dP for (key block kb, query block t): element e = query qa0 + 8(e/4) + 4g + e%4, key kj
           const int qa0 = q0 + 32 * t;
-          uint8_t* prow = sP[pb] + (32 * kb + n) * SST + 32 * t + 16 * g;
-          uint8_t* srow = sDS[pb] + (32 * kb + n) * SST + 32 * t + 16 * g;
-          if (kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31)) {
-            const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
-            const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
-            const uint32_t qsa = sQs[qb][t] >> (8 * g), dsa = sDOs[qb][t] >> (8 * g);
-            v16f st = v16f{}, dpt = v16f{};
-            st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)), kop[0], st, qsa, ksc);
-            dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), vop[0], dpt, dsa, vsc);
-            if constexpr (NC > 1) {
-              st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)), kop[NC - 1], st, qsa,
-                                 ksc);
-              dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)), vop[NC - 1], dpt, dsa,
-                                  vsc);
-            }
-            float lv[16], dv[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 l4 = *(const float4*)(&sL[qb][32 * t + 8 * q + 4 * g]);
-              const float4 d4 = *(const float4*)(&sDv[qb][32 * t + 8 * q + 4 * g]);
-              lv[4 * q] = l4.x; lv[4 * q + 1] = l4.y; lv[4 * q + 2] = l4.z; lv[4 * q + 3] = l4.w;
-              dv[4 * q] = d4.x; dv[4 * q + 1] = d4.y; dv[4 * q + 2] = d4.z; dv[4 * q + 3] = d4.w;
-            }
-            // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D)
-            const bool need_mask = qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
-            // element i is query qa0 + 4g + c_i, c_i = 8(i/4) + i%4: visible iff lo <= c_i < hi
-            const int lo = kj >= L ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
-            const int hi = L - qa0 - 4 * g;
-            float am = -INFINITY, sm = 0.f;
-            // two copies of the elementwise pass: with the mask (diagonal and edge blocks) and without
-            auto pass = [&](auto masked) {
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                float arg = fmaf(st[e], cl, -lv[e]);
-                if constexpr (decltype(masked)::value) {
-                  const int ci = 8 * (e >> 2) + (e & 3);
-                  arg = (ci >= lo && ci < hi) ? arg : -INFINITY;
-                }
-                const float p = __builtin_amdgcn_exp2f(arg);
-                const float ds = p * (dpt[e] - dv[e]);
-                st[e] = p;
-                dpt[e] = ds;
-                am = fmaxf(am, arg);
-                sm = fmaxf(sm, fabsf(ds));
-              }
-            };
-            if (need_mask) pass(std::true_type{});
-            else pass(std::false_type{});
-            const float amax = half_swap_max(am);   // 32 queries of this key
-            const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
-            // S and dP have been read: their products are done
-            keep(qsa); keep(dsa); keep(ksc); keep(vsc);
-            // ---- MX codes: dword q holds queries 8q + 4g + 0..3
-            const int kp = max(exp2_scale_code(amax), 1);
-            const int ks2 = max(scale_code(smax), 1);
-            const float psc = e8m0_f32(kp), plim = 448.f * psc;
-            const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
-            uint32_t pw[4], sw[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v2s z = {0, 0};
-              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc,
-                                                           false);
-              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim),
-                                                           psc, true);
-              pw[q] = __builtin_bit_cast(uint32_t, z);
-              v2s y = {0, 0};
-              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
-                                                           __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc,
-                                                           false);
-              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
-                                                           __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc,
-                                                           true);
-              sw[q] = __builtin_bit_cast(uint32_t, y);
-            }
-            // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
-            auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-            auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-            auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
-            auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
-            *(uint4*)prow = make_uint4(a02[0], a02[1], a13[0], a13[1]);
-            *(uint4*)srow = make_uint4(b02[0], b02[1], b13[0], b13[1]);
-            if (g == 0) sPs[pb][t][32 * kb + n] = kp;
-            if (lane == 0) sDSs[pb][t][kb] = ks2;
-          } else {
-            // keys entirely after these queries (or past either end): P and dS are zero
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            *(uint4*)prow = z;
-            *(uint4*)srow = z;
-            if (g == 0) sPs[pb][t][32 * kb + n] = 1;
-            if (lane == 0) sDSs[pb][t][kb] = 1;
+          act[t] = kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
+          edge[t] = !act[t] || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+          // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
+          lo[t] = (!act[t] || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
+          hi[t] = L - qa0 - 4 * g;
+          qsa[t] = sQs[qb][t] >> (8 * g);
+          dsa[t] = sDOs[qb][t] >> (8 * g);
+          // computed for every block (rows past either end are zero, so the values are finite):
+          // straight-line code lets every operand read be issued early; the mask zeroes p and
+          // dS where nothing is visible
+          const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
+          const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
+          st[t] = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)), kop[0], v16f{}, qsa[t], ksc);
+          dpt[t] = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), vop[0], v16f{}, dsa[t], vsc);
+          if constexpr (NC > 1) {
+            st[t] = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)), kop[NC - 1], st[t],
+                                  qsa[t], ksc);
+            dpt[t] = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)), vop[NC - 1], dpt[t],
+                                   dsa[t], vsc);
           }
+        }
+        float lv[2][16], dv[2][16];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 l4 = *(const float4*)(&sL[qb][32 * t + 8 * q + 4 * g]);
+            const float4 d4 = *(const float4*)(&sDv[qb][32 * t + 8 * q + 4 * g]);
+            lv[t][4 * q] = l4.x; lv[t][4 * q + 1] = l4.y; lv[t][4 * q + 2] = l4.z; lv[t][4 * q + 3] = l4.w;
+            dv[t][4 * q] = d4.x; dv[t][4 * q + 1] = d4.y; dv[t][4 * q + 2] = d4.z; dv[t][4 * q + 3] = d4.w;
+          }
+        // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D); two copies of the
+        // pass: with the mask (diagonal, edge or empty blocks) and without
+        float am[2] = {-INFINITY, -INFINITY}, sm[2] = {0.f, 0.f};
+        auto pass = [&](auto masked) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              float arg = fmaf(st[t][e], cl, -lv[t][e]);
+              if constexpr (decltype(masked)::value) {
+                const int ce = 8 * (e >> 2) + (e & 3);
+                arg = (ce >= lo[t] && ce < hi[t]) ? arg : -INFINITY;
+              }
+              const float p = __builtin_amdgcn_exp2f(arg);
+              const float ds = p * (dpt[t][e] - dv[t][e]);
+              st[t][e] = p;
+              dpt[t][e] = ds;
+              am[t] = fmaxf(am[t], arg);
+              sm[t] = fmaxf(sm[t], fabsf(ds));
+            }
+        };
+        if (edge[0] || edge[1]) pass(std::true_type{});
+        else pass(std::false_type{});
+        float amax[2], smax[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          amax[t] = half_swap_max(am[t]);    // 32 queries of this key
+          smax[t] = wave_max_nonneg(sm[t]);  // 32 queries x 32 keys
+        }
+        // S and dP have been read: their products are done
+        keep(qsa[0]); keep(dsa[0]); keep(qsa[1]); keep(dsa[1]); keep(ksc); keep(vsc);
+        // ---- MX codes (blocks with nothing visible get zero codes and scale 1)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int kp = max(exp2_scale_code(amax[t]), 1);
+          const int ks2 = max(scale_code(smax[t]), 1);
+          const float psc = e8m0_f32(kp), plim = 448.f * psc;
+          const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
+          uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v2s z = {0, 0};
+            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[t][4 * q], plim), clampp(st[t][4 * q + 1], plim),
+                                                         psc, false);
+            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[t][4 * q + 2], plim),
+                                                         clampp(st[t][4 * q + 3], plim), psc, true);
+            pw[q] = __builtin_bit_cast(uint32_t, z);
+            v2s y = {0, 0};
+            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q], -slim, slim),
+                                                         __builtin_amdgcn_fmed3f(dpt[t][4 * q + 1], -slim, slim), ssc,
+                                                         false);
+            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q + 2], -slim, slim),
+                                                         __builtin_amdgcn_fmed3f(dpt[t][4 * q + 3], -slim, slim), ssc,
+                                                         true);
+            sw[q] = __builtin_bit_cast(uint32_t, y);
+          }
+          // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
+          auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+          auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+          auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+          auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+          *(uint4*)(sP[pb] + (32 * kb + n) * SST + 32 * t + 16 * g) = make_uint4(a02[0], a02[1], a13[0], a13[1]);
+          *(uint4*)(sDS[pb] + (32 * kb + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+          if (g == 0) sPs[pb][t][32 * kb + n] = kp;
+          if (lane == 0) sDSs[pb][t][kb] = ks2;
         }
       }
       store_step(qn, (i + 1) % 3, nx);
@@ -424,50 +447,78 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           }
           dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
         }
-        // ---- dQ tiles (t, dc): output element e of lane l is query 32t + 8(e/4) + 4g + e%4,
-        // feature 32 dc + l%32, so a wave's atomics run along contiguous features of a few rows
+        // ---- dQ for query block t and feature chunks dc0 .. dc0 + TPW - 1 (a 32 x 32 tile each):
+        // output element e of lane l is query 32t + 8(e/4) + 4g + e%4, feature 32 dc + l%32
+        const int t = (uw * TPW) / ND, dc0 = (uw * TPW) % ND;
+        if (q0 + 32 * t < L) {
+          v16f acc[TPW];
+          int kscale[TPW][2], sscale[2];
 #pragma unroll
-        for (int c = 0; c < TPW; ++c) {
-          const int tile = uw * TPW + c;
-          const int t = tile / ND, dc = tile % ND;
-          if (q0 + 32 * t >= L) continue;
-          v16f acc = v16f{};
-          int kscale[2], sscale[2];
+          for (int kk = 0; kk < 2; ++kk) sscale[kk] = sDSs[pb][t][2 * kk + g];
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            sscale[kk] = sDSs[pb][t][2 * kk + g];
-            kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-            if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-            const v8i sb = tr_operand(sDS[pb] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-            const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);       // columns: features, K: keys
-            acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
-          }
-          keep(acc[0]);
-          keep(kscale[0]); keep(kscale[1]); keep(sscale[0]); keep(sscale[1]);
-          // lanes pair up: the even lane adds (row r, features f, f+1) of element e, the odd lane
-          // (row r + 1, features f-1, f) of element e + 1; each sends the value its partner needs
-          const int odd = lane & 1;
-          // wave-uniform base at (query q0 + 32t, feature 32 dc); 32-bit lane offsets in halves
-          _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc);
-          const uint32_t rh = (uint32_t)rowH;
-          const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
-          const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_e below this are in range
-          const float mult = a.dq_mult;
-          auto add_tile = [&](auto checked) {
+          for (int c = 0; c < TPW; ++c) {
+            acc[c] = v16f{};
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-              const float x0 = acc[e], x1 = acc[e + 1];
-              const float send = odd ? x0 : x1;
-              const float got = __int_as_float(
-                  __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
-              const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
-              const int ci = 8 * (e >> 2) + (e & 3);
-              if (!decltype(checked)::value || ci < rows_left)
-                atomic_add_h2(abase + (lofs + (uint32_t)ci * rh), lo_v * mult, hi_v * mult);
+            for (int kk = 0; kk < 2; ++kk) {
+              kscale[c][kk] = (int)((sKs[2 * kk + g] >> (8 * (dc0 + c))) & 0xFFu);
+              if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
+              const v8i sb = tr_operand(sDS[pb] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+              const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * (dc0 + c), KST, lane);   // columns: features
+              acc[c] = mfma32b<0, 0>(sb, ka, acc[c], sscale[kk], kscale[c][kk]);
             }
-          };
-          if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
-          else add_tile(std::true_type{});
+          }
+#pragma unroll
+          for (int c = 0; c < TPW; ++c) keep(acc[c][0]);
+#pragma unroll
+          for (int c = 0; c < TPW; ++c) { keep(kscale[c][0]); keep(kscale[c][1]); }
+          keep(sscale[0]); keep(sscale[1]);
+          // Packed fp16 atomics, neighbouring lanes paired (each sends the value its partner
+          // needs).  With two chunks, the even lane of a pair adds features (f, f+1) of chunk
+          // dc0 and the odd lane (f-1, f) of chunk dc0 + 1, both on row r: the 32 lanes of a
+          // half cover one whole 128-byte row.  With one chunk, the odd lane takes row r + 1.
+          const int odd = lane & 1;
+          _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc0);
+          const uint32_t rh = (uint32_t)rowH;
+          // the tile's 32 rows lie within 32 rowH halves of abase
+          const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(abase, (int)(64u * rh));
+          const float mult = a.dq_mult;
+          if constexpr (TPW == 2) {
+            const uint32_t lofs = (uint32_t)(4 * g) * rh + (uint32_t)(n + (odd ? 31 : 0));
+            const int rows_left = L - q0 - 32 * t - 4 * g;   // element rows c_e below this are in range
+            auto add_tile = [&](auto checked) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const float x0 = acc[0][e], x1 = acc[TPW - 1][e];
+                const float send = odd ? x0 : x1;
+                const float got = __int_as_float(
+                    __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
+                const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
+                const int ce = 8 * (e >> 2) + (e & 3);
+                if (!decltype(checked)::value || ce < rows_left)
+                  atomic_add_h2_buf(ars, 2u * (lofs + (uint32_t)ce * rh), lo_v * mult, hi_v * mult);
+              }
+            };
+            if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
+            else add_tile(std::true_type{});
+          } else {
+            const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
+            const int rows_left = L - q0 - 32 * t - 4 * g - odd;
+            auto add_tile = [&](auto checked) {
+#pragma unroll
+              for (int e = 0; e < 16; e += 2) {
+                const float x0 = acc[0][e], x1 = acc[0][e + 1];
+                const float send = odd ? x0 : x1;
+                const float got = __int_as_float(
+                    __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
+                const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
+                const int ce = 8 * (e >> 2) + (e & 3);
+                if (!decltype(checked)::value || ce < rows_left)
+                  atomic_add_h2_buf(ars, 2u * (lofs + (uint32_t)ce * rh), lo_v * mult, hi_v * mult);
+              }
+            };
+            if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
+            else add_tile(std::true_type{});
+          }
         }
         // the dV / dK products have finished once a later result is read
         keep(dkt[ND - 1][0]);
