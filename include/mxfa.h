@@ -176,8 +176,9 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
 
 /*
  * mx_attn_bwd_workspace_bytes -- device scratch mx_attn_bwd needs:
- * an fp16 dQ accumulator [B, S, H, D] (or [T, H, D]) and D_i [B, H, S]
- * fp32 (or [H, T]), each 256-byte aligned.  tokens = B*S or T.
+ * an fp16 dQ accumulator of tokens x H x D halves (head-major [H, tokens,
+ * D], internal) and D_i [B, H, S] fp32 (or [H, T]), each 256-byte aligned.
+ * tokens = B*S or T.
  */
 size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D);
 

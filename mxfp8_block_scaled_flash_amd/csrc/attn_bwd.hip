@@ -11,7 +11,8 @@
 //
 // Three kernels on the caller's stream:
 //  1. bwd_pre_kernel: D_i = sum_d dO_id O_id in fp32 from the unquantized
-//     tensors, and zero the fp16 dQ accumulator.
+//     tensors, and zero the fp16 dQ accumulator (head-major [H, T, D], so a
+//     head's rows are contiguous for the atomics).
 //  2. attn_bwd_kernel: one workgroup per (sequence, head, 128-key tile),
 //     four waves of 32 keys, walking 64-query tiles.  Per tile each wave
 //     computes S = Q^ K^T and dP = dO^ V^T (scaled MFMA, keys as the output
@@ -88,6 +89,13 @@ MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(v, r, (int)byte_off, 0, 0);
 }
 
+// The same with a wave-uniform part of the offset in an SGPR (soffset), so
+// per-element constants cost no vector registers.
+MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t uniform_off, float a, float b) {
+  h2v v = {(_Float16)a, (_Float16)b};
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(v, r, (int)byte_off, (int)__builtin_amdgcn_readfirstlane(uniform_off), 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ preprocess
@@ -115,9 +123,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
             bf16_hi(x.y) * bf16_hi(y.y) + bf16_lo(x.z) * bf16_lo(y.z) + bf16_hi(x.z) * bf16_hi(y.z) +
             bf16_lo(x.w) * bf16_lo(y.w) + bf16_hi(x.w) * bf16_hi(y.w);
     }
-    // zero this row's fp16 dQ accumulator (D halves)
+    // zero this row's fp16 dQ accumulator (D halves; the accumulator is head-major [H, T, D])
     uint4 z = make_uint4(0, 0, 0, 0);
-    uint16_t* accp = (uint16_t*)a.acc + row * D;
+    uint16_t* accp = (uint16_t*)a.acc + ((row % a.H) * (long)a.T + row / a.H) * D;
     for (int i = c; i < D / 8; i += LPR) *(uint4*)(accp + i * 8) = z;
   }
 #pragma unroll
@@ -133,50 +141,49 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ main kernel
-// One workgroup of eight waves per (sequence, head, 128-key tile), walking
-// 64-query steps as a two-stage pipeline, one barrier per stage interval:
-//  * producer waves 0-3 (wave w owns key block w, K^ and V^ rows in registers)
-//    compute, for step i, S and dP for their 32 keys x 64 queries (keys as the
-//    output columns: lane = one key), p and dS, and their MX codes (P: one
-//    scale per key and 32 queries; dS: one scale per square 32 x 32 block),
-//    stored in LDS as [key][query] with the scales;
-//  * consumer waves 4-7 take step i - 1 meanwhile: wave 4 + b accumulates
-//    dV^T and dK^T for key block b (all D features, 64 queries of
-//    contraction, codes read back from LDS, Q^T and dO^T through transpose
-//    reads), then forms D/64 of the 32 x 32 (query block, feature chunk)
-//    tiles of dQ = dS^ K^ over the 128 keys and adds them to the fp16
-//    accumulator with packed atomics.
-// A producer and a consumer share each SIMD, so one's softmax work overlaps
-// the other's MFMAs.  Q^ / dO^ tiles, scales, LSE and D rotate through three
-// LDS buffers (step being produced, step being consumed, step being loaded
-// from HBM by the producers), the codes through two.
+// One workgroup of eight waves per (sequence, head, 256-key tile), walking
+// 64-query steps.  The dQ atomics execute at the memory side (device-scope
+// atomics bypass the per-XCD L2s), so their volume -- one fp16 partial per
+// key tile and query -- bounds this kernel; 256-key tiles halve it.
+// Wave w owns key block w (32 keys; lane = one key) for the whole walk:
+//  A. per query block t = 0, 1: S = Q^ K^T and dP = dO^ V^T (keys as the
+//     output columns), p and dS, their MX codes (P: one scale per key and 32
+//     queries; dS: one scale per square 32 x 32 block), kept in registers as
+//     the B operands below; the dS codes also go to LDS as [key][query];
+//  B. dV^T += dO^T P^ and dK^T += Q^T dS^ for its keys and all D features
+//     (contraction over the 64 queries; Q^T, dO^T through transpose reads);
+//  -- barrier --
+//  C. wave w < 2D/32 forms one 32 x 32 (query block, feature chunk) tile of
+//     dQ = dS^ K^ over the 256 keys and adds it to the fp16 accumulator with
+//     packed atomics.
+// The next step's Q^ / dO^ tiles, scales, LSE and D are loaded into registers
+// during C and written to the other LDS buffer at the end of the step: two
+// barriers per step.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int NW = 8;
-  constexpr int BN = 128;       // keys per workgroup
+  constexpr int BN = 32 * NW;   // keys per workgroup
   constexpr int BQ = 64;        // queries per step
   constexpr int NC = D / 64;    // 64-feature chunks of the S / dP contraction
   constexpr int ND = D / 32;    // 32-feature chunks of dK, dV, dQ
-  constexpr int TPW = ND / 2;   // dQ tiles per consumer wave (2 ND tiles over 4 waves)
   constexpr int NB = D / 32;    // scale bytes per SQ32 / ROW32 scale word
-  constexpr int KST = D + 16;   // LDS row stride of K, Q, dO tiles
-  constexpr int SST = BQ + 16;  // LDS row stride of the P and dS code tiles [key][query]
+  constexpr int KST = D + 16;   // LDS row stride of K, V, Q, dO tiles
+  constexpr int SST = BQ + 16;  // LDS row stride of the dS code tile [key][query]
   constexpr int NT = NW * 64;
-  constexpr int NTP = 256;            // producer threads: they alone load and stage the query steps
   constexpr int QCH = BQ * D / 16;    // 16-byte chunks of one Q (or dO) tile
-  constexpr int CPT = 2 * QCH / NTP;  // chunks of Q and dO per producer thread per step
-  static_assert(2 * QCH % NTP == 0, "chunks must divide among the threads");
+  constexpr int CPT = 2 * QCH / NT;   // chunks of Q and dO per thread per step
+  static_assert(2 * QCH % NT == 0, "chunks must divide among the threads");
   __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[3][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[3][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sP[2][BN * SST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * SST];
-  __shared__ uint32_t sKs[4];                  // K SQ32 scale word (bytes = feature blocks) per key block
-  __shared__ uint32_t sQs[3][2], sDOs[3][2];   // [buffer][query block]
-  __shared__ __attribute__((aligned(16))) float sL[3][BQ];    // LSE log2(e)
-  __shared__ __attribute__((aligned(16))) float sDv[3][BQ];   // D
-  __shared__ int sPs[2][2][BN];                // P scale code of (query block, key)
-  __shared__ int sDSs[2][2][4];                // dS scale code of (query block, key block)
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BQ * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sDS[BN * SST];
+  __shared__ uint32_t sKs[NW];                 // K SQ32 scale word (bytes = feature blocks) per key block
+  __shared__ uint32_t sVs[BN];                 // V ROW32 scale word per key
+  __shared__ uint32_t sQs[2][2], sDOs[2][2];   // [buffer][query block]
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];    // LSE log2(e)
+  __shared__ __attribute__((aligned(16))) float sDv[2][BQ];   // D
+  __shared__ int sDSs[2][NW];                  // dS scale code of (query block, key block)
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -190,27 +197,31 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int kbase = kt * BN;
   if (kbase >= L) return;
   const long rowH = (long)a.H * D;
-  const int kb = w & 3;               // this wave's key block (both roles)
-  const int kw0 = kbase + 32 * kb;
+  const int kw0 = kbase + 32 * w;     // this wave's key block
   const int kj = kw0 + n;             // this lane's key
 
-  // ---- K tile (all keys of the workgroup) for the dQ products, and scales
+  // ---- K and V tiles (zero past the end) and their scales
   for (int ch = tid; ch < BN * D / 16; ch += NT) {
     const int r = ch / (D / 16), cx = ch % (D / 16);
-    uint4 kv = make_uint4(0, 0, 0, 0);
-    if (kbase + r < L) kv = *(const uint4*)(a.k + (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16);
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (kbase + r < L) {
+      const long off = (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16;
+      kv = *(const uint4*)(a.k + off);
+      vv = *(const uint4*)(a.v + off);
+    }
     *(uint4*)(sK + r * KST + cx * 16) = kv;
+    *(uint4*)(sV + r * KST + cx * 16) = vv;
   }
-  if (tid < 4) {
+  if (tid < NW) {
     uint32_t wk = 0;
     if (kbase + 32 * tid < L) wk = ld_scale_word(a.ks + ((long)(sblk0 + kbase / 32 + tid) * a.H + h) * NB, NB);
     sKs[tid] = wk;
   }
+  for (int r = tid; r < BN; r += NT)
+    sVs[r] = (kbase + r < L) ? ld_scale_word(a.vs + ((long)(srow0 + kbase + r) * a.H + h) * NB, NB) : 0u;
 
-  // ---- staging of one query step, by the producer waves (the consumers issue
-  // the dQ atomics; a wait for staged loads there would also wait for those).
-  // Loads are branch-free: rows past the end are clamped to the last query and
-  // zeroed (or masked later) when stored.
+  // ---- staging of one query step.  Loads are branch-free: rows past the end
+  // are clamped to the last query and zeroed (or masked later) when stored.
   struct Stage {
     uint4 x[CPT];
     float l, d;
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   auto load_step = [&](int q0, Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NTP;
+      const int ch = tid + c * NT;
       const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
       const long off = (long)(tok0 + min(q0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
       st.x[c] = *(const uint4*)((ch < QCH ? a.q : a.dob) + off);
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   auto store_step = [&](int q0, int buf, const Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NTP;
+      const int ch = tid + c * NT;
       const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
       const uint32_t m = (q0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
       const uint4 x = st.x[c];
@@ -254,311 +265,255 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     }
   };
 
+  v16f dvt[ND], dkt[ND];   // dV^T, dK^T: element e = feature 32 dc + 8(e/4) + 4g + e%4, key kj
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc) {
+    dvt[dc] = v16f{};
+    dkt[dc] = v16f{};
+  }
+  const float cl = a.c;
   const int qstart = CAUSAL ? (kbase / BQ) * BQ : 0;
   const int nsteps = (L - qstart + BQ - 1) / BQ;
-  if (w < 4) {
+  // scale operands of the last dV / dK products, pinned until those products finish
+  uint32_t dow_prev = 0, qw_prev = 0;
+  int psc_prev = 0, ssc_prev = 0;
+
+  {
     Stage st0;
     load_step(qstart, st0);
     store_step(qstart, 0, st0);
   }
   __syncthreads();
 
-  // Both roles run nsteps + 1 intervals with one barrier each: interval i
-  // produces step i, consumes step i - 1 and loads step i + 1 (past the last
-  // step, the last one is fetched again and its buffer rewritten with the same
-  // bytes, which keeps the loads free of branches).
-  if (w < 4) {
-    // ================================================================ producer
-    const float cl = a.c;
-    v8i kop[NC], vop[NC];
-    uint32_t ksc = 0, vsc = 0;
-    if (kj < L) {
-      const uint8_t* kp = a.k + (long)(tok0 + kj) * rowH + (long)h * D;
-      const uint8_t* vp = a.v + (long)(tok0 + kj) * rowH + (long)h * D;
+  for (int j = 0; j < nsteps; ++j) {
+    const int q0 = qstart + j * BQ, buf = j & 1;
+    const uint8_t* sQb = sQ[buf];
+    const uint8_t* sDOb = sDO[buf];
+    // ---- A. S and dP for (key block w, query block t): element e = query q0 + 32t + 8(e/4) + 4g + e%4
+    v8i pB, sB;        // P and dS codes as B operands: bytes 16t + 0..15 = queries 32t + 16g + 0..15
+    int kpc[2], ksc2[2];
+    const bool live = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);   // a key of the block sees a query
+    if (live) {
+      const uint8_t* kr = sK + (32 * w + n) * KST + 16 * g;
+      const uint8_t* vr = sV + (32 * w + n) * KST + 16 * g;
+      const uint32_t ksc = sKs[w] >> (8 * g), vsc = sVs[32 * w + n] >> (8 * g);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kop[c] = pack8b(*(const uint4*)(kp + 64 * c + 16 * g), *(const uint4*)(kp + 64 * c + 32 + 16 * g));
-        vop[c] = pack8b(*(const uint4*)(vp + 64 * c + 16 * g), *(const uint4*)(vp + 64 * c + 32 + 16 * g));
-      }
-      ksc = ld_scale_word(a.ks + ((long)(sblk0 + kw0 / 32) * a.H + h) * NB, NB) >> (8 * g);
-      vsc = ld_scale_word(a.vs + ((long)(srow0 + kj) * a.H + h) * NB, NB) >> (8 * g);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kop[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        vop[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-    for (int i = 0; i <= nsteps; ++i) {
-      const int qn = qstart + min(i + 1, nsteps - 1) * BQ;
-      Stage nx;
-      load_step(qn, nx);
-      if (i < nsteps) {
-        const int q0 = qstart + i * BQ, qb = i % 3, pb = i & 1;
-        const uint8_t* sQb = sQ[qb];
-        const uint8_t* sDOb = sDO[qb];
-        // ---- S and dP for (key block kb, query blocks t = 0, 1): element e of st[t], dpt[t] is
-        // query q0 + 32t + 8(e/4) + 4g + e%4, key kj.  Both blocks go through the elementwise
-        // pass, the reductions and the encoding together (independent chains side by side).
-        bool act[2], edge[2];
-        v16f st[2], dpt[2];
-        uint32_t qsa[2], dsa[2];
-        int lo[2], hi[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int qa0 = q0 + 32 * t;
-          act[t] = kw0 < L && qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
-          edge[t] = !act[t] || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
-          // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
-          lo[t] = (!act[t] || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
-          hi[t] = L - qa0 - 4 * g;
-          qsa[t] = sQs[qb][t] >> (8 * g);
-          dsa[t] = sDOs[qb][t] >> (8 * g);
-          // computed for every block (rows past either end are zero, so the values are finite):
-          // straight-line code lets every operand read be issued early; the mask zeroes p and
-          // dS where nothing is visible
-          const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
-          const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
-          st[t] = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)), kop[0], v16f{}, qsa[t], ksc);
-          dpt[t] = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), vop[0], v16f{}, dsa[t], vsc);
-          if constexpr (NC > 1) {
-            st[t] = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)), kop[NC - 1], st[t],
-                                  qsa[t], ksc);
-            dpt[t] = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)), vop[NC - 1], dpt[t],
-                                   dsa[t], vsc);
-          }
+      for (int t = 0; t < 2; ++t) {
+        const int qa0 = q0 + 32 * t;
+        const bool act = qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
+        const bool edge = !act || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+        // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
+        const int lo = (!act || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
+        const int hi = L - qa0 - 4 * g;
+        const uint32_t qsa = sQs[buf][t] >> (8 * g), dsa = sDOs[buf][t] >> (8 * g);
+        // computed for every block (rows past either end are zero, so the values are
+        // finite); the mask zeroes p and dS where nothing is visible
+        const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
+        const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
+        v16f st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
+                                pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), v16f{}, qsa, ksc);
+        v16f dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
+                                 pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), v16f{}, dsa, vsc);
+        if constexpr (NC > 1) {
+          st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
+                             pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
+          dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
+                              pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
         }
-        float lv[2][16], dv[2][16];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 l4 = *(const float4*)(&sL[qb][32 * t + 8 * q + 4 * g]);
-            const float4 d4 = *(const float4*)(&sDv[qb][32 * t + 8 * q + 4 * g]);
-            lv[t][4 * q] = l4.x; lv[t][4 * q + 1] = l4.y; lv[t][4 * q + 2] = l4.z; lv[t][4 * q + 3] = l4.w;
-            dv[t][4 * q] = d4.x; dv[t][4 * q + 1] = d4.y; dv[t][4 * q + 2] = d4.z; dv[t][4 * q + 3] = d4.w;
-          }
         // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D); two copies of the
-        // pass: with the mask (diagonal, edge or empty blocks) and without
-        float am[2] = {-INFINITY, -INFINITY}, sm[2] = {0.f, 0.f};
+        // pass: with the mask (diagonal, edge or empty blocks) and without.  LSE and D are read
+        // four queries at a time, in two halves fenced off from each other (fewer live registers).
+        float am = -INFINITY, sm = 0.f;
         auto pass = [&](auto masked) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
+          for (int q = 0; q < 4; ++q) {
+            if (q == 2) __builtin_amdgcn_sched_barrier(0);
+            const float4 l4 = *(const float4*)(&sL[buf][32 * t + 8 * q + 4 * g]);
+            const float4 d4 = *(const float4*)(&sDv[buf][32 * t + 8 * q + 4 * g]);
+            const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              float arg = fmaf(st[t][e], cl, -lv[t][e]);
+            for (int r = 0; r < 4; ++r) {
+              const int e = 4 * q + r;
+              float arg = fmaf(st[e], cl, -lq[r]);
               if constexpr (decltype(masked)::value) {
-                const int ce = 8 * (e >> 2) + (e & 3);
-                arg = (ce >= lo[t] && ce < hi[t]) ? arg : -INFINITY;
+                const int ce = 8 * q + r;
+                arg = (ce >= lo && ce < hi) ? arg : -INFINITY;
               }
               const float p = __builtin_amdgcn_exp2f(arg);
-              const float ds = p * (dpt[t][e] - dv[t][e]);
-              st[t][e] = p;
-              dpt[t][e] = ds;
-              am[t] = fmaxf(am[t], arg);
-              sm[t] = fmaxf(sm[t], fabsf(ds));
+              const float ds = p * (dpt[e] - dq[r]);
+              st[e] = p;
+              dpt[e] = ds;
+              am = fmaxf(am, arg);
+              sm = fmaxf(sm, fabsf(ds));
             }
+          }
         };
-        if (edge[0] || edge[1]) pass(std::true_type{});
+        if (edge) pass(std::true_type{});
         else pass(std::false_type{});
-        float amax[2], smax[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          amax[t] = half_swap_max(am[t]);    // 32 queries of this key
-          smax[t] = wave_max_nonneg(sm[t]);  // 32 queries x 32 keys
-        }
-        // S and dP have been read: their products are done
-        keep(qsa[0]); keep(dsa[0]); keep(qsa[1]); keep(dsa[1]); keep(ksc); keep(vsc);
-        // ---- MX codes (blocks with nothing visible get zero codes and scale 1)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int kp = max(exp2_scale_code(amax[t]), 1);
-          const int ks2 = max(scale_code(smax[t]), 1);
-          const float psc = e8m0_f32(kp), plim = 448.f * psc;
-          const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
-          uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v2s z = {0, 0};
-            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[t][4 * q], plim), clampp(st[t][4 * q + 1], plim),
-                                                         psc, false);
-            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[t][4 * q + 2], plim),
-                                                         clampp(st[t][4 * q + 3], plim), psc, true);
-            pw[q] = __builtin_bit_cast(uint32_t, z);
-            v2s y = {0, 0};
-            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q], -slim, slim),
-                                                         __builtin_amdgcn_fmed3f(dpt[t][4 * q + 1], -slim, slim), ssc,
-                                                         false);
-            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[t][4 * q + 2], -slim, slim),
-                                                         __builtin_amdgcn_fmed3f(dpt[t][4 * q + 3], -slim, slim), ssc,
-                                                         true);
-            sw[q] = __builtin_bit_cast(uint32_t, y);
-          }
-          // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
-          auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-          auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-          auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
-          auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
-          *(uint4*)(sP[pb] + (32 * kb + n) * SST + 32 * t + 16 * g) = make_uint4(a02[0], a02[1], a13[0], a13[1]);
-          *(uint4*)(sDS[pb] + (32 * kb + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
-          if (g == 0) sPs[pb][t][32 * kb + n] = kp;
-          if (lane == 0) sDSs[pb][t][kb] = ks2;
-        }
-      }
-      store_step(qn, (i + 1) % 3, nx);
-      __syncthreads();
-    }
-  } else {
-    // ================================================================ consumer
-    v16f dvt[ND], dkt[ND];   // dV^T, dK^T: element e = feature 32 dc + 8(e/4) + 4g + e%4, key kj
-#pragma unroll
-    for (int dc = 0; dc < ND; ++dc) {
-      dvt[dc] = v16f{};
-      dkt[dc] = v16f{};
-    }
-    // scale operands of the last dV / dK products, pinned until those products finish
-    uint32_t dow_prev = 0, qw_prev = 0;
-    int psc_prev = 0, ssc_prev = 0;
-    const int uw = w - 4;
-    for (int i = 0; i <= nsteps; ++i) {
-      if (i > 0) {
-        const int q0 = qstart + (i - 1) * BQ, qb = (i - 1) % 3, pb = (i - 1) & 1;
-        const uint8_t* sQb = sQ[qb];
-        const uint8_t* sDOb = sDO[qb];
-        // ---- dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries)
-        if (kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1)) {
-          const uint8_t* pr = sP[pb] + (32 * kb + n) * SST + 16 * g;
-          const uint8_t* sr = sDS[pb] + (32 * kb + n) * SST + 16 * g;
-          const v8i pP = pack8b(*(const uint4*)pr, *(const uint4*)(pr + 32));
-          const v8i pS = pack8b(*(const uint4*)sr, *(const uint4*)(sr + 32));
-          const int pscale = sPs[pb][g][32 * kb + n];
-          const int sscale = sDSs[pb][g][kb];
-          const uint32_t dow = sDOs[qb][g], qw = sQs[qb][g];
-#pragma unroll
-          for (int dc = 0; dc < ND; ++dc) {
-            const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
-            const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
-            if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pP, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, pS, dkt[0], qw, sscale); }
-            if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pP, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, pS, dkt[1], qw, sscale); }
-            if constexpr (ND > 2) {
-              if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pP, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, pS, dkt[2], qw, sscale); }
-              if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pP, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, pS, dkt[3], qw, sscale); }
-            }
-          }
-          dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
-        }
-        // ---- dQ for query block t and feature chunks dc0 .. dc0 + TPW - 1 (a 32 x 32 tile each):
-        // output element e of lane l is query 32t + 8(e/4) + 4g + e%4, feature 32 dc + l%32
-        const int t = (uw * TPW) / ND, dc0 = (uw * TPW) % ND;
-        if (q0 + 32 * t < L) {
-          v16f acc[TPW];
-          int kscale[TPW][2], sscale[2];
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) sscale[kk] = sDSs[pb][t][2 * kk + g];
-#pragma unroll
-          for (int c = 0; c < TPW; ++c) {
-            acc[c] = v16f{};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              kscale[c][kk] = (int)((sKs[2 * kk + g] >> (8 * (dc0 + c))) & 0xFFu);
-              if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-              const v8i sb = tr_operand(sDS[pb] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-              const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * (dc0 + c), KST, lane);   // columns: features
-              acc[c] = mfma32b<0, 0>(sb, ka, acc[c], sscale[kk], kscale[c][kk]);
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < TPW; ++c) keep(acc[c][0]);
-#pragma unroll
-          for (int c = 0; c < TPW; ++c) { keep(kscale[c][0]); keep(kscale[c][1]); }
-          keep(sscale[0]); keep(sscale[1]);
-          // Packed fp16 atomics, neighbouring lanes paired (each sends the value its partner
-          // needs).  With two chunks, the even lane of a pair adds features (f, f+1) of chunk
-          // dc0 and the odd lane (f-1, f) of chunk dc0 + 1, both on row r: the 32 lanes of a
-          // half cover one whole 128-byte row.  With one chunk, the odd lane takes row r + 1.
-          const int odd = lane & 1;
-          _Float16* abase = (_Float16*)a.acc + ((long)(tok0 + q0 + 32 * t) * rowH + (long)h * D + 32 * dc0);
-          const uint32_t rh = (uint32_t)rowH;
-          // the tile's 32 rows lie within 32 rowH halves of abase
-          const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(abase, (int)(64u * rh));
-          const float mult = a.dq_mult;
-          if constexpr (TPW == 2) {
-            const uint32_t lofs = (uint32_t)(4 * g) * rh + (uint32_t)(n + (odd ? 31 : 0));
-            const int rows_left = L - q0 - 32 * t - 4 * g;   // element rows c_e below this are in range
-            auto add_tile = [&](auto checked) {
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const float x0 = acc[0][e], x1 = acc[TPW - 1][e];
-                const float send = odd ? x0 : x1;
-                const float got = __int_as_float(
-                    __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
-                const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
-                const int ce = 8 * (e >> 2) + (e & 3);
-                if (!decltype(checked)::value || ce < rows_left)
-                  atomic_add_h2_buf(ars, 2u * (lofs + (uint32_t)ce * rh), lo_v * mult, hi_v * mult);
-              }
-            };
-            if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
-            else add_tile(std::true_type{});
-          } else {
-            const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
-            const int rows_left = L - q0 - 32 * t - 4 * g - odd;
-            auto add_tile = [&](auto checked) {
-#pragma unroll
-              for (int e = 0; e < 16; e += 2) {
-                const float x0 = acc[0][e], x1 = acc[0][e + 1];
-                const float send = odd ? x0 : x1;
-                const float got = __int_as_float(
-                    __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
-                const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
-                const int ce = 8 * (e >> 2) + (e & 3);
-                if (!decltype(checked)::value || ce < rows_left)
-                  atomic_add_h2_buf(ars, 2u * (lofs + (uint32_t)ce * rh), lo_v * mult, hi_v * mult);
-              }
-            };
-            if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
-            else add_tile(std::true_type{});
-          }
-        }
-        // the dV / dK products have finished once a later result is read
-        keep(dkt[ND - 1][0]);
+        const float amax = half_swap_max(am);   // 32 queries of this key
+        const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
+        // S and dP have been read: their products (and every earlier one) are done
+        keep(qsa); keep(dsa); keep(ksc); keep(vsc);
         keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
+        // ---- MX codes (nothing visible: zero codes, scale 1)
+        const int kp = max(exp2_scale_code(amax), 1);
+        const int ks2 = max(scale_code(smax), 1);
+        const float psc = e8m0_f32(kp), plim = 448.f * psc;
+        const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
+        uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v2s z = {0, 0};
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc,
+                                                       false);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim),
+                                                       psc, true);
+          pw[q] = __builtin_bit_cast(uint32_t, z);
+          v2s y = {0, 0};
+          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
+                                                       __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc,
+                                                       false);
+          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
+                                                       __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc,
+                                                       true);
+          sw[q] = __builtin_bit_cast(uint32_t, y);
+        }
+        // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
+        auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+        auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+        auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+        auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+        pB[4 * t + 0] = a02[0]; pB[4 * t + 1] = a02[1]; pB[4 * t + 2] = a13[0]; pB[4 * t + 3] = a13[1];
+        sB[4 * t + 0] = b02[0]; sB[4 * t + 1] = b02[1]; sB[4 * t + 2] = b13[0]; sB[4 * t + 3] = b13[1];
+        *(uint4*)(sDS + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+        if (lane == 0) sDSs[t][w] = ks2;
+        kpc[t] = kp;
+        ksc2[t] = ks2;
       }
-      __syncthreads();
+      // ---- B. dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries;
+      // lane half g supplies the scale of query block g)
+      const int pscale = g ? kpc[1] : kpc[0];
+      const int sscale = g ? ksc2[1] : ksc2[0];
+      const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc) {
+        const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
+        const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
+        if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, sB, dkt[0], qw, sscale); }
+        if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, sB, dkt[1], qw, sscale); }
+        if constexpr (ND > 2) {
+          if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pB, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, sB, dkt[2], qw, sscale); }
+          if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pB, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, sB, dkt[3], qw, sscale); }
+        }
+      }
+      dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
+    } else {
+      // every key of the block comes after every query of the step: dS is zero
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      uint8_t* rowp = sDS + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
+      *(uint4*)rowp = z;
+      *(uint4*)(rowp + 16) = z;
+      if (lane == 0) {
+        sDSs[0][w] = 1;
+        sDSs[1][w] = 1;
+      }
+    }
+    // the next step's operands are in flight during the dQ products and atomics (after
+    // the last step, the last one is fetched again and its buffer rewritten)
+    const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
+    Stage nx;
+    load_step(qn, nx);
+    __syncthreads();
+
+    // ---- C. dQ tile (query block t, feature chunk dc) = (w / ND, w % ND) over the 256 keys, into
+    // the head-major fp16 accumulator [H, T, D] (a head's rows are contiguous).  Output element e
+    // of lane l: query 32t + 8(e/4) + 4g + e%4, feature 32 dc + l%32.
+    if (w < 2 * ND) {
+      const int t = w / ND, dc = w % ND;
+      if (q0 + 32 * t < L) {
+        v16f acc = v16f{};
+        int kscale[BN / 64], sscale[BN / 64];
+#pragma unroll
+        for (int kk = 0; kk < BN / 64; ++kk) {
+          sscale[kk] = sDSs[t][2 * kk + g];
+          kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
+          if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
+          const v8i sb = tr_operand(sDS + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+          const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features
+          acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
+        }
+        keep(acc[0]);
+#pragma unroll
+        for (int kk = 0; kk < BN / 64; ++kk) {
+          keep(kscale[kk]);
+          keep(sscale[kk]);
+        }
+        // packed fp16 atomics, neighbouring lanes paired: the even lane of a pair adds (row r,
+        // features f, f+1) of element e, the odd lane (row r + 1, features f-1, f) of element e + 1
+        const int odd = lane & 1;
+        _Float16* abase = (_Float16*)a.acc + (((long)h * a.T + tok0 + q0 + 32 * t) * D + 32 * dc);
+        const uint32_t rh = (uint32_t)D;
+        // the tile's 32 rows lie within 32 D halves of abase
+        const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(abase, (int)(64u * rh));
+        const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
+        const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_e below this are in range
+        const float mult = a.dq_mult;
+        auto add_tile = [&](auto checked) {
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const float x0 = acc[e], x1 = acc[e + 1];
+            const float send = odd ? x0 : x1;
+            const float got = __int_as_float(
+                __builtin_amdgcn_update_dpp(__float_as_int(send), __float_as_int(send), 0xB1, 0xF, 0xF, false));
+            const float lo_v = odd ? got : x0, hi_v = odd ? x1 : got;
+            const int ce = 8 * (e >> 2) + (e & 3);
+            if (!decltype(checked)::value || ce < rows_left)
+              atomic_add_h2_buf(ars, 2u * lofs, 2u * (uint32_t)ce * rh, lo_v * mult, hi_v * mult);
+          }
+        };
+        if (q0 + 32 * t + 32 <= L) add_tile(std::false_type{});
+        else add_tile(std::true_type{});
+      }
     }
 
-    // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
-    keep(dvt[ND - 1][0]);
-    keep(dkt[ND - 1][0]);
-    keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
-    if (kj >= L) return;
-    const long orow = (long)(tok0 + kj) * rowH + (long)h * D;
-#pragma unroll
-    for (int dc = 0; dc < ND; ++dc)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = 32 * dc + 8 * q + 4 * g;
-        const float k0 = dkt[dc][4 * q] * a.sigma, k1 = dkt[dc][4 * q + 1] * a.sigma,
-                    k2 = dkt[dc][4 * q + 2] * a.sigma, k3 = dkt[dc][4 * q + 3] * a.sigma;
-        const float v0 = dvt[dc][4 * q], v1 = dvt[dc][4 * q + 1], v2 = dvt[dc][4 * q + 2], v3 = dvt[dc][4 * q + 3];
-        if (a.grad_f32) {
-          *(float4*)((float*)a.dk + orow + d) = make_float4(k0, k1, k2, k3);
-          *(float4*)((float*)a.dv + orow + d) = make_float4(v0, v1, v2, v3);
-        } else {
-          *(uint2*)((uint16_t*)a.dk + orow + d) =
-              make_uint2(f32_to_bf16(k0) | (f32_to_bf16(k1) << 16), f32_to_bf16(k2) | (f32_to_bf16(k3) << 16));
-          *(uint2*)((uint16_t*)a.dv + orow + d) =
-              make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
-        }
-      }
+    store_step(qn, buf ^ 1, nx);
+    __syncthreads();
   }
+
+  // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
+  keep(dvt[ND - 1][0]);
+  keep(dkt[ND - 1][0]);
+  keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
+  if (kj >= L) return;
+  const long orow = (long)(tok0 + kj) * rowH + (long)h * D;
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * dc + 8 * q + 4 * g;
+      const float k0 = dkt[dc][4 * q] * a.sigma, k1 = dkt[dc][4 * q + 1] * a.sigma,
+                  k2 = dkt[dc][4 * q + 2] * a.sigma, k3 = dkt[dc][4 * q + 3] * a.sigma;
+      const float v0 = dvt[dc][4 * q], v1 = dvt[dc][4 * q + 1], v2 = dvt[dc][4 * q + 2], v3 = dvt[dc][4 * q + 3];
+      if (a.grad_f32) {
+        *(float4*)((float*)a.dk + orow + d) = make_float4(k0, k1, k2, k3);
+        *(float4*)((float*)a.dv + orow + d) = make_float4(v0, v1, v2, v3);
+      } else {
+        *(uint2*)((uint16_t*)a.dk + orow + d) =
+            make_uint2(f32_to_bf16(k0) | (f32_to_bf16(k1) << 16), f32_to_bf16(k2) | (f32_to_bf16(k3) << 16));
+        *(uint2*)((uint16_t*)a.dv + orow + d) =
+            make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
+      }
+    }
 }
 
 // ------------------------------------------------------------ dQ finalize
+template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n8) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;   // 8-element chunk of dQ [T, H, D]
   if (i >= n8) return;
-  const uint4 raw = *((const uint4*)a.acc + i);
+  const long row = i / (D / 8);                          // (token, head) row
+  const long src = ((row % a.H) * (long)a.T + row / a.H) * (D / 8) + i % (D / 8);
+  const uint4 raw = *((const uint4*)a.acc + src);
   const _Float16* hp = (const _Float16*)&raw;
   float v[8];
 #pragma unroll
@@ -600,7 +555,7 @@ hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_l
   }
   // 2. main
   {
-    constexpr int BN = 128;
+    constexpr int BN = 256;   // keys per workgroup
     a.nkt = (max_len + BN - 1) / BN;
     const long units = (long)a.nseq * a.H;
     const long grid = ((units + 7) / 8) * 8 * a.nkt;
@@ -616,7 +571,8 @@ hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_l
   {
     const long n8 = rows * D / 8;
     dim3 g((unsigned)((n8 + 255) / 256)), b(256);
-    bwd_dq_kernel<<<g, b, 0, st>>>(a, n8);
+    if (D == 64) bwd_dq_kernel<64><<<g, b, 0, st>>>(a, n8);
+    else bwd_dq_kernel<128><<<g, b, 0, st>>>(a, n8);
     return hipGetLastError();
   }
 }
