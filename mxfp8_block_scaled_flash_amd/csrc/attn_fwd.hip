@@ -14,9 +14,10 @@
 //    v_mfma_scale_f32_32x32x64_f8f6f4, so every lane holds one query and 16
 //    keys of each 32-key block: the row max needs one cross-lane step and the
 //    block scale of P is set per lane.
-//  * Softmax runs in the log2 domain under an integer frame M = ceil(max t),
-//    so rescaling O and l is an exact power of two and P's codes do not depend
-//    on how keys are tiled.
+//  * Softmax runs in the log2 domain under an integer frame M (moved lazily,
+//    once ceil(max t) exceeds it by more than 8), so rescaling O and l is an
+//    exact power of two and P's codes do not depend on how keys are tiled
+//    (up to the fp32 rounding of the argument t - M).
 //  * P's block amax is 2^(block max of t - M), so its E8M0 scale follows
 //    from the maxima already reduced for M, with no extra exp (and no
 //    dependence on the accuracy of the hardware exp2).  The fp32->fp8 convert (which divides by
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
   constexpr int KST = D + 16;   // LDS row stride of the K and V tiles
+  constexpr float kLazy = 8.f;  // largest log2 of p before the frame moves
   constexpr int NT = NW * 64;
   static_assert(BN * D / 16 % NT == 0, "tile chunks must divide among the threads");
   // two buffers: the tile being computed and the next one, written while it is computed
@@ -224,13 +226,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       keep(ksc[1]);
       keep(vsc_prev);
       keep(psc_prev);
-      const float m_new = fmaxf(m_run, ceilf(fmaxf(bm[0], bm[1]) * c));
-      if (m_new > m_run) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_new));
+      // Lazy frame: M moves (and O, l are rescaled by 2^(M_old - M_new)) only once the tile's
+      // ceil(max) exceeds it by more than kLazy, so p stays below 2^kLazy.  In exact arithmetic
+      // every frame gives P^ the same codes (its scales absorb the power of two) and the same
+      // O and LSE; in fp32 the argument S c - M rounds at the frame's magnitude.
+      const float m_tile = ceilf(fmaxf(bm[0], bm[1]) * c);
+      if (m_tile > m_run + kLazy) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_tile));
 #pragma unroll
         for (int dc = 0; dc < ND; ++dc) o[dc] *= alpha;
         l_run *= alpha;
-        m_run = m_new;
+        m_run = m_tile;
       }
       const float negM = -m_run;
       // ---- p = 2^(S c - M), running sum
