@@ -76,12 +76,6 @@ MX_DEV void atomic_add_h2(_Float16* p, float a, float b) {
   __builtin_amdgcn_global_atomic_fadd_v2f16((h2v __attribute__((address_space(1)))*)(p), v);
 }
 
-// Buffer resource over `bytes` bytes from base (raw, untyped accesses; the
-// word-3 value is the gfx9-family default for such buffers).
-MX_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
-}
-
 // Packed fp16 atomic add through a buffer resource: a 32-bit byte offset from
 // a scalar base (buffer_atomic_pk_add_f16).
 MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float a, float b) {
@@ -191,7 +185,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int u = (jj / a.nkt) * 8 + xcd;
   if (u >= a.nseq * a.H) return;
   const int kt = jj % a.nkt;          // low key tiles see the most queries under causality: first
-  const int h = u % a.H, s = u / a.H;
+  const int h = __builtin_amdgcn_readfirstlane(u % a.H), s = __builtin_amdgcn_readfirstlane(u / a.H);
   int tok0, L, srow0, sblk0;
   a.seq.get(s, tok0, L, srow0, sblk0);
   const int kbase = kt * BN;

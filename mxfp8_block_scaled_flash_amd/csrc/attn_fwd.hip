@@ -89,55 +89,65 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   const int u = (j / a.nqt) * 8 + xcd;
   if (u >= a.nseq * a.H) return;
   const int qt = a.nqt - 1 - (j % a.nqt);
-  const int h = u % a.H, s = u / a.H;
+  const int h = __builtin_amdgcn_readfirstlane(u % a.H), s = __builtin_amdgcn_readfirstlane(u / a.H);
   int tok0, L, srow0, sblk0;
   a.seq.get(s, tok0, L, srow0, sblk0);
+  // wave-uniform (they come from the workgroup index): lets the buffer resources live in SGPRs
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);
+  L = __builtin_amdgcn_readfirstlane(L);
+  srow0 = __builtin_amdgcn_readfirstlane(srow0);
+  sblk0 = __builtin_amdgcn_readfirstlane(sblk0);
   const int qbase = qt * BM;
   if (qbase >= L) return;
   const int q0 = qbase + 32 * w;
   const int qi = q0 + n;
   const long rowH = (long)a.H * D;
 
-  // ---- staging of one K/V tile: global loads into registers, then LDS stores
-  // Loads are branch-free (rows past the end are clamped to the last key and
-  // zeroed when stored), so no wait on them is forced before the tile that is
-  // being computed needs it.  Every wave fetches the scales of key `lane`;
-  // wave 0 stores the K ones, wave 1 the V ones.
+  // ---- staging of one K/V tile: buffer loads into registers, then LDS stores.
+  // Each tile gets scalar buffer resources that end with the sequence, so rows
+  // (and scale blocks) past its end read as zero: no clamps, no branches, and no
+  // wait on the loads before the tile being computed needs them.  Every wave
+  // fetches the scales of key `lane`; wave 0 stores the K ones, wave 1 the V ones.
+  const int KSB = D / 32;   // bytes per K ROW32 scale word
   auto load_tile = [&](int t, KVStage<D, NT>& st) {
     const int k0 = t * BN;
+    const int rows = min(BN, L - k0);   // >= 1
+    const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
+    const int nrec = (rows - 1) * (int)rowH + D;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tb, nrec), rv = buffer_rsrc(a.v + tb, nrec);
 #pragma unroll
     for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
       const int ch = tid + c * NT;
-      const int r = ch / (D / 16), cx = ch % (D / 16);
-      const long off = (long)(tok0 + min(k0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
-      st.k[c] = *(const uint4*)(a.k + off);
-      st.v[c] = *(const uint4*)(a.v + off);
+      const int off = (ch / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
+      st.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      st.v[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-    const long srow = ((long)(srow0 + min(k0 + lane, L - 1)) * a.H + h);
-    st.ks = (D == 128) ? *(const uint32_t*)(a.ks + srow * 4) : *(const uint16_t*)(a.ks + srow * 2);
-    const int vblk = min(2 * t + (lane >> 5), (L - 1) >> 5);
-    const uint8_t* vp = a.vs + ((long)(sblk0 + vblk) * a.H + h) * D + (lane & 31);
+    const __amdgpu_buffer_rsrc_t rks =
+        buffer_rsrc(a.ks + ((long)(srow0 + k0) * a.H + h) * KSB, (rows - 1) * a.H * KSB + KSB);
+    st.ks = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, lane * a.H * KSB, 0, 0)
+                       : __builtin_amdgcn_raw_buffer_load_b16(rks, lane * a.H * KSB, 0, 0);
+    const int nblk = (rows + 31) / 32;
+    const __amdgpu_buffer_rsrc_t rvs =
+        buffer_rsrc(a.vs + ((long)(sblk0 + 2 * t) * a.H + h) * D, (nblk - 1) * a.H * D + D);
+    const int voff = (lane >> 5) * a.H * D + (lane & 31);
 #pragma unroll
-    for (int dc = 0; dc < ND; ++dc) st.vb[dc] = vp[32 * dc];
+    for (int dc = 0; dc < ND; ++dc) st.vb[dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
   };
-  auto store_tile = [&](int t, int buf, const KVStage<D, NT>& st) {
-    const int k0 = t * BN;
+  auto store_tile = [&](int buf, const KVStage<D, NT>& st) {
 #pragma unroll
     for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
       const int ch = tid + c * NT;
       const int r = ch / (D / 16), cx = ch % (D / 16);
-      const uint32_t m = (k0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
-      const uint4 kk = st.k[c], vv = st.v[c];
-      *(uint4*)(&sK[buf][r * KST + cx * 16]) = make_uint4(kk.x & m, kk.y & m, kk.z & m, kk.w & m);
-      *(uint4*)(&sV[buf][r * KST + cx * 16]) = make_uint4(vv.x & m, vv.y & m, vv.z & m, vv.w & m);
+      *(uint4*)(&sK[buf][r * KST + cx * 16]) = st.k[c];
+      *(uint4*)(&sV[buf][r * KST + cx * 16]) = st.v[c];
     }
     if (w == 0) {
-      sKs[buf][lane] = (k0 + lane < L) ? st.ks : 0u;
+      sKs[buf][lane] = st.ks;
     } else if (w == 1) {
       uint32_t vs = 0;
 #pragma unroll
       for (int dc = 0; dc < ND; ++dc) vs |= st.vb[dc] << (8 * dc);
-      sVs[buf][lane] = ((2 * t + (lane >> 5)) * 32 < L) ? vs : 0u;
+      sVs[buf][lane] = vs;
     }
   };
 
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   {
     KVStage<D, NT> st0;
     load_tile(0, st0);
-    store_tile(0, 0, st0);
+    store_tile(0, st0);
   }
   __syncthreads();
 
@@ -204,13 +214,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
       if (need_mask) {
+        // element i is key k0 + 32 kb + 4g + c_i, c_i = 8(i/4) + i%4: visible iff c_i < hi
+        const int last = CAUSAL ? min(L - 1, qi) : L - 1;   // last visible key of this query
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int hi = last - k0 - 32 * kb - 4 * g + 1;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= L || (CAUSAL && key > qi)) st[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i) st[kb][i] = (8 * (i >> 2) + (i & 3) < hi) ? st[kb][i] : -INFINITY;
+        }
       }
       // ---- block maxima, frame update
       float bm[2];
@@ -265,7 +276,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          v2s z = {0, 0};
+          // the two converts fill both halves of z, so any register serves as its old value
+          v2s z = __builtin_bit_cast(v2s, st[kb][4 * q]);
           z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q], lim[kb]), clampp(st[kb][4 * q + 1], lim[kb]),
                                                        sc[kb], false);
           z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q + 2], lim[kb]),
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       vsc_prev = vsc;
       psc_prev = psc;
     }
-    store_tile(tn, cur ^ 1, nxt);
+    store_tile(cur ^ 1, nxt);
     __syncthreads();
   }
 

@@ -52,10 +52,24 @@ MX_DEV int scale_code(float amax) {
 // interval).  No other fp32 a lies that close below an integer.  This makes
 // the decision independent of the accuracy of the hardware exp2.
 MX_DEV int exp2_scale_code(float a_max) {
-  if (!(a_max > -1.0e30f)) return 0;   // empty or fully masked block
-  float f = floorf(a_max);
-  if (a_max < 0.f && a_max >= __uint_as_float(0xB338AA3Bu)) f = 0.f;
+  // branch-free: an empty or fully masked block (a_max = -inf) ends at code 0
+  float f = fmaxf(floorf(a_max), -256.f);
+  f = (a_max < 0.f && a_max >= __uint_as_float(0xB338AA3Bu)) ? 0.f : f;
   return min(max((int)f + 119, 0), 254);
+}
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes from base (untyped accesses; word 3 is
+// the gfx9-family default).  Loads past `bytes` return zero.  base and bytes
+// must be the same in every lane of the wave: they are read from the first
+// lane, so the resource sits in scalar registers.
+MX_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  const uint64_t v = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // 2^(k-127) as an fp32 value, for k in [1, 254].
