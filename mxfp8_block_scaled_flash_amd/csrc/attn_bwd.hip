@@ -188,6 +188,10 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int h = __builtin_amdgcn_readfirstlane(u % a.H), s = __builtin_amdgcn_readfirstlane(u / a.H);
   int tok0, L, srow0, sblk0;
   a.seq.get(s, tok0, L, srow0, sblk0);
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);   // wave-uniform (from the workgroup index)
+  L = __builtin_amdgcn_readfirstlane(L);
+  srow0 = __builtin_amdgcn_readfirstlane(srow0);
+  sblk0 = __builtin_amdgcn_readfirstlane(sblk0);
   const int kbase = kt * BN;
   if (kbase >= L) return;
   const long rowH = (long)a.H * D;
@@ -214,8 +218,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   for (int r = tid; r < BN; r += NT)
     sVs[r] = (kbase + r < L) ? ld_scale_word(a.vs + ((long)(srow0 + kbase + r) * a.H + h) * NB, NB) : 0u;
 
-  // ---- staging of one query step.  Loads are branch-free: rows past the end
-  // are clamped to the last query and zeroed (or masked later) when stored.
+  // ---- staging of one query step
   struct Stage {
     uint4 x[CPT];
     float l, d;
@@ -224,38 +227,47 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   auto lse_index = [&](int q) -> long {
     return a.seq.cu ? (long)h * a.T + tok0 + q : ((long)s * a.H + h) * a.seq.S + q;
   };
+  // Per-step buffer resources end with the sequence: rows, LSE/D entries and
+  // scale blocks past its end read as zero (masked later), with no clamps.
   auto load_step = [&](int q0, Stage& st) {
+    const int rows = min(BQ, L - q0);   // >= 1
+    const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
+    const int nrec = (rows - 1) * (int)rowH + D;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + tb, nrec), rdo = buffer_rsrc(a.dob + tb, nrec);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
-      const long off = (long)(tok0 + min(q0 + r, L - 1)) * rowH + (long)h * D + cx * 16;
-      st.x[c] = *(const uint4*)((ch < QCH ? a.q : a.dob) + off);
+      const int ch = tid + c * NT;   // Q chunks first, then dO (the split falls between waves)
+      const int off = ((ch % QCH) / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
+      st.x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(c * NT + 64 * w < QCH ? rq : rdo, off, 0, 0));
     }
-    const long li = lse_index(min(q0 + lane, L - 1));
-    st.l = a.lse[li];
-    st.d = a.Dbuf[li];
-    const long so = ((long)(sblk0 + min(q0 / 32 + (lane & 1), (L - 1) / 32)) * a.H + h) * NB;
-    st.qs = ld_scale_word(a.qs + so, NB);
-    st.dos = ld_scale_word(a.dos + so, NB);
+    const long li = lse_index(q0);
+    st.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + li, rows * 4), lane * 4, 0, 0));
+    st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.Dbuf + li, rows * 4), lane * 4, 0, 0));
+    const long so = ((long)(sblk0 + q0 / 32) * a.H + h) * NB;
+    const int snrec = ((rows + 31) / 32 - 1) * a.H * NB + NB;
+    const int soff = (lane & 1) * a.H * NB;
+    if constexpr (NB == 4) {
+      st.qs = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
+      st.dos = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
+    } else {
+      st.qs = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
+      st.dos = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
+    }
   };
-  auto store_step = [&](int q0, int buf, const Stage& st) {
+  auto store_step = [&](int buf, const Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * NT;
       const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
-      const uint32_t m = (q0 + r < L) ? ~0u : 0u;   // a mask, not a select (keeps st in registers)
-      const uint4 x = st.x[c];
       uint8_t* dst = (ch < QCH ? sQ[buf] : sDO[buf]) + r * KST + cx * 16;
-      *(uint4*)dst = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+      *(uint4*)dst = st.x[c];
     }
     if (w == 0) {
       sL[buf][lane] = st.l * 1.44269504088896340736f;
       sDv[buf][lane] = st.d;
     } else if (w == 1 && lane < 2) {
-      const bool ok = q0 + 32 * lane < L;
-      sQs[buf][lane] = ok ? st.qs : 0u;
-      sDOs[buf][lane] = ok ? st.dos : 0u;
+      sQs[buf][lane] = st.qs;
+      sDOs[buf][lane] = st.dos;
     }
   };
 
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   {
     Stage st0;
     load_step(qstart, st0);
-    store_step(qstart, 0, st0);
+    store_step(0, st0);
   }
   __syncthreads();
 
@@ -357,13 +369,14 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          v2s z = {0, 0};
+          // the two converts fill both halves, so any register serves as the old value
+          v2s z = __builtin_bit_cast(v2s, st[4 * q]);
           z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc,
                                                        false);
           z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim),
                                                        psc, true);
           pw[q] = __builtin_bit_cast(uint32_t, z);
-          v2s y = {0, 0};
+          v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
           y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
                                                        __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc,
                                                        false);
@@ -470,7 +483,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       }
     }
 
-    store_step(qn, buf ^ 1, nx);
+    store_step(buf ^ 1, nx);
     __syncthreads();
   }
 
