@@ -143,6 +143,24 @@ def main():
     b_ms = sum(r[2].elapsed_time(r[3]) for r in recs) / len(recs) if do_bwd else 0.0
     ms_step = total_ms / args.steps
 
+    # fused RMSNorm + quantize (the upstream producer of the Q / K operands; outside the step):
+    # Q through ROW32 + SQ32, timed alone on the same stream
+    gamma = torch.ones(D, dtype=torch.float32, device="cuda")
+    rq = mx.alloc_quantized(x["q"].shape, ROW | SQ, x["q"].device)
+
+    def rmsnorm_q():
+        mx.mx_rmsnorm_quantize(x["q"], gamma, 1e-6, B, S, H, D, ROW | SQ, rq[ROW][0], rq[ROW][1], None, None,
+                               rq[SQ][0], rq[SQ][1])
+
+    rmsnorm_q()
+    r0, r1 = ev(), ev()
+    r0.record(stream)
+    for _ in range(5):
+        rmsnorm_q()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    n_ms = r0.elapsed_time(r1) / 5
+
     pairs = B * H * S * (S + 1) / 2
     f_flop = 4.0 * D * pairs
     b_flop = 10.0 * D * pairs if do_bwd else 0.0
@@ -180,6 +198,8 @@ def main():
         "bwd_pct_peak": round(100 * b_tflops / MXFP8_PEAK_TFLOPS, 2) if b_tflops else None,
         "quantize_ms": round(q_ms, 4),
         "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "rmsnorm_quantize_ms": round(n_ms, 4),
+        "rmsnorm_quantize_gbs": round(B * S * H * D * (2 + per_layout[ROW] + per_layout[SQ]) / (n_ms * 1e-3) / 1e9, 1),
         "fwd_ms": round(f_ms, 4),
         "bwd_ms": round(b_ms, 4) if do_bwd else None,
         "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),

@@ -136,6 +136,41 @@ mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype,
                              hipStream_t stream);
 
 /*
+ * mx_rmsnorm_quantize -- fused RMSNorm + MX quantization (one read of x).
+ * Defines: [News], contributions paragraph (fused RMSNorm + Quantize
+ * producers emitting FP8 with several scale layouts in one pass).  The
+ * pages give no formula; this library's reading (the usual RMSNorm, per
+ * (token, head) row over D, as for normalized query and key heads):
+ *   rstd = fl32(1 / sqrt(sum_d x_d^2 / D + eps))   (sum, divide, sqrt and
+ *          reciprocal in fp64; the squares of bf16 / fp32 inputs are exact)
+ *   y_d  = fl32(fl32(x_d * rstd) * gamma_d)
+ * then y is quantized exactly as mx_quantize quantizes x.
+ *   gamma   device fp32 [D], 4-byte aligned (read only)
+ *   eps     finite, >= 0
+ * Everything else (layouts, shapes, outputs, errors) as mx_quantize;
+ * MX_EINVAL also for a null or misaligned gamma or a bad eps.
+ */
+mx_status mx_rmsnorm_quantize(const void* x, mx_dtype x_dtype, const float* gamma, float eps,
+                              int B, int S, int H, int D, unsigned layouts,
+                              uint8_t* row32_data, uint8_t* row32_scale,
+                              uint8_t* col32_data, uint8_t* col32_scale,
+                              uint8_t* sq32_data, uint8_t* sq32_scale,
+                              hipStream_t stream);
+
+/*
+ * mx_rmsnorm_quantize_varlen -- mx_rmsnorm_quantize for a packed [T, H, D]
+ * tensor; the sequence arguments as mx_quantize_varlen.
+ */
+mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const float* gamma, float eps,
+                                     const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                                     int total_tokens, int total_scale_rows, int H, int D,
+                                     unsigned layouts,
+                                     uint8_t* row32_data, uint8_t* row32_scale,
+                                     uint8_t* col32_data, uint8_t* col32_scale,
+                                     uint8_t* sq32_data, uint8_t* sq32_scale,
+                                     hipStream_t stream);
+
+/*
  * mx_attn_fwd -- fused MXFP8 attention forward.
  * Defines: [Blog], "1. End-to-End Block-Scaled GEMM Fusion" (S = Q K^T and
  * P V both on block-scaled operands, nothing written to HBM in between) and

@@ -31,6 +31,10 @@ _SIGS = {
     "mx_varlen_scale_offsets": ([_vp, _c_int, _vp, _vp], _c_int),
     "mx_quantize_varlen": ([_vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint]
                            + [_vp] * 6 + [_vp], _c_int),
+    "mx_rmsnorm_quantize": ([_vp, _c_int, _vp, _c_float, _c_int, _c_int, _c_int, _c_int, ctypes.c_uint]
+                            + [_vp] * 6 + [_vp], _c_int),
+    "mx_rmsnorm_quantize_varlen": ([_vp, _c_int, _vp, _c_float, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
@@ -121,6 +125,23 @@ def mx_quantize_varlen(x, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_s
                                     _ptr(sq32_scale), _stream(stream)), "mx_quantize_varlen")
 
 
+def mx_rmsnorm_quantize(x, gamma, eps, B, S, H, D, layouts, row32_data, row32_scale, col32_data, col32_scale,
+                        sq32_data, sq32_scale, stream=None):
+    _check(lib().mx_rmsnorm_quantize(_ptr(x), _dtype_code(x.dtype), _ptr(gamma), float(eps), B, S, H, D, layouts,
+                                     _ptr(row32_data), _ptr(row32_scale), _ptr(col32_data), _ptr(col32_scale),
+                                     _ptr(sq32_data), _ptr(sq32_scale), _stream(stream)), "mx_rmsnorm_quantize")
+
+
+def mx_rmsnorm_quantize_varlen(x, gamma, eps, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows, H,
+                               D, layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale,
+                               stream=None):
+    _check(lib().mx_rmsnorm_quantize_varlen(_ptr(x), _dtype_code(x.dtype), _ptr(gamma), float(eps),
+                                            _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq, total_tokens,
+                                            total_scale_rows, H, D, layouts, _ptr(row32_data), _ptr(row32_scale),
+                                            _ptr(col32_data), _ptr(col32_scale), _ptr(sq32_data), _ptr(sq32_scale),
+                                            _stream(stream)), "mx_rmsnorm_quantize_varlen")
+
+
 def mx_attn_fwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal, o, lse,
                 stream=None):
     _check(lib().mx_attn_fwd(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
@@ -194,6 +215,17 @@ def quantize(x, layouts=ROW32 | COL32 | SQ32):
     return out
 
 
+def rmsnorm_quantize(x, gamma, eps=1e-6, layouts=ROW32 | COL32 | SQ32):
+    """Fused RMSNorm (over D, gain ``gamma`` fp32 [D]) + MX quantization of a [B, S, H, D]
+    tensor; returns {layout: (data, scale)}."""
+    B, S, H, D = x.shape
+    out = alloc_quantized(x.shape, layouts, x.device)
+    g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
+    mx_rmsnorm_quantize(x, gamma, eps, B, S, H, D, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0), g(COL32, 1),
+                        g(SQ32, 0), g(SQ32, 1))
+    return out
+
+
 def padded_scale_rows(seqlens) -> int:
     return int(sum((int(L) + 127) // 128 * 128 for L in seqlens))
 
@@ -209,6 +241,21 @@ def quantize_varlen(x, cu_seqlens, seqlens, layouts=ROW32 | COL32 | SQ32):
     g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
     mx_quantize_varlen(x, cu_seqlens, csr, nseq, T, Tp, H, D, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0),
                        g(COL32, 1), g(SQ32, 0), g(SQ32, 1))
+    return out, csr
+
+
+def rmsnorm_quantize_varlen(x, gamma, cu_seqlens, seqlens, eps=1e-6, layouts=ROW32 | COL32 | SQ32):
+    """Fused RMSNorm + MX quantization of a packed [T, H, D] tensor; returns
+    ({layout: (data, scale)}, cu_scale_rows)."""
+    T, H, D = x.shape
+    nseq = len(seqlens)
+    Tp = padded_scale_rows(seqlens)
+    csr = torch.empty(nseq + 1, dtype=torch.int32, device=x.device)
+    mx_varlen_scale_offsets(cu_seqlens, nseq, csr)
+    out = alloc_quantized(x.shape, layouts, x.device, Tp)
+    g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
+    mx_rmsnorm_quantize_varlen(x, gamma, eps, cu_seqlens, csr, nseq, T, Tp, H, D, layouts, g(ROW32, 0),
+                               g(ROW32, 1), g(COL32, 0), g(COL32, 1), g(SQ32, 0), g(SQ32, 1))
     return out, csr
 
 

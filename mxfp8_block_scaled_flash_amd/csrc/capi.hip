@@ -70,9 +70,14 @@ const char* mx_status_str(mx_status s) {
   return "unknown mx_status";
 }
 
-mx_status mx_quantize(const void* x, mx_dtype x_dtype, int B, int S, int H, int D, unsigned layouts,
-                      uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
-                      uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the plain and the fused RMSNorm quantizers (gamma == nullptr: plain).
+mx_status quantize_fixed(const void* x, mx_dtype x_dtype, const float* gamma, float eps, int B, int S, int H, int D,
+                         unsigned layouts, uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data,
+                         uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
   if (B < 0 || S < 0 || H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
   if (!valid_layouts(layouts)) return MX_EINVAL;
@@ -94,19 +99,15 @@ mx_status mx_quantize(const void* x, mx_dtype x_dtype, int B, int S, int H, int 
   a.row_data = row32_data; a.row_scale = row32_scale;
   a.col_data = col32_data; a.col_scale = col32_scale;
   a.sq_data = sq32_data; a.sq_scale = sq32_scale;
-  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, a, stream));
+  a.gamma = gamma;
+  a.eps = (double)eps;
+  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, gamma != nullptr, a, stream));
 }
 
-mx_status mx_varlen_scale_offsets(const int32_t* cu_seqlens, int nseq, int32_t* cu_scale_rows, hipStream_t stream) {
-  if (nseq < 1 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
-  if (mx_status st = check_device()) return st;
-  return from_hip(mxk::launch_scale_offsets(cu_seqlens, nseq, cu_scale_rows, stream));
-}
-
-mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens, const int32_t* cu_scale_rows,
-                             int nseq, int total_tokens, int total_scale_rows, int H, int D, unsigned layouts,
-                             uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
-                             uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+mx_status quantize_jagged(const void* x, mx_dtype x_dtype, const float* gamma, float eps, const int32_t* cu_seqlens,
+                          const int32_t* cu_scale_rows, int nseq, int total_tokens, int total_scale_rows, int H, int D,
+                          unsigned layouts, uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data,
+                          uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
   if (nseq < 1 || total_tokens < 0 || total_scale_rows < 0 || total_scale_rows % 128 != 0) return MX_EINVAL;
   if (total_scale_rows < total_tokens) return MX_EINVAL;
   if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
@@ -131,7 +132,60 @@ mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_
   a.row_data = row32_data; a.row_scale = row32_scale;
   a.col_data = col32_data; a.col_scale = col32_scale;
   a.sq_data = sq32_data; a.sq_scale = sq32_scale;
-  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, a, stream));
+  a.gamma = gamma;
+  a.eps = (double)eps;
+  return from_hip(mxk::launch_quantize(x, x_dtype == MX_F32, D, gamma != nullptr, a, stream));
+}
+
+bool valid_norm(const float* gamma, float eps) {
+  return gamma && (reinterpret_cast<uintptr_t>(gamma) & 3u) == 0 && std::isfinite(eps) && eps >= 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_quantize(const void* x, mx_dtype x_dtype, int B, int S, int H, int D, unsigned layouts,
+                      uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
+                      uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+  return quantize_fixed(x, x_dtype, nullptr, 0.f, B, S, H, D, layouts, row32_data, row32_scale, col32_data,
+                        col32_scale, sq32_data, sq32_scale, stream);
+}
+
+mx_status mx_rmsnorm_quantize(const void* x, mx_dtype x_dtype, const float* gamma, float eps, int B, int S, int H,
+                              int D, unsigned layouts, uint8_t* row32_data, uint8_t* row32_scale,
+                              uint8_t* col32_data, uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale,
+                              hipStream_t stream) {
+  if (!valid_norm(gamma, eps)) return MX_EINVAL;
+  return quantize_fixed(x, x_dtype, gamma, eps, B, S, H, D, layouts, row32_data, row32_scale, col32_data,
+                        col32_scale, sq32_data, sq32_scale, stream);
+}
+
+mx_status mx_varlen_scale_offsets(const int32_t* cu_seqlens, int nseq, int32_t* cu_scale_rows, hipStream_t stream) {
+  if (nseq < 1 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_scale_offsets(cu_seqlens, nseq, cu_scale_rows, stream));
+}
+
+mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens, const int32_t* cu_scale_rows,
+                             int nseq, int total_tokens, int total_scale_rows, int H, int D, unsigned layouts,
+                             uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data, uint8_t* col32_scale,
+                             uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
+  return quantize_jagged(x, x_dtype, nullptr, 0.f, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows,
+                         H, D, layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale,
+                         stream);
+}
+
+mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const float* gamma, float eps,
+                                     const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                                     int total_tokens, int total_scale_rows, int H, int D, unsigned layouts,
+                                     uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data,
+                                     uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale,
+                                     hipStream_t stream) {
+  if (!valid_norm(gamma, eps)) return MX_EINVAL;
+  return quantize_jagged(x, x_dtype, gamma, eps, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows,
+                         H, D, layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale,
+                         stream);
 }
 
 static mx_status fwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,

@@ -14,6 +14,8 @@ struct QuantArgs {
   long nwaves;        // one wave per (sequence or batch, 32-token block, head)
   unsigned layouts;   // bit 0 ROW32, bit 1 COL32, bit 2 SQ32
   uint8_t *row_data, *row_scale, *col_data, *col_scale, *sq_data, *sq_scale;
+  const float* gamma; // RMSNorm gain [D] (fused RMSNorm + quantize only)
+  double eps;         // RMSNorm epsilon
 };
 
 struct FwdArgs {
@@ -48,7 +50,7 @@ struct BwdArgs {
   float* Dbuf;          // D_i (workspace), indexed like lse
 };
 
-hipError_t launch_quantize(const void* x, bool fp32, int D, const QuantArgs& a, hipStream_t st);
+hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const QuantArgs& a, hipStream_t st);
 hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipStream_t st);
 hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);

@@ -10,6 +10,13 @@
 // token positions and pads only the scale rows to 128-row boundaries (same
 // paragraph).
 //
+// The fused RMSNorm + quantize variant (the same paragraph's "fused RMSNorm +
+// Quantize" producer) normalizes each (token, head) row over D first:
+// rstd = fl32(1 / sqrt(sum(x^2) / D + eps)) with the sum of squares, the
+// division, the square root and the reciprocal in fp64 (the squares of bf16 or
+// fp32 inputs are exact there), then y = fl32(fl32(x rstd) gamma), and
+// quantizes y.
+//
 // Work unit: one wavefront per (sequence, 32-token block, head): a 32 x D
 // tile, read once with 16-byte loads (row = D contiguous elements), reduced
 // for all three block shapes in registers (cross-lane steps by shuffles), and
@@ -21,7 +28,7 @@
 
 namespace mxk {
 
-template <typename T, int D>
+template <typename T, int D, bool NORM>
 __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, QuantArgs a) {
   constexpr int ES = sizeof(T);
   constexpr int CPR = D * ES / 16;   // 16-byte chunks per token row
@@ -71,6 +78,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, 
     } else {
       v[p][0] = __uint_as_float(w.x); v[p][1] = __uint_as_float(w.y);
       v[p][2] = __uint_as_float(w.z); v[p][3] = __uint_as_float(w.w);
+    }
+  }
+
+  if constexpr (NORM) {
+    // ---- RMSNorm of each row over D: the row's CPR lanes are neighbours
+    float gm[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) gm[e] = a.gamma[cc * EPC + e];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      double ss = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ss += (double)v[p][e] * (double)v[p][e];
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+      const float rstd = (float)(1.0 / sqrt(ss / (double)D + a.eps));
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[p][e] = (v[p][e] * rstd) * gm[e];
     }
   }
 
@@ -194,16 +219,23 @@ __global__ void scale_offsets_kernel(const int32_t* __restrict__ cu, int nseq, i
   }
 }
 
-hipError_t launch_quantize(const void* x, bool fp32, int D, const QuantArgs& a, hipStream_t st) {
+template <bool NORM>
+static void launch_quantize_t(const void* x, bool fp32, int D, const QuantArgs& a, dim3 grid, dim3 block,
+                              hipStream_t st) {
+  if (fp32) {
+    if (D == 64) quantize_kernel<float, 64, NORM><<<grid, block, 0, st>>>((const float*)x, a);
+    else quantize_kernel<float, 128, NORM><<<grid, block, 0, st>>>((const float*)x, a);
+  } else {
+    if (D == 64) quantize_kernel<uint16_t, 64, NORM><<<grid, block, 0, st>>>((const uint16_t*)x, a);
+    else quantize_kernel<uint16_t, 128, NORM><<<grid, block, 0, st>>>((const uint16_t*)x, a);
+  }
+}
+
+hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const QuantArgs& a, hipStream_t st) {
   if (a.nwaves == 0) return hipSuccess;
   dim3 grid((unsigned)((a.nwaves + 3) / 4)), block(256);
-  if (fp32) {
-    if (D == 64) quantize_kernel<float, 64><<<grid, block, 0, st>>>((const float*)x, a);
-    else quantize_kernel<float, 128><<<grid, block, 0, st>>>((const float*)x, a);
-  } else {
-    if (D == 64) quantize_kernel<uint16_t, 64><<<grid, block, 0, st>>>((const uint16_t*)x, a);
-    else quantize_kernel<uint16_t, 128><<<grid, block, 0, st>>>((const uint16_t*)x, a);
-  }
+  if (rmsnorm) launch_quantize_t<true>(x, fp32, D, a, grid, block, st);
+  else launch_quantize_t<false>(x, fp32, D, a, grid, block, st);
   return hipGetLastError();
 }
 

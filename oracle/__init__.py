@@ -15,4 +15,4 @@ External specifications used where the pages are silent: the OCP 8-bit
 floating point specification (E4M3 encoding) and the OCP Microscaling (MX)
 v1.0 specification (E8M0 shared-scale selection).
 """
-from . import mx, attention  # noqa: F401
+from . import mx, attention, norm  # noqa: F401

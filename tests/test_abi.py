@@ -82,6 +82,26 @@ def test_varlen_rejects_invalid_arguments():
                                 None, None) == EINVAL
 
 
+@pytest.mark.parametrize("gamma,eps", [(None, 1e-6), (16, -1.0), (16, float("nan")), (16, float("inf")), (18, 1e-6)])
+def test_rmsnorm_quantize_rejects_invalid_norm_arguments(gamma, eps):
+    L = mx.lib()
+    # null or misaligned gain, negative or non-finite epsilon: rejected before any device work
+    assert L.mx_rmsnorm_quantize(16, mx.BF16, gamma, eps, 1, 32, 1, 128, mx.ROW32, 16, 16, None, None, None, None,
+                                 None) == EINVAL
+    assert L.mx_rmsnorm_quantize_varlen(16, mx.BF16, gamma, eps, 16, 16, 1, 10, 128, 1, 128, mx.ROW32, 16, 16,
+                                        None, None, None, None, None) == EINVAL
+
+
+def test_rmsnorm_quantize_rejects_invalid_shapes():
+    L = mx.lib()
+    assert L.mx_rmsnorm_quantize(16, mx.BF16, 16, 1e-6, 1, 32, 1, 96, mx.ROW32, 16, 16, None, None, None, None,
+                                 None) == EINVAL
+    assert L.mx_rmsnorm_quantize(16, mx.F16, 16, 1e-6, 1, 32, 1, 128, mx.ROW32, 16, 16, None, None, None, None,
+                                 None) == EINVAL
+    assert L.mx_rmsnorm_quantize(16, mx.BF16, 16, 1e-6, 1, 32, 1, 128, 0, 16, 16, None, None, None, None,
+                                 None) == EINVAL
+
+
 def test_workspace_size():
     n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
     assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
