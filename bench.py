@@ -161,6 +161,33 @@ def main():
     torch.cuda.synchronize()
     n_ms = r0.elapsed_time(r1) / 5
 
+    # fused GEMM + quantize (the projection that produces Q; outside the step): tokens x (H D) from a
+    # hidden state of width H D, MX operands made by the quantizer, C written as ROW32 + SQ32
+    gM, gN, gK = B * S, H * D, H * D
+    hid = torch.randn((1, gM, gK // 128, 128), device=dev, dtype=torch.bfloat16)
+    wgt = torch.randn((1, gN, gK // 128, 128), device=dev, dtype=torch.bfloat16) * (1.0 / math.sqrt(gK))
+    ga, gb = mx.alloc_quantized(hid.shape, ROW, dev), mx.alloc_quantized(wgt.shape, ROW, dev)
+    mx.mx_quantize(hid, 1, gM, gK // 128, 128, ROW, ga[ROW][0], ga[ROW][1], None, None, None, None)
+    mx.mx_quantize(wgt, 1, gN, gK // 128, 128, ROW, gb[ROW][0], gb[ROW][1], None, None, None, None)
+    del hid, wgt
+    gc = {l: (torch.empty((gM, gN), dtype=torch.uint8, device=dev),
+              torch.empty(((gM, (gN + 31) // 32) if l == ROW else ((gM + 31) // 32, (gN + 31) // 32)),
+                          dtype=torch.uint8, device=dev)) for l in (ROW, SQ)}
+
+    def gemm_q():
+        mx.mx_gemm_quantize(ga[ROW][0], ga[ROW][1], gb[ROW][0], gb[ROW][1], gM, gN, gK, ROW | SQ, gc[ROW][0],
+                            gc[ROW][1], None, None, gc[SQ][0], gc[SQ][1], None)
+
+    gemm_q()
+    r0, r1 = ev(), ev()
+    r0.record(stream)
+    for _ in range(5):
+        gemm_q()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    g_ms = r0.elapsed_time(r1) / 5
+    g_tflops = 2.0 * gM * gN * gK / (g_ms * 1e-3) / 1e12
+
     pairs = B * H * S * (S + 1) / 2
     f_flop = 4.0 * D * pairs
     b_flop = 10.0 * D * pairs if do_bwd else 0.0
@@ -200,6 +227,8 @@ def main():
         "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "rmsnorm_quantize_ms": round(n_ms, 4),
         "rmsnorm_quantize_gbs": round(B * S * H * D * (2 + per_layout[ROW] + per_layout[SQ]) / (n_ms * 1e-3) / 1e9, 1),
+        "gemm_quantize": {"M": gM, "N": gN, "K": gK, "layouts": "row32+sq32", "ms": round(g_ms, 4),
+                          "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2)},
         "fwd_ms": round(f_ms, 4),
         "bwd_ms": round(b_ms, 4) if do_bwd else None,
         "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),

@@ -171,6 +171,34 @@ mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const floa
                                      hipStream_t stream);
 
 /*
+ * mx_gemm_quantize -- MX GEMM with a quantizing epilogue: C = A B^T.
+ * Defines: [News], contributions paragraph (fused GEMM + Quantize producers
+ * emitting FP8 with several scale layouts in one pass); the block-scaled
+ * GEMM itself as in [Blog], "1. End-to-End Block-Scaled GEMM Fusion".
+ *   a_data, a_scale  A [M, K] E4M3 payload, ROW32 scales [M, K/32]
+ *   b_data, b_scale  B [N, K] E4M3 payload, ROW32 scales [N, K/32]
+ *                    (B is the [out, in] weight; C[m, n] = sum_k A[m,k] B[n,k])
+ *   C is accumulated in fp32 by the block-scaled matrix instruction, then
+ *   quantized to MXFP8 in the requested layouts (0 allowed when c_f32 is
+ *   given), blocks aligned at row and column 0, short tail blocks at the
+ *   edges, encoding as mx_quantize:
+ *     ROW32  payload [M, N], scales [M, ceil(N/32)]   (32 columns per block)
+ *     COL32  payload [M, N], scales [ceil(M/32), N]   (32 rows per block)
+ *     SQ32   payload [M, N], scales [ceil(M/32), ceil(N/32)]
+ *   c_f32  optional fp32 copy of C [M, N] (may be NULL)
+ * Requirements: K a positive multiple of 64 and at most 2^20, N a multiple of 16, every
+ * pointer 16-byte aligned.  MX_EINVAL otherwise; M = 0 or N = 0: MX_OK.
+ * Ownership: all buffers belong to the caller; nothing is allocated.
+ */
+mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale,
+                           const uint8_t* b_data, const uint8_t* b_scale,
+                           int M, int N, int K, unsigned layouts,
+                           uint8_t* c_row32_data, uint8_t* c_row32_scale,
+                           uint8_t* c_col32_data, uint8_t* c_col32_scale,
+                           uint8_t* c_sq32_data, uint8_t* c_sq32_scale,
+                           float* c_f32, hipStream_t stream);
+
+/*
  * mx_attn_fwd -- fused MXFP8 attention forward.
  * Defines: [Blog], "1. End-to-End Block-Scaled GEMM Fusion" (S = Q K^T and
  * P V both on block-scaled operands, nothing written to HBM in between) and

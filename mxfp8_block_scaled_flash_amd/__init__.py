@@ -35,6 +35,7 @@ _SIGS = {
                             + [_vp] * 6 + [_vp], _c_int),
     "mx_rmsnorm_quantize_varlen": ([_vp, _c_int, _vp, _c_float, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
+    "mx_gemm_quantize": ([_vp] * 4 + [_c_int] * 3 + [ctypes.c_uint] + [_vp] * 7 + [_vp], _c_int),
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
@@ -142,6 +143,14 @@ def mx_rmsnorm_quantize_varlen(x, gamma, eps, cu_seqlens, cu_scale_rows, nseq, t
                                             _stream(stream)), "mx_rmsnorm_quantize_varlen")
 
 
+def mx_gemm_quantize(a_data, a_scale, b_data, b_scale, M, N, K, layouts, c_row32_data, c_row32_scale,
+                     c_col32_data, c_col32_scale, c_sq32_data, c_sq32_scale, c_f32, stream=None):
+    _check(lib().mx_gemm_quantize(_ptr(a_data), _ptr(a_scale), _ptr(b_data), _ptr(b_scale), M, N, K, layouts,
+                                  _ptr(c_row32_data), _ptr(c_row32_scale), _ptr(c_col32_data), _ptr(c_col32_scale),
+                                  _ptr(c_sq32_data), _ptr(c_sq32_scale), _ptr(c_f32), _stream(stream)),
+           "mx_gemm_quantize")
+
+
 def mx_attn_fwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal, o, lse,
                 stream=None):
     _check(lib().mx_attn_fwd(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
@@ -224,6 +233,23 @@ def rmsnorm_quantize(x, gamma, eps=1e-6, layouts=ROW32 | COL32 | SQ32):
     mx_rmsnorm_quantize(x, gamma, eps, B, S, H, D, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0), g(COL32, 1),
                         g(SQ32, 0), g(SQ32, 1))
     return out
+
+
+def gemm_quantize(a, b, layouts=ROW32 | COL32 | SQ32, with_f32=False):
+    """C = A B^T from MX operands a = (data [M, K], scale [M, K/32]) and b = (data [N, K],
+    scale [N, K/32]); returns ({layout: (data [M, N], scale)}, C fp32 or None)."""
+    M, K = a[0].shape
+    N = b[0].shape[0]
+    dev = a[0].device
+    shapes = {ROW32: (M, (N + 31) // 32), COL32: ((M + 31) // 32, N), SQ32: ((M + 31) // 32, (N + 31) // 32)}
+    out = {lay: (torch.empty((M, N), dtype=torch.uint8, device=dev), torch.empty(shapes[lay], dtype=torch.uint8,
+                                                                                   device=dev))
+           for lay in (ROW32, COL32, SQ32) if layouts & lay}
+    c32 = torch.empty((M, N), dtype=torch.float32, device=dev) if with_f32 else None
+    g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
+    mx_gemm_quantize(a[0], a[1], b[0], b[1], M, N, K, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0), g(COL32, 1),
+                     g(SQ32, 0), g(SQ32, 1), c32)
+    return out, c32
 
 
 def padded_scale_rows(seqlens) -> int:

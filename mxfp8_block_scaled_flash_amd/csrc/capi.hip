@@ -188,6 +188,34 @@ mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const floa
                          stream);
 }
 
+mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const uint8_t* b_data,
+                           const uint8_t* b_scale, int M, int N, int K, unsigned layouts, uint8_t* c_row32_data,
+                           uint8_t* c_row32_scale, uint8_t* c_col32_data, uint8_t* c_col32_scale,
+                           uint8_t* c_sq32_data, uint8_t* c_sq32_scale, float* c_f32, hipStream_t stream) {
+  // K bounded so that a 128-row tile of an operand stays within 32-bit buffer offsets
+  if (M < 0 || N < 0 || K < 64 || K > (1 << 20) || K % 64 != 0 || N % 16 != 0) return MX_EINVAL;
+  if ((layouts & ~7u) != 0 || (layouts == 0 && !c_f32)) return MX_EINVAL;
+  if ((long)M * K > kMaxElems || (long)N * K > kMaxElems || (long)M * N > kMaxElems) return MX_EINVAL;
+  if ((long)M * N == 0) return MX_OK;
+  if (!all_aligned({a_data, a_scale, b_data, b_scale})) return MX_EINVAL;
+  if (layouts && !layout_ptrs_ok(layouts, c_row32_data, c_row32_scale, c_col32_data, c_col32_scale, c_sq32_data,
+                                 c_sq32_scale))
+    return MX_EINVAL;
+  if (c_f32 && !aligned16(c_f32)) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  mxk::GemmArgs a{};
+  a.a = a_data; a.as = a_scale; a.b = b_data; a.bs = b_scale;
+  a.M = M; a.N = N; a.K = K;
+  a.tm = (M + 127) / 128;
+  a.tn = (N + 127) / 128;
+  a.layouts = layouts;
+  a.row_data = c_row32_data; a.row_scale = c_row32_scale;
+  a.col_data = c_col32_data; a.col_scale = c_col32_scale;
+  a.sq_data = c_sq32_data; a.sq_scale = c_sq32_scale;
+  a.c32 = c_f32;
+  return from_hip(mxk::launch_gemm_quantize(a, stream));
+}
+
 static mx_status fwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale, int H, int D,
                             float softmax_scale, void* o, mx_dtype o_dtype, mxk::FwdArgs& a) {

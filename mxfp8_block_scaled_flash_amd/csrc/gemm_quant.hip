@@ -1,0 +1,265 @@
+// MX GEMM with a quantizing epilogue: C = A B^T from E4M3 payloads with ROW32
+// (E8M0 per 32 along K) scales, fp32 accumulation in the block-scaled matrix
+// instruction, and C written as MXFP8 in any of ROW32 / COL32 / SQ32 (one
+// pass over the fp32 tile, several scale layouts), optionally also in fp32.
+//
+// This is the "fused GEMM + Quantize" producer of "Low Precision Flash
+// Attention 4: End-to-End Block-Scaled Attention for Blackwell",
+// contributions paragraph (FP8 output with dual scale layouts in one pass,
+// e.g. for the projections that feed the attention operands).
+//
+// gfx950 design:
+//  * workgroup = 4 waves = one 128 x 128 tile of C; wave w holds the 64 x 64
+//    sub-tile (rows 64 (w/2), columns 64 (w%2)) as 2 x 2 accumulators of
+//    v_mfma_scale_f32_32x32x64_f8f6f4;
+//  * K advances 64 per step; A and B tiles (128 rows x 64 bytes) and their
+//    scale pairs are staged in two LDS buffers, the next step's buffer loads
+//    in flight while the current one is multiplied, one barrier per step;
+//  * the operands are swapped (B rows as the instruction's A operand), so a
+//    lane ends with one row of C and 16 of its columns per 32 x 32 block:
+//    ROW32 maxima are in-lane plus one v_permlane32_swap, COL32 maxima are
+//    DPP / permlane reductions across the 32 rows of a lane half, SQ32 from
+//    those; codes are regrouped with v_permlane32_swap so each lane stores 16
+//    consecutive bytes of its row;
+//  * encoding as in the quantizer: exact power-of-two ldexp, clamp to +-448,
+//    round-to-nearest-even fp8 convert.
+#include "mx_common.h"
+#include "mx_launch.h"
+
+namespace mxk {
+
+namespace {
+
+MX_DEV v8i pack8g(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// max over the 32 lanes of each lane half (non-negative values; integer order = value order)
+MX_DEV float half_max_nonneg(float f) {
+  int v = __float_as_int(f);
+  v = max(v, dpp_i32<0xB1>(v));
+  v = max(v, dpp_i32<0x4E>(v));
+  v = max(v, dpp_i32<0x141>(v));
+  v = max(v, dpp_i32<0x140>(v));
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  return __int_as_float(max((int)a[0], (int)a[1]));
+}
+
+// four values times 2^sh each, clamped to +-448, packed as E4M3 codes (little-endian)
+MX_DEV uint32_t enc4(float y0, float y1, float y2, float y3, int sh0, int sh1, int sh2, int sh3) {
+  const float a0 = __builtin_amdgcn_fmed3f(ldexpf(y0, sh0), -448.f, 448.f);
+  const float a1 = __builtin_amdgcn_fmed3f(ldexpf(y1, sh1), -448.f, 448.f);
+  const float a2 = __builtin_amdgcn_fmed3f(ldexpf(y2, sh2), -448.f, 448.f);
+  const float a3 = __builtin_amdgcn_fmed3f(ldexpf(y3, sh3), -448.f, 448.f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
+  return (uint32_t)r;
+}
+
+template <int OA, int OB>
+MX_DEV v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
+  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int KST = BK + 16;   // LDS row stride of the staged tiles
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * KST];
+  __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // tiles in row-major order, split into 8 contiguous runs, one per XCD (blockIdx % 8), so
+  // neighbouring tiles that share rows of A run on the same XCD
+  const int ntiles = a.tm * a.tn;
+  const int per = (ntiles + 7) / 8;
+  const int tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3));
+  if (tile >= ntiles) return;
+  const int m0 = (tile / a.tn) * BM, n0 = (tile % a.tn) * BN;
+  const int K = a.K, kb32 = K / 32;
+
+  // ---- staging: 128 rows x 64 bytes of A and of B per step, 2 chunks of 16 bytes per thread each
+  struct Stage {
+    uint4 av[2], bv[2];
+    uint32_t as, bs;
+  };
+  const int rowsA = min(BM, a.M - m0), rowsB = min(BN, a.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.a + (long)m0 * K, (rowsA - 1) * K + K);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.b + (long)n0 * K, (rowsB - 1) * K + K);
+  const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(a.as + (long)m0 * kb32, rowsA * kb32);
+  const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(a.bs + (long)n0 * kb32, rowsB * kb32);
+  auto load = [&](int kt, Stage& st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = tid + 256 * c;   // 512 chunks: row ch / 4, 16-byte column ch % 4
+      const int off = (ch >> 2) * K + kt * BK + (ch & 3) * 16;
+      st.av[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+      st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    }
+    // thread t: scale pair of A row t (t < 128) or of B row t - 128
+    const int r = tid & 127;
+    const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(tid < 128 ? ras : rbs, r * kb32 + 2 * kt, 0, 0);
+    st.as = s;
+    st.bs = s;
+  };
+  auto store = [&](int buf, const Stage& st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = tid + 256 * c;
+      *(uint4*)(&sA[buf][(ch >> 2) * KST + (ch & 3) * 16]) = st.av[c];
+      *(uint4*)(&sB[buf][(ch >> 2) * KST + (ch & 3) * 16]) = st.bv[c];
+    }
+    if (tid < 128) sAs[buf][tid] = st.as;
+    else sBs[buf][tid - 128] = st.bs;
+  };
+
+  // acc[i][j]: C block (rows m0 + 64 (w/2) + 32 i, columns n0 + 64 (w%2) + 32 j); element e of
+  // lane (n, g) = row + n, column + 8(e/4) + 4g + e%4
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  const int wr = 64 * (w >> 1), wc = 64 * (w & 1);
+  const int nk = K / BK;
+  int sa_prev[2] = {0, 0}, sb_prev[2] = {0, 0};   // scale operands of the last products, pinned
+
+  {
+    Stage s0;
+    load(0, s0);
+    store(0, s0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    Stage nx;
+    load(min(kt + 1, nk - 1), nx);   // past the last step the last one is fetched again
+    v8i ao[2], bo[2];
+    int sa[2], sb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint8_t* pa = sA[cur] + (wr + 32 * i + n) * KST + 16 * g;
+      ao[i] = pack8g(*(const uint4*)pa, *(const uint4*)(pa + 32));
+      sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
+      const uint8_t* pb = sB[cur] + (wc + 32 * i + n) * KST + 16 * g;
+      bo[i] = pack8g(*(const uint4*)pb, *(const uint4*)(pb + 32));
+      sb[i] = (int)(sBs[cur][wc + 32 * i + n] >> (8 * g));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<0, 0>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
+    keep(sa_prev[0]); keep(sa_prev[1]); keep(sb_prev[0]); keep(sb_prev[1]);
+    sa_prev[0] = sa[0]; sa_prev[1] = sa[1]; sb_prev[0] = sb[0]; sb_prev[1] = sb[1];
+    store(cur ^ 1, nx);
+    __syncthreads();
+  }
+  keep(acc[1][1][0]);
+  keep(sa_prev[0]); keep(sa_prev[1]); keep(sb_prev[0]); keep(sb_prev[1]);
+
+  // ---- epilogue, per 32 x 32 block
+  const long ldc = a.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const v16f& c = acc[i][j];
+      const int row = m0 + wr + 32 * i + n;      // this lane's row
+      const int col0 = n0 + wc + 32 * j;         // first column of the block
+      const bool row_ok = row < a.M;
+      // fp32 copy: dword group q holds columns col0 + 8q + 4g + 0..3
+      if (a.c32 && row_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cc = col0 + 8 * q + 4 * g;
+          float* dst = a.c32 + (long)row * ldc + cc;
+          if (cc + 3 < a.N) {
+            *(float4*)dst = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (cc + e < a.N) dst[e] = c[4 * q + e];
+          }
+        }
+      }
+      // maxima: per row (ROW32), per column (COL32), per block (SQ32)
+      float rm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rm = fmaxf(rm, fabsf(c[e]));
+      rm = half_swap_max(rm);                    // the row's 32 columns
+      float cm[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cm[e] = half_max_nonneg(fabsf(c[e]));   // the column's 32 rows
+      float bmx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bmx = fmaxf(bmx, cm[e]);
+      bmx = half_swap_max(bmx);
+      // encode one layout: per-element shifts, then regroup so lane half g holds columns 16g + 0..15
+      auto emit = [&](uint8_t* data, const int* sh) {
+        uint32_t dw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dw[q] = enc4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3], sh[4 * q], sh[4 * q + 1], sh[4 * q + 2],
+                       sh[4 * q + 3]);
+        auto s02 = __builtin_amdgcn_permlane32_swap(dw[0], dw[2], false, false);
+        auto s13 = __builtin_amdgcn_permlane32_swap(dw[1], dw[3], false, false);
+        const int cs = col0 + 16 * g;
+        if (row_ok) {
+          uint8_t* dst = data + (long)row * ldc + cs;
+          const uint32_t v[4] = {s02[0], s02[1], s13[0], s13[1]};
+          if (cs + 15 < a.N) {
+            *(uint4*)dst = make_uint4(v[0], v[1], v[2], v[3]);
+          } else {
+            for (int b = 0; b < 16 && cs + b < a.N; ++b) dst[b] = (uint8_t)(v[b >> 2] >> (8 * (b & 3)));
+          }
+        }
+      };
+      const int nbn = (a.N + 31) / 32;
+      if (a.layouts & 1) {   // ROW32: one scale per row and 32 columns
+        const int k = scale_code(rm);
+        int sh[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sh[e] = 127 - k;
+        emit(a.row_data, sh);
+        if (g == 0 && row_ok && col0 < a.N) a.row_scale[(long)row * nbn + col0 / 32] = (uint8_t)k;
+      }
+      if (a.layouts & 2) {   // COL32: one scale per column and 32 rows
+        int sh[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sh[e] = 127 - scale_code(cm[e]);
+        emit(a.col_data, sh);
+        if (n == 0 && m0 + wr + 32 * i < a.M) {   // blocks wholly past the last row have no scales
+          const int rb = (m0 + wr + 32 * i) / 32;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int cc = col0 + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (cc < a.N) a.col_scale[(long)rb * ldc + cc] = (uint8_t)(127 - sh[e]);
+          }
+        }
+      }
+      if (a.layouts & 4) {   // SQ32: one scale per 32 x 32 block
+        const int k = scale_code(bmx);
+        int sh[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sh[e] = 127 - k;
+        emit(a.sq_data, sh);
+        if (lane == 0 && m0 + wr + 32 * i < a.M && col0 < a.N)
+          a.sq_scale[(long)((m0 + wr + 32 * i) / 32) * nbn + col0 / 32] = (uint8_t)k;
+      }
+    }
+}
+
+hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st) {
+  const long ntiles = (long)a.tm * a.tn;
+  if (ntiles == 0) return hipSuccess;
+  const long grid = (ntiles + 7) / 8 * 8;
+  gemm_quant_kernel<<<dim3((unsigned)grid), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

@@ -30,6 +30,15 @@ struct FwdArgs {
   float* lse;
 };
 
+struct GemmArgs {
+  const uint8_t *a, *as, *b, *bs;   // A [M, K], B [N, K] E4M3 payloads; ROW32 scales [M, K/32], [N, K/32]
+  int M, N, K;
+  int tm, tn;                       // tiles along M and N
+  unsigned layouts;                 // output layouts of C = A B^T
+  uint8_t *row_data, *row_scale, *col_data, *col_scale, *sq_data, *sq_scale;
+  float* c32;                       // optional fp32 copy of C [M, N]
+};
+
 struct BwdArgs {
   const uint8_t *q, *qs, *k, *ks, *v, *vs, *dob, *dos;   // SQ32 Q, K, dO; ROW32 V
   const void* o;        // forward output [tokens, H, D]
@@ -54,5 +63,6 @@ hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const 
 hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipStream_t st);
 hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);
+hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mxk

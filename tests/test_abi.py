@@ -102,6 +102,25 @@ def test_rmsnorm_quantize_rejects_invalid_shapes():
                                  None) == EINVAL
 
 
+def _gemm(**kw):
+    a = dict(a=16, as_=16, b=16, bs=16, M=64, N=64, K=64, lay=mx.ROW32, rd=16, rs=16, cd=None, cs=None, sd=None,
+             ss=None, c32=None)
+    a.update(kw)
+    return mx.lib().mx_gemm_quantize(a["a"], a["as_"], a["b"], a["bs"], a["M"], a["N"], a["K"], a["lay"], a["rd"],
+                                     a["rs"], a["cd"], a["cs"], a["sd"], a["ss"], a["c32"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(K=32), dict(K=0), dict(K=96), dict(N=40), dict(M=-1), dict(N=-16),
+                                 dict(lay=8), dict(lay=0), dict(a=None), dict(bs=24), dict(rd=None),
+                                 dict(lay=mx.COL32), dict(c32=20), dict(K=(1 << 20) + 64)])
+def test_gemm_quantize_rejects_invalid_arguments(bad):
+    assert _gemm(**bad) == EINVAL
+
+
+def test_empty_gemm_quantize_is_a_no_op():
+    assert _gemm(M=0) == 0 and _gemm(N=0) == 0 and _gemm(M=0, lay=0, rd=None, rs=None, c32=16) == 0
+
+
 def test_workspace_size():
     n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
     assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
