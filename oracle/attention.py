@@ -50,6 +50,15 @@ def fl32(x):
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
+def bf16(x):
+    """Round to bfloat16, nearest with ties to even, from the fp32 value (x is fp32-exact
+    and finite): keep the top 16 bits of the fp32 pattern after adding 0x7FFF plus the
+    lowest kept bit."""
+    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def log2_scale(sigma: float) -> float:
     """c = fl32(fl32(sigma) * fl32(log2 e))."""
     return float(fl32(float(np.float32(sigma)) * LOG2E32))
@@ -62,7 +71,7 @@ def visible(Lq: int, Lk: int, causal: bool) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- forward
-def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None, gemm="mfma"):
+def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None, gemm="mfma", p_round=None):
     """One (batch, head): q, k, v are [L, D] source values (fp32 or bf16 upcast).
 
     Returns a dict with O [L, D] (float64, before the output cast), LSE [L]
@@ -71,6 +80,8 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None
     rounding (used only to pin the oracle to textbook attention).
     ``q_rows`` (optional index array) computes only those query rows; every
     step is row-wise, so each returned row equals the full computation's.
+    ``p_round="bf16"`` (with ``quantize=False``): the BF16 attention baseline, in
+    which P enters P V rounded to bfloat16 and l still sums the fp32 p.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -103,7 +114,7 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None
         pc, pk = mx.quantize_col32(p, axis=1)           # 32 keys per block, per query
         ph = mx.dequantize_col32(pc, pk, axis=1)
     else:
-        pc, pk, ph = None, None, p
+        pc, pk, ph = None, None, (bf16(p) if p_round == "bf16" else p)
     O = (ph @ vh) / l[:, None]
     LSE = math.log(2.0) * (M + np.log2(l))
     return {"O": O, "LSE": LSE, "M": M, "l": l, "P_codes": pc, "P_scales": pk, "S": S}
@@ -190,10 +201,12 @@ def _heads(x, cu_seqlens):
                 yield (s, h), x[cu_seqlens[s]:cu_seqlens[s + 1], h, :]
 
 
-def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None):
+def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=False):
     """Forward over [B, S, H, D] (or packed [T, H, D] with cu_seqlens).
 
     Returns O (float64, q's shape) and LSE ([B, H, S] or [H, T], float64).
+    ``bf16_baseline``: no MX step, P rounded to bfloat16 before P V (the BF16
+    attention the pages compare against, [News] headline figures).
     """
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     O = np.zeros_like(q)
@@ -205,7 +218,8 @@ def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None):
     for key, qh in _heads(q, cu_seqlens):
         if qh.shape[0] == 0:
             continue
-        res = forward_head(qh, ks[key], vs[key], sigma, causal)
+        res = (forward_head(qh, ks[key], vs[key], sigma, causal, quantize=False, p_round="bf16")
+               if bf16_baseline else forward_head(qh, ks[key], vs[key], sigma, causal))
         a, h = key
         if cu_seqlens is None:
             O[a, :, h, :] = res["O"]
