@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MXFP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 / MXFP8 MFMA peak
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak
 HBM_PEAK_GBS = 8000.0
 
 
@@ -188,6 +189,21 @@ def main():
     g_ms = r0.elapsed_time(r1) / 5
     g_tflops = 2.0 * gM * gN * gK / (g_ms * 1e-3) / 1e12
 
+    # BF16 attention forward on the same inputs (the baseline of the MX speed-up), timed alone
+    o16 = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+
+    def fwd_bf16():
+        mx.mx_attn_fwd_bf16(x["q"], x["k"], x["v"], B, S, H, D, sigma, True, o16, lse)
+
+    fwd_bf16()
+    r0, r1 = ev(), ev()
+    r0.record(stream)
+    for _ in range(3):
+        fwd_bf16()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    f16_ms = r0.elapsed_time(r1) / 3
+
     pairs = B * H * S * (S + 1) / 2
     f_flop = 4.0 * D * pairs
     b_flop = 10.0 * D * pairs if do_bwd else 0.0
@@ -229,6 +245,9 @@ def main():
         "rmsnorm_quantize_gbs": round(B * S * H * D * (2 + per_layout[ROW] + per_layout[SQ]) / (n_ms * 1e-3) / 1e9, 1),
         "gemm_quantize": {"M": gM, "N": gN, "K": gK, "layouts": "row32+sq32", "ms": round(g_ms, 4),
                           "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2)},
+        "bf16_fwd": {"ms": round(f16_ms, 4), "tflops": round(f_flop / (f16_ms * 1e-3) / 1e12, 2),
+                     "pct_bf16_peak": round(100 * f_flop / (f16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                     "mx_speedup": round(f16_ms / f_ms, 3)},
         "fwd_ms": round(f_ms, 4),
         "bwd_ms": round(b_ms, 4) if do_bwd else None,
         "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),

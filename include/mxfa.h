@@ -3,7 +3,8 @@
  *
  * A C ABI over hand-written HIP kernels: MX quantization, the fused MXFP8
  * attention forward, and the fused MXFP8 attention backward, each with a
- * fixed-length and a jagged (varlen) form.
+ * fixed-length and a jagged (varlen) form; the fused producers (RMSNorm +
+ * quantize, GEMM + quantize) and the BF16 attention baseline.
  *
  * Pages cited (by title):
  *   [News]  "Low Precision Flash Attention 4: End-to-End Block-Scaled
@@ -236,6 +237,34 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              int total_tokens, int max_seqlen, int H, int D,
                              float softmax_scale, int causal,
                              void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * mx_attn_fwd_bf16 -- BF16 attention forward, the baseline of the pages'
+ * speed-up figures ([News], headline comparison with BF16 FlashAttention-4).
+ * Reading (the pages do not define it): mx_attn_fwd with every MX step
+ * removed; Q, K, V bfloat16; S = Q K^T accumulated in fp32; the same integer
+ * frame, p and l as mx_attn_fwd; P rounded to bfloat16 (nearest even) for
+ * O = (P V) / l; LSE as mx_attn_fwd.
+ *   q, k, v  [B, S, H, D] bfloat16 (device, 16-byte aligned)
+ *   D 64 or 128; causal keeps keys j <= i
+ *   o        [B, S, H, D], o_dtype MX_BF16 or MX_F32
+ *   lse      [B, H, S] fp32, natural log; may be NULL
+ * Errors: MX_EINVAL for a bad shape, dtype, scale or alignment; B = 0 or
+ * S = 0: MX_OK.  Ownership: all buffers belong to the caller.
+ */
+mx_status mx_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           int B, int S, int H, int D, float softmax_scale, int causal,
+                           void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
+ * mx_attn_fwd_bf16_varlen -- mx_attn_fwd_bf16 over packed sequences
+ * ([T, H, D] tensors, cu_seqlens [nseq+1] device int32).  lse is [H, T].
+ * max_seqlen bounds every sequence length (host int).
+ */
+mx_status mx_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_seqlens, int nseq, int total_tokens,
+                                  int max_seqlen, int H, int D, float softmax_scale, int causal,
+                                  void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
 
 /*
  * mx_attn_bwd_workspace_bytes -- device scratch mx_attn_bwd needs:

@@ -39,6 +39,8 @@ _SIGS = {
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
+    "mx_attn_fwd_bf16": ([_vp] * 3 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
+    "mx_attn_fwd_bf16_varlen": ([_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
     "mx_attn_bwd": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
                     + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
@@ -166,6 +168,18 @@ def mx_attn_fwd_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seq
                                     _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_varlen")
 
 
+def mx_attn_fwd_bf16(q, k, v, B, S, H, D, softmax_scale, causal, o, lse, stream=None):
+    _check(lib().mx_attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), B, S, H, D, float(softmax_scale), int(bool(causal)),
+                                  _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_bf16")
+
+
+def mx_attn_fwd_bf16_varlen(q, k, v, cu_seqlens, nseq, total_tokens, max_seqlen, H, D, softmax_scale, causal, o,
+                            lse, stream=None):
+    _check(lib().mx_attn_fwd_bf16_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, total_tokens,
+                                         max_seqlen, H, D, float(softmax_scale), int(bool(causal)), _ptr(o),
+                                         _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_bf16_varlen")
+
+
 def mx_attn_bwd_workspace_bytes(tokens, H, D) -> int:
     return lib().mx_attn_bwd_workspace_bytes(tokens, H, D)
 
@@ -291,6 +305,24 @@ def attn_fwd(q, k, v, softmax_scale, causal, out_dtype=torch.bfloat16, with_lse=
     o = torch.empty((B, S, H, D), dtype=out_dtype, device=q[0].device)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q[0].device) if with_lse else None
     mx_attn_fwd(q[0], q[1], k[0], k[1], v[0], v[1], B, S, H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_fwd_bf16(q, k, v, softmax_scale, causal, out_dtype=torch.bfloat16, with_lse=True):
+    """BF16 attention forward: q, k, v bfloat16 [B, S, H, D].  Returns (O, LSE)."""
+    B, S, H, D = q.shape
+    o = torch.empty((B, S, H, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if with_lse else None
+    mx_attn_fwd_bf16(q, k, v, B, S, H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, seqlens, softmax_scale, causal, out_dtype=torch.bfloat16,
+                         with_lse=True):
+    T, H, D = q.shape
+    o = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if with_lse else None
+    mx_attn_fwd_bf16_varlen(q, k, v, cu_seqlens, len(seqlens), T, max(seqlens), H, D, softmax_scale, causal, o, lse)
     return o, lse
 
 

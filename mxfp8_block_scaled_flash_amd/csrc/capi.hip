@@ -274,6 +274,54 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, cons
   return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, a, max_seqlen, stream));
 }
 
+static mx_status fwd_bf16_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int D,
+                                 float softmax_scale, void* o, mx_dtype o_dtype, float* lse, mxk::FwdArgs& a) {
+  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (o_dtype != MX_BF16 && o_dtype != MX_F32) return MX_EINVAL;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
+  if (!all_aligned({q, k, v, o})) return MX_EINVAL;
+  if (lse && !aligned16(lse)) return MX_EINVAL;
+  a.q = (const uint8_t*)q; a.k = (const uint8_t*)k; a.v = (const uint8_t*)v;
+  a.H = H;
+  a.c = log2_scale(softmax_scale);
+  a.o = o;
+  a.lse = lse;
+  return MX_OK;
+}
+
+mx_status mx_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int S, int H, int D,
+                           float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse,
+                           hipStream_t stream) {
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  mxk::FwdArgs a{};
+  if (mx_status st = fwd_bf16_common(q, k, v, H, D, softmax_scale, o, o_dtype, lse, a)) return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.nseq = B;
+  a.T = B * S;
+  return from_hip(mxk::launch_attn_fwd_bf16(D, causal != 0, o_dtype == MX_BF16, a, S, stream));
+}
+
+mx_status mx_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen, int H,
+                                  int D, float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse,
+                                  hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens) return MX_EINVAL;
+  if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
+  mxk::FwdArgs a{};
+  if (mx_status st = fwd_bf16_common(q, k, v, H, D, softmax_scale, o, o_dtype, lse, a)) return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_seqlens;   // no scale rows in this path; the map only needs a readable array
+  a.nseq = nseq;
+  a.T = total_tokens;
+  return from_hip(mxk::launch_attn_fwd_bf16(D, causal != 0, o_dtype == MX_BF16, a, max_seqlen, stream));
+}
+
 size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D) {
   if (tokens < 0 || H < 1 || D < 1) return 0;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };

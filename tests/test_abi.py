@@ -121,6 +121,27 @@ def test_empty_gemm_quantize_is_a_no_op():
     assert _gemm(M=0) == 0 and _gemm(N=0) == 0 and _gemm(M=0, lay=0, rd=None, rs=None, c32=16) == 0
 
 
+def _fwd16(**kw):
+    a = dict(q=16, k=16, v=16, B=1, S=64, H=1, D=128, sc=0.1, causal=1, o=16, odt=mx.BF16, lse=None)
+    a.update(kw)
+    return mx.lib().mx_attn_fwd_bf16(a["q"], a["k"], a["v"], a["B"], a["S"], a["H"], a["D"], a["sc"], a["causal"],
+                                     a["o"], a["odt"], a["lse"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(D=96), dict(H=0), dict(B=-1), dict(sc=0.0), dict(sc=float("inf")),
+                                 dict(odt=mx.F16), dict(q=None), dict(v=24), dict(o=8), dict(lse=20)])
+def test_bf16_forward_rejects_invalid_arguments(bad):
+    assert _fwd16(**bad) == EINVAL
+
+
+def test_bf16_forward_empty_and_varlen_validation():
+    assert _fwd16(B=0) == 0 and _fwd16(S=0) == 0
+    L = mx.lib()
+    assert L.mx_attn_fwd_bf16_varlen(16, 16, 16, None, 1, 10, 10, 1, 128, 0.1, 1, 16, mx.BF16, None, None) == EINVAL
+    assert L.mx_attn_fwd_bf16_varlen(16, 16, 16, 16, 0, 10, 10, 1, 128, 0.1, 1, 16, mx.BF16, None, None) == EINVAL
+    assert L.mx_attn_fwd_bf16_varlen(16, 16, 16, 16, 1, 0, 10, 1, 128, 0.1, 1, 16, mx.BF16, None, None) == 0
+
+
 def test_workspace_size():
     n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
     assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
