@@ -121,9 +121,11 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None
 
 
 # ---------------------------------------------------------------- backward
-def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False, gemm="mfma"):
+def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False, gemm="mfma", p_round=None):
     """One (batch, head) backward.  o, do: [L, D] (the forward output as the
     caller holds it, and the incoming gradient); lse: [L] (fp32 values).
+    ``p_round="bf16"`` (with ``quantize=False``): the BF16 baseline, in which P
+    (for dV) and dS (for dK and dQ) enter their products rounded to bfloat16.
 
     Returns float64 dQ, dK, dV [L, D] and the internals (p, dS, D).
     """
@@ -153,6 +155,8 @@ def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False
     if quantize:
         dSh = mx.dequantize_sq32(*mx.quantize_sq32(dS, 0), 0)   # [32 q x 32 k] blocks
         pb = mx.dequantize_col32(*mx.quantize_col32(p, axis=0), axis=0)  # 32 queries per key
+    elif p_round == "bf16":
+        dSh, pb = bf16(dS), bf16(p)
     else:
         dSh, pb = dS, p
     dV = pb.T @ dos
@@ -230,8 +234,9 @@ def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=
     return O, LSE
 
 
-def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None):
-    """Backward over whole tensors; lse is [B, H, S] (or [H, T]).  Returns float64 dQ, dK, dV."""
+def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None, bf16_baseline=False):
+    """Backward over whole tensors; lse is [B, H, S] (or [H, T]).  Returns float64 dQ, dK, dV.
+    ``bf16_baseline``: no MX step, P and dS rounded to bfloat16 before their products."""
     q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
     lse = np.asarray(lse, np.float64)
     dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -246,6 +251,8 @@ def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None):
         else:
             lh = lse[h, cu_seqlens[a]:cu_seqlens[a + 1]]
             sl = (slice(cu_seqlens[a], cu_seqlens[a + 1]), h, slice(None))
-        res = backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal)
+        res = (backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal, quantize=False,
+                             p_round="bf16") if bf16_baseline
+               else backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal))
         dQ[sl], dK[sl], dV[sl] = res["dQ"], res["dK"], res["dV"]
     return dQ, dK, dV

@@ -62,3 +62,38 @@ def test_bf16_p_error_bound(causal):
     diff = np.abs(b["O"] - a["O"])
     assert np.all(diff <= bound)
     assert np.max(diff) > 0 and np.array_equal(a["LSE"], b["LSE"])
+
+
+def test_backward_bf16_rounding_is_exact_on_representable_p_and_ds():
+    # c = 1, lse = 0, o = 0 (so D = 0) and integer q, k, v, dO: p = 2^S and dS = p dP are bf16-exact
+    sigma = float(np.float32(math.log(2)))
+    rng = np.random.default_rng(3)
+    L, D = 64, 32
+    q = rng.integers(-1, 2, (L, D)).astype(np.float64)
+    k = rng.integers(-1, 2, (L, D)).astype(np.float64)
+    v = rng.integers(-2, 3, (L, D)).astype(np.float64)
+    do = rng.integers(-2, 3, (L, D)).astype(np.float64)
+    o, lse = np.zeros((L, D)), np.zeros(L)
+    for causal in (False, True):
+        a = at.backward_head(q, k, v, o, do, lse, sigma, causal, quantize=False)
+        b = at.backward_head(q, k, v, o, do, lse, sigma, causal, quantize=False, p_round="bf16")
+        assert np.max(np.abs(a["dS"])) > 1                      # not a trivial case
+        for g in ("dQ", "dK", "dV"):
+            assert np.array_equal(a[g], b[g]), g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bf16_error_bounds(causal):
+    rng = np.random.default_rng(4)
+    L, D, sigma = 96, 64, 1 / 8
+    q, k, v, do = (rng.standard_normal((L, D)).astype(np.float32).astype(np.float64) for _ in range(4))
+    f = at.forward_head(q, k, v, sigma, causal, quantize=False)
+    o, lse = f["O"].astype(np.float32).astype(np.float64), f["LSE"].astype(np.float32).astype(np.float64)
+    a = at.backward_head(q, k, v, o, do, lse, sigma, causal, quantize=False)
+    b = at.backward_head(q, k, v, o, do, lse, sigma, causal, quantize=False, p_round="bf16")
+    u = 2.0**-8 * (1 + 1e-6)
+    assert np.all(np.abs(b["dV"] - a["dV"]) <= u * (np.abs(a["p"]).T @ np.abs(do)))
+    assert np.all(np.abs(b["dK"] - a["dK"]) <= u * sigma * (np.abs(a["dS"]).T @ np.abs(q)))
+    assert np.all(np.abs(b["dQ"] - a["dQ"]) <= u * sigma * (np.abs(a["dS"]) @ np.abs(k)))
+    for g in ("dQ", "dK", "dV"):
+        assert np.max(np.abs(b[g] - a[g])) > 0, g
