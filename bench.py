@@ -204,6 +204,28 @@ def main():
     torch.cuda.synchronize()
     f16_ms = r0.elapsed_time(r1) / 3
 
+    b16_ms = None
+    if do_bwd:
+        # BF16 attention backward on the same bf16 inputs (O and LSE from the BF16 forward)
+        dq16, dk16, dv16 = (torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        ws16 = torch.empty(mx.mx_attn_bwd_bf16_workspace_bytes(B * S, H), dtype=torch.uint8, device=dev)
+        lse16 = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        mx.mx_attn_fwd_bf16(x["q"], x["k"], x["v"], B, S, H, D, sigma, True, o16, lse16)
+
+        def bwd_bf16():
+            mx.mx_attn_bwd_bf16(x["q"], x["k"], x["v"], o16, x["do"], lse16, B, S, H, D, sigma, True, dq16, dk16,
+                                dv16, ws16)
+
+        bwd_bf16()
+        r0, r1 = ev(), ev()
+        r0.record(stream)
+        for _ in range(2):
+            bwd_bf16()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        b16_ms = r0.elapsed_time(r1) / 2
+        del dq16, dk16, dv16, ws16
+
     pairs = B * H * S * (S + 1) / 2
     f_flop = 4.0 * D * pairs
     b_flop = 10.0 * D * pairs if do_bwd else 0.0
@@ -248,6 +270,9 @@ def main():
         "bf16_fwd": {"ms": round(f16_ms, 4), "tflops": round(f_flop / (f16_ms * 1e-3) / 1e12, 2),
                      "pct_bf16_peak": round(100 * f_flop / (f16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
                      "mx_speedup": round(f16_ms / f_ms, 3)},
+        "bf16_bwd": ({"ms": round(b16_ms, 4), "tflops": round(b_flop / (b16_ms * 1e-3) / 1e12, 2),
+                      "pct_bf16_peak": round(100 * b_flop / (b16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                      "mx_speedup": round(b16_ms / b_ms, 3)} if b16_ms else None),
         "fwd_ms": round(f_ms, 4),
         "bwd_ms": round(b_ms, 4) if do_bwd else None,
         "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),

@@ -275,6 +275,45 @@ mx_status mx_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const ui
 size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D);
 
 /*
+ * mx_attn_bwd_bf16_workspace_bytes -- device scratch mx_attn_bwd_bf16 needs:
+ * D_i as fp32 [B, H, S] (or [H, T]), tokens = B*S or T; 256-byte rounded.
+ */
+size_t mx_attn_bwd_bf16_workspace_bytes(int tokens, int H);
+
+/*
+ * mx_attn_bwd_bf16 -- BF16 attention backward, the baseline of the MXFP8
+ * backward ([News], headline comparison with BF16 FlashAttention-4).
+ * Reading (the pages do not define it): mx_attn_bwd with every MX step
+ * removed; p = 2^(S c - fl32(LSE log2 e)) with S = Q K^T in fp32,
+ * dP = dO V^T, D_i = sum_d dO_id O_id (fp32), dS = p (dP - D); P and dS
+ * rounded to bfloat16 (nearest even) for dV = P^T dO, dK = softmax_scale
+ * dS^T Q, dQ = softmax_scale dS K.  dQ is accumulated per query tile (no
+ * atomics, deterministic).
+ *   q, k, v, o, dout  [B, S, H, D] bfloat16 (o and lse from the forward)
+ *   lse               [B, H, S] fp32
+ *   dq, dk, dv        [B, S, H, D] in grad_dtype (MX_BF16 or MX_F32)
+ *   workspace         >= mx_attn_bwd_bf16_workspace_bytes(B*S, H) bytes
+ * Errors: MX_EINVAL (shape, dtype, scale, alignment), MX_EWORKSPACE (missing
+ * or short workspace); B = 0 or S = 0: MX_OK.  Ownership: caller's buffers.
+ */
+mx_status mx_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const uint16_t* dout, const float* lse,
+                           int B, int S, int H, int D, float softmax_scale, int causal,
+                           void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_attn_bwd_bf16_varlen -- mx_attn_bwd_bf16 over packed sequences
+ * ([T, H, D] tensors, lse [H, T], cu_seqlens [nseq+1] device int32).
+ */
+mx_status mx_attn_bwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const uint16_t* o, const uint16_t* dout, const float* lse,
+                                  const int32_t* cu_seqlens, int nseq, int total_tokens,
+                                  int max_seqlen, int H, int D, float softmax_scale, int causal,
+                                  void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mx_attn_bwd -- fused MXFP8 attention backward.
  * Defines: [News], forward/backward paragraph (Q, K, dO quantized in
  * square [32, 32] blocks so one payload feeds both GEMMs; P recomputed;

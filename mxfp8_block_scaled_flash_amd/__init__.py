@@ -42,6 +42,11 @@ _SIGS = {
     "mx_attn_fwd_bf16": ([_vp] * 3 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_bf16_varlen": ([_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
+    "mx_attn_bwd_bf16_workspace_bytes": ([_c_int, _c_int], _c_size),
+    "mx_attn_bwd_bf16": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int] + [_vp] * 3 + [_c_int, _vp, _c_size, _vp],
+                         _c_int),
+    "mx_attn_bwd_bf16_varlen": ([_vp] * 6 + [_vp] + [_c_int] * 5 + [_c_float, _c_int] + [_vp] * 3
+                                + [_c_int, _vp, _c_size, _vp], _c_int),
     "mx_attn_bwd": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
                     + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
     "mx_attn_bwd_varlen": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_vp, _vp] + [_c_int] * 5
@@ -178,6 +183,26 @@ def mx_attn_fwd_bf16_varlen(q, k, v, cu_seqlens, nseq, total_tokens, max_seqlen,
     _check(lib().mx_attn_fwd_bf16_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), nseq, total_tokens,
                                          max_seqlen, H, D, float(softmax_scale), int(bool(causal)), _ptr(o),
                                          _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_bf16_varlen")
+
+
+def mx_attn_bwd_bf16_workspace_bytes(tokens, H) -> int:
+    return lib().mx_attn_bwd_bf16_workspace_bytes(tokens, H)
+
+
+def mx_attn_bwd_bf16(q, k, v, o, dout, lse, B, S, H, D, softmax_scale, causal, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), B, S, H, D,
+                                  float(softmax_scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _dtype_code(dq.dtype), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mx_attn_bwd_bf16")
+
+
+def mx_attn_bwd_bf16_varlen(q, k, v, o, dout, lse, cu_seqlens, nseq, total_tokens, max_seqlen, H, D, softmax_scale,
+                            causal, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd_bf16_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
+                                         nseq, total_tokens, max_seqlen, H, D, float(softmax_scale),
+                                         int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq.dtype),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mx_attn_bwd_bf16_varlen")
 
 
 def mx_attn_bwd_workspace_bytes(tokens, H, D) -> int:
@@ -324,6 +349,26 @@ def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, seqlens, softmax_scale, causal, ou
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if with_lse else None
     mx_attn_fwd_bf16_varlen(q, k, v, cu_seqlens, len(seqlens), T, max(seqlens), H, D, softmax_scale, causal, o, lse)
     return o, lse
+
+
+def attn_bwd_bf16(q, k, v, o, dout, lse, softmax_scale, causal, grad_dtype=torch.bfloat16):
+    """BF16 attention backward: q, k, v, o, dout bfloat16 [B, S, H, D], lse [B, H, S].
+    Returns (dQ, dK, dV)."""
+    B, S, H, D = q.shape
+    dq, dk, dv = (torch.empty((B, S, H, D), dtype=grad_dtype, device=q.device) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_bf16_workspace_bytes(B * S, H), dtype=torch.uint8, device=q.device)
+    mx_attn_bwd_bf16(q, k, v, o, dout, lse, B, S, H, D, softmax_scale, causal, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def attn_bwd_bf16_varlen(q, k, v, o, dout, lse, cu_seqlens, seqlens, softmax_scale, causal,
+                         grad_dtype=torch.bfloat16):
+    T, H, D = q.shape
+    dq, dk, dv = (torch.empty((T, H, D), dtype=grad_dtype, device=q.device) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_bf16_workspace_bytes(T, H), dtype=torch.uint8, device=q.device)
+    mx_attn_bwd_bf16_varlen(q, k, v, o, dout, lse, cu_seqlens, len(seqlens), T, max(seqlens), H, D, softmax_scale,
+                            causal, dq, dk, dv, ws)
+    return dq, dk, dv
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal,

@@ -117,10 +117,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
             bf16_hi(x.y) * bf16_hi(y.y) + bf16_lo(x.z) * bf16_lo(y.z) + bf16_hi(x.z) * bf16_hi(y.z) +
             bf16_lo(x.w) * bf16_lo(y.w) + bf16_hi(x.w) * bf16_hi(y.w);
     }
-    // zero this row's fp16 dQ accumulator (D halves; the accumulator is head-major [H, T, D])
-    uint4 z = make_uint4(0, 0, 0, 0);
-    uint16_t* accp = (uint16_t*)a.acc + ((row % a.H) * (long)a.T + row / a.H) * D;
-    for (int i = c; i < D / 8; i += LPR) *(uint4*)(accp + i * 8) = z;
+    // zero this row's fp16 dQ accumulator (D halves; the accumulator is head-major [H, T, D]),
+    // when the caller's path has one
+    if (a.acc) {
+      uint4 z = make_uint4(0, 0, 0, 0);
+      uint16_t* accp = (uint16_t*)a.acc + ((row % a.H) * (long)a.T + row / a.H) * D;
+      for (int i = c; i < D / 8; i += LPR) *(uint4*)(accp + i * 8) = z;
+    }
   }
 #pragma unroll
   for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
@@ -544,20 +547,26 @@ template __global__ void attn_bwd_kernel<64, false>(BwdArgs);
 template __global__ void attn_bwd_kernel<128, true>(BwdArgs);
 template __global__ void attn_bwd_kernel<128, false>(BwdArgs);
 
+hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st) {
+  const long rows = (long)a.T * a.H;
+  if (rows == 0) return hipSuccess;
+  const int epc = io_f32 ? 4 : 8;
+  const int rpw = 64 / (D / epc);
+  const long waves = (rows + rpw - 1) / rpw;
+  dim3 g((unsigned)((waves + 3) / 4)), b(256);
+  if (D == 64 && !io_f32) bwd_pre_kernel<64, false><<<g, b, 0, st>>>(a);
+  else if (D == 64) bwd_pre_kernel<64, true><<<g, b, 0, st>>>(a);
+  else if (!io_f32) bwd_pre_kernel<128, false><<<g, b, 0, st>>>(a);
+  else bwd_pre_kernel<128, true><<<g, b, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st) {
   const long rows = (long)a.T * a.H;
   if (rows == 0) return hipSuccess;
   // 1. D_i and zeroed accumulator
   {
-    const int epc = io_f32 ? 4 : 8;
-    const int rpw = 64 / (D / epc);
-    const long waves = (rows + rpw - 1) / rpw;
-    dim3 g((unsigned)((waves + 3) / 4)), b(256);
-    if (D == 64 && !io_f32) bwd_pre_kernel<64, false><<<g, b, 0, st>>>(a);
-    else if (D == 64) bwd_pre_kernel<64, true><<<g, b, 0, st>>>(a);
-    else if (!io_f32) bwd_pre_kernel<128, false><<<g, b, 0, st>>>(a);
-    else bwd_pre_kernel<128, true><<<g, b, 0, st>>>(a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_bwd_pre(D, io_f32, a, st);
     if (e != hipSuccess) return e;
   }
   // 2. main

@@ -1,0 +1,449 @@
+// BF16 attention backward for gfx950: the baseline of the MXFP8 backward
+// ("Low Precision Flash Attention 4: End-to-End Block-Scaled Attention for
+// Blackwell", headline speed-ups over BF16 FlashAttention-4).
+//
+// Same computation as the MXFP8 backward with every MX step removed: S and dP
+// from bf16 operands in fp32, p = 2^(S c - LSE log2 e), D_i = rowsum(dO o O)
+// in fp32, dS = p (dP - D), P and dS rounded to bf16 (nearest even) for
+// dV = P^T dO, dK = sigma dS^T Q and dQ = sigma dS K.
+//
+// gfx950 design.  Device-scope atomics execute at the memory side on this
+// chip (the per-XCD L2s are not coherent with each other), and an fp32 dQ
+// reduction over 128-key tiles would move about four times the atomic
+// traffic that bounds the MXFP8 backward.  So dQ is not reduced with atomics:
+//  1. bwd_pre_kernel (shared with the MXFP8 path): D_i.
+//  2. dkdv kernel, key-stationary: a workgroup of 4 waves owns 128 keys, each
+//     wave 32 keys whose K and V rows stay in registers; it walks 64-query
+//     steps (Q, dO, LSE, D double-buffered in LDS), computes S = Q K^T and
+//     dP = dO V^T with keys as the output columns (a lane owns one key), and
+//     accumulates dV^T += dO^T P and dK^T += Q^T dS in registers, the
+//     transposed Q and dO operands read with ds_read_b64_tr_b16.
+//  3. dq kernel, query-stationary (the forward's skeleton): a wave owns 32
+//     queries with Q and dO resident, walks 64-key tiles of K and V staged in
+//     LDS, recomputes S^T and dP^T, and accumulates dQ^T += K^T dS^T in
+//     registers; one write per element, no reduction across workgroups.
+// The recompute costs three extra products per pair (7 instead of 5), in
+// exchange for no atomics and a deterministic result.
+#include "mx_common.h"
+#include "mx_launch.h"
+
+namespace mxk {
+
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+MX_DEV v16f mfma_bf16(uint4 a, uint4 b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+MX_DEV uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
+
+MX_DEV uint2 lds_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(p)));
+}
+
+// Transposed operand from a row-major bf16 tile with row stride RS bytes: lane (n, g) receives
+// element (rows r0 + 8g + 0..7, column c0 + n), i.e. 8 consecutive rows of one column.  In each
+// 16-lane group G, lane i addresses row r0 + 8g + 4h + i/4 at column c0 + 16(G%2) + 4(i%4) for
+// the h-th read, and receives column c0 + 16(G%2) + i of the four rows read by lanes i/4 + 4m.
+template <int RS>
+MX_DEV uint4 tr_operand(const uint8_t* tile, int r0, int c0, int lane) {
+  const int G = lane >> 4, i16 = lane & 15, g = lane >> 5;
+  const uint8_t* p = tile + (r0 + 8 * g + (i16 >> 2)) * RS + 2 * (c0 + 16 * (G & 1) + 4 * (i16 & 3));
+  const uint2 a = lds_tr16(p), b = lds_tr16(p + 4 * RS);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Regroup 16 fp32 values held in the 32x32 output layout (element i = row 8(i/4) + 4g + i%4 of
+// the block) into bf16 operands: op[h] holds rows 16h + 8g + 0..7 of the block, in order.
+MX_DEV void to_operands(const float* x, uint4 op[2]) {
+  uint32_t w[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[q][0] = pack_bf16(x[4 * q], x[4 * q + 1]);
+    w[q][1] = pack_bf16(x[4 * q + 2], x[4 * q + 3]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * h][0], w[2 * h + 1][0], false, false);
+    auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * h][1], w[2 * h + 1][1], false, false);
+    op[h] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+  }
+}
+
+// store 4 consecutive values of one row, bf16 or fp32
+MX_DEV void store4(void* base, long off, bool f32, float v0, float v1, float v2, float v3) {
+  if (f32) {
+    *(float4*)((float*)base + off) = make_float4(v0, v1, v2, v3);
+  } else {
+    *(uint2*)((uint16_t*)base + off) =
+        make_uint2(f32_to_bf16(v0) | (f32_to_bf16(v1) << 16), f32_to_bf16(v2) | (f32_to_bf16(v3) << 16));
+  }
+}
+
+template <int D>
+struct Step16 {
+  static constexpr int CH = 64 * 2 * D / 16 / 256;   // 16-byte chunks per thread per tensor
+  uint4 q[CH], d[CH];
+  float lse2;   // fl32(LSE log2 e) of query lane (threads 0..63) or D (threads 64..127)
+};
+
+}  // namespace
+
+// ------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
+  constexpr int BN = 128;       // keys per workgroup (4 waves x 32)
+  constexpr int BQ = 64;        // queries per step
+  constexpr int NK = D / 16;    // 16-feature steps of the S and dP contractions
+  constexpr int ND = D / 32;    // 32-feature chunks of dK, dV
+  constexpr int RB = 2 * D;     // bytes per token row of one head
+  constexpr int RS = RB + 32;   // LDS row stride
+  constexpr int CPR = RB / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t sO[2][BQ * RS];   // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];          // fl32(LSE log2 e)
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];          // D_i
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int u = (j / a.nkt) * 8 + xcd;
+  if (u >= a.nseq * a.H) return;
+  const int kt = j % a.nkt;   // causal: the first key tiles have the most queries, so they go first
+  const int h = __builtin_amdgcn_readfirstlane(u % a.H), s = __builtin_amdgcn_readfirstlane(u / a.H);
+  int tok0, L, srow0, sblk0;
+  a.seq.get(s, tok0, L, srow0, sblk0);
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int k0 = kt * BN;
+  if (k0 >= L) return;
+  const int kw0 = k0 + 32 * w;   // this wave's first key
+  const int key = kw0 + n;
+  const long rowH = (long)a.H * D;
+  const uint16_t *gq = (const uint16_t*)a.q, *gk = (const uint16_t*)a.k, *gv = (const uint16_t*)a.v;
+  const uint16_t* gd = (const uint16_t*)a.dout;
+
+  // own K and V rows: second operands of S = Q K^T and dP = dO V^T (lane (n, g): features 16k + 8g..)
+  uint4 kr[NK], vr[NK];
+  if (key < L) {
+    const long off = (long)(tok0 + key) * rowH + (long)h * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      kr[k] = *(const uint4*)(gk + off + 16 * k);
+      vr[k] = *(const uint4*)(gv + off + 16 * k);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) kr[k] = vr[k] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int nsteps = (L - qstart + BQ - 1) / BQ;
+  const float c = a.c;
+
+  // one 64-query step: rows past the sequence read as zero (and LSE, D as 0)
+  auto load_step = [&](int t, Step16<D>& st) {
+    const int q0 = qstart + t * BQ;
+    const int rows = min(BQ, L - q0);
+    const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
+    const int nrec = ((rows - 1) * (int)rowH + D) * 2;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(gq + tb, nrec), rd = buffer_rsrc(gd + tb, nrec);
+#pragma unroll
+    for (int cc = 0; cc < Step16<D>::CH; ++cc) {
+      const int ch = tid + cc * 256;
+      const int off = (ch / CPR) * (int)rowH * 2 + (ch % CPR) * 16;
+      st.q[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      st.d[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+    // LSE and D rows of this head: [B, H, S] (fixed) or [H, T] (varlen)
+    const long li = a.seq.cu ? (long)h * a.T + tok0 + q0 : ((long)s * a.H + h) * a.seq.S + q0;
+    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.lse + li, rows * 4), rD = buffer_rsrc(a.Dbuf + li, rows * 4);
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(tid < 64 ? rl : rD, (tid & 63) * 4, 0, 0));
+    st.lse2 = tid < 64 ? x * 1.44269504088896340736f : x;
+  };
+  auto store_step = [&](int buf, const Step16<D>& st) {
+#pragma unroll
+    for (int cc = 0; cc < Step16<D>::CH; ++cc) {
+      const int ch = tid + cc * 256;
+      const int r = ch / CPR, cx = ch % CPR;
+      *(uint4*)(&sQ[buf][r * RS + cx * 16]) = st.q[cc];
+      *(uint4*)(&sO[buf][r * RS + cx * 16]) = st.d[cc];
+    }
+    if (tid < 64) sL[buf][tid] = st.lse2;
+    else if (tid < 128) sD[buf][tid - 64] = st.lse2;
+  };
+
+  v16f dk[ND], dv[ND];
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc) dk[dc] = dv[dc] = v16f{};
+
+  {
+    Step16<D> s0;
+    load_step(0, s0);
+    store_step(0, s0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < nsteps; ++t) {
+    const int cur = t & 1;
+    const int q0 = qstart + t * BQ;
+    Step16<D> nx;
+    load_step(min(t + 1, nsteps - 1), nx);
+
+    const bool compute = kw0 < L && !(CAUSAL && q0 + BQ - 1 < kw0);
+    if (compute) {
+      const uint8_t* sQc = sQ[cur];
+      const uint8_t* sOc = sO[cur];
+      const bool need_mask = (q0 + BQ > L) || (CAUSAL && q0 < kw0 + 31);
+      uint4 pop[4], sop[4];   // P and dS operands: step k4 holds queries 16 k4 + 8g + 0..7 of key n
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // S, dP: element i = query q0 + 32 qb + 8(i/4) + 4g + i%4, key = key
+        v16f S = v16f{}, dP = v16f{};
+        const uint8_t* qp = sQc + (32 * qb + n) * RS + 16 * g;
+        const uint8_t* op = sOc + (32 * qb + n) * RS + 16 * g;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          S = mfma_bf16(*(const uint4*)(qp + 32 * k), kr[k], S);
+          dP = mfma_bf16(*(const uint4*)(op + 32 * k), vr[k], dP);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 l4 = *(const float4*)&sL[cur][32 * qb + 8 * q + 4 * g];
+          const float4 d4 = *(const float4*)&sD[cur][32 * qb + 8 * q + 4 * g];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            float pv = __builtin_amdgcn_exp2f(fmaf(S[i], c, -lv[e]));
+            if (need_mask) {
+              const int qq = q0 + 32 * qb + 8 * q + 4 * g + e;
+              const bool vis = qq < L && (!CAUSAL || qq >= key);
+              pv = vis ? pv : 0.f;
+            }
+            p[i] = pv;
+            ds[i] = pv * (dP[i] - dvv[e]);
+          }
+        }
+        to_operands(p, &pop[2 * qb]);
+        to_operands(ds, &sop[2 * qb]);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS: rows d = 32 dc + ..., columns = key n, contraction = 64 queries
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          dv[dc] = mfma_bf16(tr_operand<RS>(sOc, 16 * k4, 32 * dc, lane), pop[k4], dv[dc]);
+          dk[dc] = mfma_bf16(tr_operand<RS>(sQc, 16 * k4, 32 * dc, lane), sop[k4], dk[dc]);
+        }
+    }
+    store_step(cur ^ 1, nx);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane = key, element i of chunk dc = feature 32 dc + 8(i/4) + 4g + i%4
+  if (key >= L) return;
+  const long row = (long)(tok0 + key) * rowH + (long)h * D;
+  const bool f32 = a.grad_f32 != 0;
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * dc + 8 * q + 4 * g;
+      store4(a.dv, row + d, f32, dv[dc][4 * q], dv[dc][4 * q + 1], dv[dc][4 * q + 2], dv[dc][4 * q + 3]);
+      store4(a.dk, row + d, f32, a.sigma * dk[dc][4 * q], a.sigma * dk[dc][4 * q + 1], a.sigma * dk[dc][4 * q + 2],
+             a.sigma * dk[dc][4 * q + 3]);
+    }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+struct KV16 {
+  static constexpr int CH = 64 * 2 * D / 16 / 256;
+  uint4 k[CH], v[CH];
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_bwd_bf16_dq_kernel(BwdArgs a) {
+  constexpr int BM = 128;       // queries per workgroup (4 waves x 32)
+  constexpr int BN = 64;        // keys per tile
+  constexpr int NK = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int RB = 2 * D;
+  constexpr int RS = RB + 32;
+  constexpr int CPR = RB / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][BN * RS];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int u = (j / a.nkt) * 8 + xcd;
+  if (u >= a.nseq * a.H) return;
+  const int qt = a.nkt - 1 - (j % a.nkt);   // longest causal query tiles first
+  const int h = __builtin_amdgcn_readfirstlane(u % a.H), s = __builtin_amdgcn_readfirstlane(u / a.H);
+  int tok0, L, srow0, sblk0;
+  a.seq.get(s, tok0, L, srow0, sblk0);
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int qbase = qt * BM;
+  if (qbase >= L) return;
+  const int q0 = qbase + 32 * w;
+  const int qi = q0 + n;
+  const long rowH = (long)a.H * D;
+  const uint16_t *gq = (const uint16_t*)a.q, *gk = (const uint16_t*)a.k, *gv = (const uint16_t*)a.v;
+  const uint16_t* gd = (const uint16_t*)a.dout;
+
+  auto load_tile = [&](int t, KV16<D>& st) {
+    const int k0 = t * BN;
+    const int rows = min(BN, L - k0);
+    const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
+    const int nrec = ((rows - 1) * (int)rowH + D) * 2;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk + tb, nrec), rv = buffer_rsrc(gv + tb, nrec);
+#pragma unroll
+    for (int cc = 0; cc < KV16<D>::CH; ++cc) {
+      const int ch = tid + cc * 256;
+      const int off = (ch / CPR) * (int)rowH * 2 + (ch % CPR) * 16;
+      st.k[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      st.v[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  auto store_tile = [&](int buf, const KV16<D>& st) {
+#pragma unroll
+    for (int cc = 0; cc < KV16<D>::CH; ++cc) {
+      const int ch = tid + cc * 256;
+      const int r = ch / CPR, cx = ch % CPR;
+      *(uint4*)(&sK[buf][r * RS + cx * 16]) = st.k[cc];
+      *(uint4*)(&sV[buf][r * RS + cx * 16]) = st.v[cc];
+    }
+  };
+
+  // Q and dO of query qi as second operands (features 16k + 8g + 0..7); LSE, D of qi
+  uint4 qa[NK], da[NK];
+  float l2 = 0.f, Dq = 0.f;
+  if (qi < L) {
+    const long off = (long)(tok0 + qi) * rowH + (long)h * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      qa[k] = *(const uint4*)(gq + off + 16 * k);
+      da[k] = *(const uint4*)(gd + off + 16 * k);
+    }
+    const long li = a.seq.cu ? (long)h * a.T + tok0 + qi : ((long)s * a.H + h) * a.seq.S + qi;
+    l2 = a.lse[li] * 1.44269504088896340736f;
+    Dq = a.Dbuf[li];
+  } else {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) qa[k] = da[k] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int kend = CAUSAL ? min(L, qbase + BM) : L;
+  const int ntiles = (kend + BN - 1) / BN;
+  const float c = a.c;
+  v16f dq[ND];
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc) dq[dc] = v16f{};
+
+  {
+    KV16<D> st0;
+    load_tile(0, st0);
+    store_tile(0, st0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    const int cur = t & 1;
+    KV16<D> nxt;
+    load_tile(min(t + 1, ntiles - 1), nxt);
+
+    const bool compute = q0 < L && !(CAUSAL && k0 > q0 + 31);
+    if (compute) {
+      const uint8_t* sKc = sK[cur];
+      const uint8_t* sVc = sV[cur];
+      const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T, dP^T: element i = key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
+        v16f St = v16f{}, dPt = v16f{};
+        const uint8_t* kp = sKc + (32 * kb + n) * RS + 16 * g;
+        const uint8_t* vp = sVc + (32 * kb + n) * RS + 16 * g;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          St = mfma_bf16(*(const uint4*)(kp + 32 * k), qa[k], St);
+          dPt = mfma_bf16(*(const uint4*)(vp + 32 * k), da[k], dPt);
+        }
+        float ds[16];
+        const int last = CAUSAL ? min(L - 1, qi) : L - 1;
+        const int hi = last - k0 - 32 * kb - 4 * g + 1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(St[i], c, -l2));
+          if (need_mask) pv = (8 * (i >> 2) + (i & 3) < hi) ? pv : 0.f;
+          ds[i] = pv * (dPt[i] - Dq);
+        }
+        uint4 sop[2];   // dS^T operand: step h holds keys 32 kb + 16 h + 8g + 0..7 of query qi
+        to_operands(ds, sop);
+        // dQ^T += K^T dS^T: rows d = 32 dc + n, contraction over the block's 32 keys
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+            dq[dc] = mfma_bf16(tr_operand<RS>(sKc, 32 * kb + 16 * h2, 32 * dc, lane), sop[h2], dq[dc]);
+      }
+    }
+    store_tile(cur ^ 1, nxt);
+    __syncthreads();
+  }
+
+  if (qi >= L) return;
+  const long row = (long)(tok0 + qi) * rowH + (long)h * D;
+  const bool f32 = a.grad_f32 != 0;
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * dc + 8 * q + 4 * g;
+      store4(a.dq, row + d, f32, a.sigma * dq[dc][4 * q], a.sigma * dq[dc][4 * q + 1], a.sigma * dq[dc][4 * q + 2],
+             a.sigma * dq[dc][4 * q + 3]);
+    }
+}
+
+hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipStream_t st) {
+  const long rows = (long)a.T * a.H;
+  if (rows == 0) return hipSuccess;
+  a.acc = nullptr;
+  if (hipError_t e = launch_bwd_pre(D, false, a, st); e != hipSuccess) return e;
+  const long units = (long)a.nseq * a.H;
+  {
+    BwdArgs b = a;
+    b.nkt = (max_len + 127) / 128;
+    const long grid = ((units + 7) / 8) * 8 * b.nkt;
+    dim3 gd((unsigned)grid), bd(256);
+    if (D == 64 && causal) attn_bwd_bf16_dkdv_kernel<64, true><<<gd, bd, 0, st>>>(b);
+    else if (D == 64) attn_bwd_bf16_dkdv_kernel<64, false><<<gd, bd, 0, st>>>(b);
+    else if (causal) attn_bwd_bf16_dkdv_kernel<128, true><<<gd, bd, 0, st>>>(b);
+    else attn_bwd_bf16_dkdv_kernel<128, false><<<gd, bd, 0, st>>>(b);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  {
+    BwdArgs b = a;
+    b.nkt = (max_len + 127) / 128;   // query tiles of 128
+    const long grid = ((units + 7) / 8) * 8 * b.nkt;
+    dim3 gd((unsigned)grid), bd(256);
+    if (D == 64 && causal) attn_bwd_bf16_dq_kernel<64, true><<<gd, bd, 0, st>>>(b);
+    else if (D == 64) attn_bwd_bf16_dq_kernel<64, false><<<gd, bd, 0, st>>>(b);
+    else if (causal) attn_bwd_bf16_dq_kernel<128, true><<<gd, bd, 0, st>>>(b);
+    else attn_bwd_bf16_dq_kernel<128, false><<<gd, bd, 0, st>>>(b);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace mxk

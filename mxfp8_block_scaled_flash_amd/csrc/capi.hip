@@ -358,6 +358,72 @@ static mx_status bwd_common(const uint8_t* q_data, const uint8_t* q_scale, const
   return MX_OK;
 }
 
+size_t mx_attn_bwd_bf16_workspace_bytes(int tokens, int H) {
+  if (tokens < 0 || H < 1) return 0;
+  return ((size_t)tokens * H * 4 + 255) / 256 * 256;
+}
+
+static mx_status bwd_bf16_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                 const uint16_t* dout, const float* lse, int H, int D, float softmax_scale, void* dq,
+                                 void* dk, void* dv, mx_dtype grad_dtype, void* workspace, size_t workspace_bytes,
+                                 int tokens, mxk::BwdArgs& a) {
+  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (grad_dtype != MX_BF16 && grad_dtype != MX_F32) return MX_EINVAL;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
+  if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return MX_EINVAL;
+  if (!workspace || !aligned16(workspace)) return MX_EWORKSPACE;
+  if (workspace_bytes < mx_attn_bwd_bf16_workspace_bytes(tokens, H)) return MX_EWORKSPACE;
+  a.q = (const uint8_t*)q; a.k = (const uint8_t*)k; a.v = (const uint8_t*)v;
+  a.o = o; a.dout = dout; a.lse = lse;
+  a.H = H;
+  a.c = log2_scale(softmax_scale);
+  a.sigma = softmax_scale;
+  a.grad_f32 = grad_dtype == MX_F32;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.acc = nullptr;
+  a.Dbuf = static_cast<float*>(workspace);
+  return MX_OK;
+}
+
+mx_status mx_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                           const uint16_t* dout, const float* lse, int B, int S, int H, int D, float softmax_scale,
+                           int causal, void* dq, void* dk, void* dv, mx_dtype grad_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_bf16_common(q, k, v, o, dout, lse, H, D, softmax_scale, dq, dk, dv, grad_dtype, workspace,
+                                     workspace_bytes, B * S, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.nseq = B;
+  a.T = B * S;
+  return from_hip(mxk::launch_attn_bwd_bf16(D, causal != 0, a, S, stream));
+}
+
+mx_status mx_attn_bwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                  const uint16_t* dout, const float* lse, const int32_t* cu_seqlens, int nseq,
+                                  int total_tokens, int max_seqlen, int H, int D, float softmax_scale, int causal,
+                                  void* dq, void* dk, void* dv, mx_dtype grad_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens) return MX_EINVAL;
+  if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_bf16_common(q, k, v, o, dout, lse, H, D, softmax_scale, dq, dk, dv, grad_dtype, workspace,
+                                     workspace_bytes, total_tokens, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_seqlens;   // no scale rows in this path
+  a.nseq = nseq;
+  a.T = total_tokens;
+  return from_hip(mxk::launch_attn_bwd_bf16(D, causal != 0, a, max_seqlen, stream));
+}
+
 mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data, const uint8_t* k_scale,
                       const uint8_t* v_data, const uint8_t* v_scale, const uint8_t* do_data, const uint8_t* do_scale,
                       const void* o, const void* dout, mx_dtype io_dtype, const float* lse, int B, int S, int H, int D,

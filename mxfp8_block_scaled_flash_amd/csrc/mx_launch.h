@@ -64,6 +64,8 @@ hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipSt
 hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_fwd_bf16(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);
+hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st);
+hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mxk

@@ -142,6 +142,23 @@ def test_bf16_forward_empty_and_varlen_validation():
     assert L.mx_attn_fwd_bf16_varlen(16, 16, 16, 16, 1, 0, 10, 1, 128, 0.1, 1, 16, mx.BF16, None, None) == 0
 
 
+def test_bf16_backward_validation():
+    L = mx.lib()
+    n = L.mx_attn_bwd_bf16_workspace_bytes(64, 2)
+    assert n == 512 and L.mx_attn_bwd_bf16_workspace_bytes(-1, 2) == 0
+    args = [16] * 6 + [1, 64, 1, 128, 0.1, 1] + [16] * 3 + [mx.BF16, 16, n, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return L.mx_attn_bwd_bf16(*a)
+    assert call(a9=80) == EINVAL and call(a10=0.0) == EINVAL and call(a15=mx.F16) == EINVAL
+    assert call(a0=None) == EINVAL and call(a5=24) == EINVAL
+    assert call(a16=None) == 4 and call(a17=L.mx_attn_bwd_bf16_workspace_bytes(64, 1) - 1) == 4
+    assert call(a6=0) == 0
+
+
 def test_workspace_size():
     n = mx.lib().mx_attn_bwd_workspace_bytes(1000, 3, 128)
     assert n >= 1000 * 3 * 128 * 2 + 1000 * 3 * 4 and n % 256 == 0
