@@ -1,0 +1,76 @@
+"""Pins of the MXFP6 / MXFP4 codec (oracle/mxsmall.py) against the OCP MX
+format definitions and brute force, independent of any kernel."""
+import numpy as np
+import pytest
+
+from oracle import mxsmall as ms
+
+# facts of the OCP MX v1.0 element formats: (largest, smallest normal, smallest subnormal, #codes)
+SPEC = {"e2m3": (7.5, 1.0, 0.125, 64), "e3m2": (28.0, 0.25, 0.0625, 64), "e2m1": (6.0, 1.0, 0.5, 16)}
+
+
+@pytest.mark.parametrize("fmt", list(SPEC))
+def test_decode_table_matches_the_format_facts(fmt):
+    mx_, mn, sub, n = SPEC[fmt]
+    v = ms.decode(np.arange(n), fmt)
+    pos = v[: n // 2]
+    assert np.all(np.diff(pos) > 0), "codes of one sign increase with the value"
+    assert pos[0] == 0 and pos[1] == sub and pos[-1] == mx_ == ms.max_value(fmt)
+    assert np.min(pos[pos >= mn]) == mn and np.all(np.isin(mn, pos))
+    assert np.array_equal(v[n // 2:], -pos)                       # sign bit mirrors
+    if fmt == "e2m1":
+        assert pos.tolist() == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+@pytest.mark.parametrize("fmt", list(SPEC))
+def test_encode_is_nearest_with_ties_to_even_and_saturates(fmt):
+    n = SPEC[fmt][3]
+    vals = ms.decode(np.arange(n // 2), fmt)
+    rng = np.random.default_rng(0)
+    y = np.concatenate([rng.uniform(-1.3, 1.3, 4000) * ms.max_value(fmt),
+                        (vals[1:] + vals[:-1]) / 2, -(vals[1:] + vals[:-1]) / 2,    # exact ties
+                        vals, -vals, [1e9, -1e9, 0.0]])
+    got = ms.encode(y, fmt)
+    a = np.minimum(np.abs(y), ms.max_value(fmt))
+    d = np.abs(vals[None, :] - a[:, None])
+    best = d == d.min(axis=1, keepdims=True)
+    # among equally near codes take the even one (ties to even mantissa)
+    cand = [np.flatnonzero(b) for b in best]
+    want = np.array([c[0] if len(c) == 1 else c[c % 2 == 0][0] for c in cand])
+    assert np.array_equal(got & (n // 2 - 1), want)
+    assert np.array_equal(got >= n // 2, np.signbit(y))
+
+
+@pytest.mark.parametrize("fmt", list(SPEC))
+def test_scale_rule_puts_the_block_max_in_the_top_binade(fmt):
+    emax = ms.FORMATS[fmt][3]
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((200, 64)) * np.exp2(rng.integers(-20, 20, (200, 1)))
+    codes, k = ms.quantize_rows(x, fmt)
+    xb = np.abs(x.reshape(200, 2, 32)).max(axis=-1)
+    assert np.array_equal(k.astype(int), np.floor(np.log2(xb)).astype(int) - emax + 127)
+    y = xb / np.exp2(k.astype(float) - 127)
+    assert np.all((y >= 2.0**emax) & (y < 2.0 ** (emax + 1)))
+    # a block whose max is exactly the format's largest value times a power of two is exact
+    z = np.zeros((1, 32))
+    z[0, 5] = ms.max_value(fmt) * 2.0**-3
+    c, kk = ms.quantize_rows(z, fmt)
+    assert ms.dequantize_rows(c, kk, fmt)[0, 5] == z[0, 5] and np.all(ms.dequantize_rows(c, kk, fmt)[0, :5] == 0)
+    assert ms.scale_code(0.0, fmt) == 0
+
+
+@pytest.mark.parametrize("fmt", list(SPEC))
+def test_pack_unpack_and_bit_order(fmt):
+    n = SPEC[fmt][3]
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, n, (3, 64)).astype(np.uint8)
+    p = ms.pack(c, fmt)
+    assert p.shape == (3, 64 * ms.BITS[fmt] // 8)
+    assert np.array_equal(ms.unpack(p, 64, fmt), c)
+    if fmt == "e2m1":
+        assert ms.pack(np.array([[2, 7]], np.uint8), fmt).tolist() == [[0x72]]     # element 0 in the low nibble
+    else:
+        # element 0 in bits 0..5, element 1 in bits 6..11, ...
+        assert ms.pack(np.array([[1, 0, 0, 0]], np.uint8), fmt).tolist() == [[1, 0, 0]]
+        assert ms.pack(np.array([[0, 1, 0, 0]], np.uint8), fmt).tolist() == [[0x40, 0, 0]]
+        assert ms.pack(np.array([[0, 0, 0, 63]], np.uint8), fmt).tolist() == [[0, 0, 0xFC]]
