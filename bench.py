@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 MXFP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 / MXFP8 MFMA peak
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak
+FP6_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp6 / fp4 MFMA peak
 HBM_PEAK_GBS = 8000.0
 
 
@@ -176,7 +177,7 @@ def main():
                           dtype=torch.uint8, device=dev)) for l in (ROW, SQ)}
 
     def gemm_q():
-        mx.mx_gemm_quantize(ga[ROW][0], ga[ROW][1], gb[ROW][0], gb[ROW][1], gM, gN, gK, ROW | SQ, gc[ROW][0],
+        mx.mx_gemm_quantize(ga[ROW][0], ga[ROW][1], gb[ROW][0], gb[ROW][1], mx.E4M3, gM, gN, gK, ROW | SQ, gc[ROW][0],
                             gc[ROW][1], None, None, gc[SQ][0], gc[SQ][1], None)
 
     gemm_q()
@@ -188,6 +189,29 @@ def main():
     torch.cuda.synchronize()
     g_ms = r0.elapsed_time(r1) / 5
     g_tflops = 2.0 * gM * gN * gK / (g_ms * 1e-3) / 1e12
+    # the same GEMM with MXFP6 (E2M3) and MXFP4 (E2M1) operands, produced by the row quantizer
+    g_fmt = {}
+    hid = torch.randn((gM, gK), device=dev, dtype=torch.bfloat16)
+    wgt = torch.randn((gN, gK), device=dev, dtype=torch.bfloat16) * (1.0 / math.sqrt(gK))
+    for name, fmt in (("mxfp6_e2m3", mx.E2M3), ("mxfp4_e2m1", mx.E2M1)):
+        qa, qb = mx.quantize_rows(hid, fmt), mx.quantize_rows(wgt, fmt)
+
+        def gemm_f(qa=qa, qb=qb, fmt=fmt):
+            mx.mx_gemm_quantize(qa[0], qa[1], qb[0], qb[1], fmt, gM, gN, gK, ROW | SQ, gc[ROW][0], gc[ROW][1],
+                                None, None, gc[SQ][0], gc[SQ][1], None)
+
+        gemm_f()
+        r0, r1 = ev(), ev()
+        r0.record(stream)
+        for _ in range(5):
+            gemm_f()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        ms_ = r0.elapsed_time(r1) / 5
+        tf = 2.0 * gM * gN * gK / (ms_ * 1e-3) / 1e12
+        g_fmt[name] = {"ms": round(ms_, 4), "tflops": round(tf, 2), "pct_peak": round(100 * tf / FP6_FP4_PEAK_TFLOPS, 2)}
+        del qa, qb
+    del hid, wgt
 
     # BF16 attention forward on the same inputs (the baseline of the MX speed-up), timed alone
     o16 = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
@@ -266,7 +290,8 @@ def main():
         "rmsnorm_quantize_ms": round(n_ms, 4),
         "rmsnorm_quantize_gbs": round(B * S * H * D * (2 + per_layout[ROW] + per_layout[SQ]) / (n_ms * 1e-3) / 1e9, 1),
         "gemm_quantize": {"M": gM, "N": gN, "K": gK, "layouts": "row32+sq32", "ms": round(g_ms, 4),
-                          "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2)},
+                          "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2),
+                          **g_fmt},
         "bf16_fwd": {"ms": round(f16_ms, 4), "tflops": round(f_flop / (f16_ms * 1e-3) / 1e12, 2),
                      "pct_bf16_peak": round(100 * f_flop / (f16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
                      "mx_speedup": round(f16_ms / f_ms, 3)},

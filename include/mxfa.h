@@ -87,6 +87,14 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1, MX_F16 = 2 } mx_dtype;
 
 enum { MX_ROW32 = 1, MX_COL32 = 2, MX_SQ32 = 4 };
 
+/* Element formats of MX payloads, numbered as the block-scaled matrix
+ * instruction's format fields: MXFP8 E4M3, MXFP6 E2M3 and E3M2, MXFP4 E2M1
+ * ([News], paragraph on the block-scaled MMA instructions; element
+ * definitions of OCP MX v1.0: no Inf/NaN in the 6- and 4-bit formats,
+ * round to nearest even, saturating).  A w-bit payload row is a
+ * little-endian bitstream: element j at bits [w j, w j + w). */
+typedef enum { MX_E4M3 = 0, MX_E2M3 = 2, MX_E3M2 = 3, MX_E2M1 = 4 } mx_elem;
+
 /* ABI version (MXFA_ABI_VERSION) and a static string for a status code. */
 int mx_abi_version(void);
 const char* mx_status_str(mx_status s);
@@ -172,12 +180,32 @@ mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const floa
                                      hipStream_t stream);
 
 /*
+ * mx_quantize_rows -- MX quantization of a GEMM operand in any element format:
+ * blocks of 32 along each row of x [rows, K] (the contraction axis), E8M0
+ * scale clamp(floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3),
+ * 2 (E2M3, E2M1) or 4 (E3M2), elements RNE-encoded and saturated.
+ *   x       [rows, K] in x_dtype (MX_BF16 or MX_F32), 16-byte aligned
+ *   K       a positive multiple of 32
+ *   data    [rows, K * w / 8] bytes, w = 8, 6, 4 bits (16-byte aligned)
+ *   scale   [rows, K / 32] E8M0 bytes
+ * For E4M3 this equals mx_quantize's ROW32 output of an [rows, 1, K/D, D]
+ * tensor.  Errors: MX_EINVAL for a bad shape, format, dtype or alignment;
+ * rows = 0: MX_OK.  Ownership: caller's buffers.
+ */
+mx_status mx_quantize_rows(const void* x, mx_dtype x_dtype, int rows, int K, mx_elem format,
+                           uint8_t* data, uint8_t* scale, hipStream_t stream);
+
+/*
  * mx_gemm_quantize -- MX GEMM with a quantizing epilogue: C = A B^T.
  * Defines: [News], contributions paragraph (fused GEMM + Quantize producers
  * emitting FP8 with several scale layouts in one pass); the block-scaled
  * GEMM itself as in [Blog], "1. End-to-End Block-Scaled GEMM Fusion".
- *   a_data, a_scale  A [M, K] E4M3 payload, ROW32 scales [M, K/32]
- *   b_data, b_scale  B [N, K] E4M3 payload, ROW32 scales [N, K/32]
+ *   a_data, a_scale  A [M, K] payload in ab_format (packed rows of K*w/8
+ *                    bytes, as mx_quantize_rows writes), ROW32 scales [M, K/32]
+ *   b_data, b_scale  B [N, K] likewise
+ *   ab_format        element format of A and B: MX_E4M3, MX_E2M3, MX_E3M2 or
+ *                    MX_E2M1 (the matrix instruction's format fields; the
+ *                    6- and 4-bit formats are the pages' MXFP6 / MXFP4)
  *                    (B is the [out, in] weight; C[m, n] = sum_k A[m,k] B[n,k])
  *   C is accumulated in fp32 by the block-scaled matrix instruction, then
  *   quantized to MXFP8 in the requested layouts (0 allowed when c_f32 is
@@ -192,7 +220,7 @@ mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const floa
  * Ownership: all buffers belong to the caller; nothing is allocated.
  */
 mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale,
-                           const uint8_t* b_data, const uint8_t* b_scale,
+                           const uint8_t* b_data, const uint8_t* b_scale, mx_elem ab_format,
                            int M, int N, int K, unsigned layouts,
                            uint8_t* c_row32_data, uint8_t* c_row32_scale,
                            uint8_t* c_col32_data, uint8_t* c_col32_scale,

@@ -18,6 +18,9 @@ import torch
 ROW32, COL32, SQ32 = 1, 2, 4
 F32, BF16, F16 = 0, 1, 2
 LAYOUT_NAMES = {ROW32: "row32", COL32: "col32", SQ32: "sq32"}
+# element formats (the block-scaled matrix instruction's format codes) and their widths in bits
+E4M3, E2M3, E3M2, E2M1 = 0, 2, 3, 4
+ELEM_BITS = {E4M3: 8, E2M3: 6, E3M2: 6, E2M1: 4}
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfa.so")
 _lib = None
@@ -35,7 +38,8 @@ _SIGS = {
                             + [_vp] * 6 + [_vp], _c_int),
     "mx_rmsnorm_quantize_varlen": ([_vp, _c_int, _vp, _c_float, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
-    "mx_gemm_quantize": ([_vp] * 4 + [_c_int] * 3 + [ctypes.c_uint] + [_vp] * 7 + [_vp], _c_int),
+    "mx_quantize_rows": ([_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "mx_gemm_quantize": ([_vp] * 4 + [_c_int] * 4 + [ctypes.c_uint] + [_vp] * 7 + [_vp], _c_int),
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
@@ -150,9 +154,14 @@ def mx_rmsnorm_quantize_varlen(x, gamma, eps, cu_seqlens, cu_scale_rows, nseq, t
                                             _stream(stream)), "mx_rmsnorm_quantize_varlen")
 
 
-def mx_gemm_quantize(a_data, a_scale, b_data, b_scale, M, N, K, layouts, c_row32_data, c_row32_scale,
+def mx_quantize_rows(x, rows, K, fmt, data, scale, stream=None):
+    _check(lib().mx_quantize_rows(_ptr(x), _dtype_code(x.dtype), rows, K, fmt, _ptr(data), _ptr(scale),
+                                  _stream(stream)), "mx_quantize_rows")
+
+
+def mx_gemm_quantize(a_data, a_scale, b_data, b_scale, fmt, M, N, K, layouts, c_row32_data, c_row32_scale,
                      c_col32_data, c_col32_scale, c_sq32_data, c_sq32_scale, c_f32, stream=None):
-    _check(lib().mx_gemm_quantize(_ptr(a_data), _ptr(a_scale), _ptr(b_data), _ptr(b_scale), M, N, K, layouts,
+    _check(lib().mx_gemm_quantize(_ptr(a_data), _ptr(a_scale), _ptr(b_data), _ptr(b_scale), fmt, M, N, K, layouts,
                                   _ptr(c_row32_data), _ptr(c_row32_scale), _ptr(c_col32_data), _ptr(c_col32_scale),
                                   _ptr(c_sq32_data), _ptr(c_sq32_scale), _ptr(c_f32), _stream(stream)),
            "mx_gemm_quantize")
@@ -274,10 +283,10 @@ def rmsnorm_quantize(x, gamma, eps=1e-6, layouts=ROW32 | COL32 | SQ32):
     return out
 
 
-def gemm_quantize(a, b, layouts=ROW32 | COL32 | SQ32, with_f32=False):
-    """C = A B^T from MX operands a = (data [M, K], scale [M, K/32]) and b = (data [N, K],
-    scale [N, K/32]); returns ({layout: (data [M, N], scale)}, C fp32 or None)."""
-    M, K = a[0].shape
+def gemm_quantize(a, b, layouts=ROW32 | COL32 | SQ32, with_f32=False, fmt=E4M3):
+    """C = A B^T from MX operands a = (data [M, K w/8], scale [M, K/32]) and b = (data [N, K w/8],
+    scale [N, K/32]) in element format fmt; returns ({layout: (data [M, N], scale)}, C fp32 or None)."""
+    M, K = a[0].shape[0], a[1].shape[1] * 32
     N = b[0].shape[0]
     dev = a[0].device
     shapes = {ROW32: (M, (N + 31) // 32), COL32: ((M + 31) // 32, N), SQ32: ((M + 31) // 32, (N + 31) // 32)}
@@ -286,9 +295,19 @@ def gemm_quantize(a, b, layouts=ROW32 | COL32 | SQ32, with_f32=False):
            for lay in (ROW32, COL32, SQ32) if layouts & lay}
     c32 = torch.empty((M, N), dtype=torch.float32, device=dev) if with_f32 else None
     g = lambda lay, i: out[lay][i] if lay in out else None  # noqa: E731
-    mx_gemm_quantize(a[0], a[1], b[0], b[1], M, N, K, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0), g(COL32, 1),
-                     g(SQ32, 0), g(SQ32, 1), c32)
+    mx_gemm_quantize(a[0], a[1], b[0], b[1], fmt, M, N, K, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0),
+                     g(COL32, 1), g(SQ32, 0), g(SQ32, 1), c32)
     return out, c32
+
+
+def quantize_rows(x, fmt=E4M3):
+    """MX quantization of a [rows, K] operand along K in element format fmt.
+    Returns (packed data [rows, K w/8], scales [rows, K/32])."""
+    rows, K = x.shape
+    data = torch.empty((rows, K * ELEM_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    mx_quantize_rows(x, rows, K, fmt, data, scale)
+    return data, scale
 
 
 def padded_scale_rows(seqlens) -> int:

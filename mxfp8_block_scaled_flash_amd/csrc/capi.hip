@@ -188,13 +188,28 @@ mx_status mx_rmsnorm_quantize_varlen(const void* x, mx_dtype x_dtype, const floa
                          stream);
 }
 
+static bool valid_elem(int f) { return f == MX_E4M3 || f == MX_E2M3 || f == MX_E3M2 || f == MX_E2M1; }
+
+mx_status mx_quantize_rows(const void* x, mx_dtype x_dtype, int rows, int K, mx_elem format, uint8_t* data,
+                           uint8_t* scale, hipStream_t stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0 || !valid_elem(format)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  if ((long)rows * K > kMaxElems) return MX_EINVAL;
+  if (rows == 0) return MX_OK;
+  if (!all_aligned({x, data}) || !scale) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_quantize_rows(x, x_dtype == MX_F32, rows, K, (int)format, data, scale, stream));
+}
+
 mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const uint8_t* b_data,
-                           const uint8_t* b_scale, int M, int N, int K, unsigned layouts, uint8_t* c_row32_data,
+                           const uint8_t* b_scale, mx_elem ab_format, int M, int N, int K, unsigned layouts,
+                           uint8_t* c_row32_data,
                            uint8_t* c_row32_scale, uint8_t* c_col32_data, uint8_t* c_col32_scale,
                            uint8_t* c_sq32_data, uint8_t* c_sq32_scale, float* c_f32, hipStream_t stream) {
   // K bounded so that a 128-row tile of an operand stays within 32-bit buffer offsets
   if (M < 0 || N < 0 || K < 64 || K > (1 << 20) || K % 64 != 0 || N % 16 != 0) return MX_EINVAL;
   if ((layouts & ~7u) != 0 || (layouts == 0 && !c_f32)) return MX_EINVAL;
+  if (!valid_elem(ab_format)) return MX_EINVAL;
   if ((long)M * K > kMaxElems || (long)N * K > kMaxElems || (long)M * N > kMaxElems) return MX_EINVAL;
   if ((long)M * N == 0) return MX_OK;
   if (!all_aligned({a_data, a_scale, b_data, b_scale})) return MX_EINVAL;
@@ -206,6 +221,7 @@ mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const 
   mxk::GemmArgs a{};
   a.a = a_data; a.as = a_scale; a.b = b_data; a.bs = b_scale;
   a.M = M; a.N = N; a.K = K;
+  a.fmt = (int)ab_format;
   a.tm = (M + 127) / 128;
   a.tn = (N + 127) / 128;
   a.layouts = layouts;

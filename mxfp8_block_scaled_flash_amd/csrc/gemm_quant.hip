@@ -1,7 +1,9 @@
-// MX GEMM with a quantizing epilogue: C = A B^T from E4M3 payloads with ROW32
-// (E8M0 per 32 along K) scales, fp32 accumulation in the block-scaled matrix
-// instruction, and C written as MXFP8 in any of ROW32 / COL32 / SQ32 (one
-// pass over the fp32 tile, several scale layouts), optionally also in fp32.
+// MX GEMM with a quantizing epilogue: C = A B^T from MX payloads (MXFP8 E4M3,
+// MXFP6 E2M3 / E3M2 or MXFP4 E2M1, the element formats of the block-scaled
+// matrix instruction) with ROW32 (E8M0 per 32 along K) scales, fp32
+// accumulation in that instruction, and C written as MXFP8 in any of ROW32 /
+// COL32 / SQ32 (one pass over the fp32 tile, several scale layouts),
+// optionally also in fp32.
 //
 // This is the "fused GEMM + Quantize" producer of "Low Precision Flash
 // Attention 4: End-to-End Block-Scaled Attention for Blackwell",
@@ -12,9 +14,14 @@
 //  * workgroup = 4 waves = one 128 x 128 tile of C; wave w holds the 64 x 64
 //    sub-tile (rows 64 (w/2), columns 64 (w%2)) as 2 x 2 accumulators of
 //    v_mfma_scale_f32_32x32x64_f8f6f4;
-//  * K advances 64 per step; A and B tiles (128 rows x 64 bytes) and their
-//    scale pairs are staged in two LDS buffers, the next step's buffer loads
-//    in flight while the current one is multiplied, one barrier per step;
+//  * K advances 64 per step; A and B tiles (128 rows x 8w bytes for w-bit
+//    elements) and their scale pairs are staged in two LDS buffers, the next
+//    step's buffer loads in flight while the current one is multiplied, one
+//    barrier per step;
+//  * operand layout (measured): for E4M3 a lane of half g supplies bytes
+//    16g..16g+15 and 32+16g..32+16g+15 of its row's 64 K values; for the 6-
+//    and 4-bit formats it supplies the whole K block g (K values 32g..32g+31)
+//    as a 24- or 16-byte little-endian bitstream, the packed row layout;
 //  * the operands are swapped (B rows as the instruction's A operand), so a
 //    lane ends with one row of C and 16 of its columns per 32 x 32 block:
 //    ROW32 maxima are in-lane plus one v_permlane32_swap, COL32 maxima are
@@ -59,16 +66,41 @@ MX_DEV uint32_t enc4(float y0, float y1, float y2, float y3, int sh0, int sh1, i
   return (uint32_t)r;
 }
 
-template <int OA, int OB>
+template <int FMT>
 MX_DEV v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
+}
+
+// bits per element of a matrix-instruction format code (0 E4M3, 2 E2M3, 3 E3M2, 4 E2M1)
+template <int FMT>
+constexpr int fmt_bits() { return FMT == 0 ? 8 : FMT == 4 ? 4 : 6; }
+
+// lane (n, g)'s operand from its row's 8w-byte K chunk in LDS
+template <int FMT>
+MX_DEV v8i load_operand(const uint8_t* row, int g) {
+  if constexpr (FMT == 0) {
+    return pack8g(*(const uint4*)(row + 16 * g), *(const uint4*)(row + 32 + 16 * g));
+  } else if constexpr (fmt_bits<FMT>() == 6) {
+    const uint2* p = (const uint2*)(row + 24 * g);
+    const uint2 a = p[0], b = p[1], c = p[2];
+    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+  } else {
+    const uint4 a = *(const uint4*)(row + 16 * g);
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  }
 }
 
 }  // namespace
 
+template <int FMT>
 __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
-  constexpr int BM = 128, BN = 128, BK = 64;
-  constexpr int KST = BK + 16;   // LDS row stride of the staged tiles
+  constexpr int BM = 128, BN = 128;
+  constexpr int W = fmt_bits<FMT>();
+  constexpr int RBK = 8 * W;                        // bytes of one row per 64-deep K step
+  constexpr int KST = RBK + (W == 6 ? 32 : 16);     // LDS row stride: 16-byte aligned, rows on distinct banks
+  constexpr int CPR = RBK / 16;                     // 16-byte chunks per row and step
+  constexpr int NCH = BM * CPR;                     // chunks per tile and step
+  constexpr int CPT = (NCH + 255) / 256;            // chunks per thread
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * KST];
   __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
@@ -83,24 +115,27 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
   if (tile >= ntiles) return;
   const int m0 = (tile / a.tn) * BM, n0 = (tile % a.tn) * BN;
   const int K = a.K, kb32 = K / 32;
+  const int rowb = K / 8 * W;   // bytes per packed row
 
   // ---- staging: 128 rows x 64 bytes of A and of B per step, 2 chunks of 16 bytes per thread each
   struct Stage {
-    uint4 av[2], bv[2];
+    uint4 av[CPT], bv[CPT];
     uint32_t as, bs;
   };
   const int rowsA = min(BM, a.M - m0), rowsB = min(BN, a.N - n0);
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.a + (long)m0 * K, (rowsA - 1) * K + K);
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.b + (long)n0 * K, (rowsB - 1) * K + K);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.a + (long)m0 * rowb, rowsA * rowb);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.b + (long)n0 * rowb, rowsB * rowb);
   const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(a.as + (long)m0 * kb32, rowsA * kb32);
   const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(a.bs + (long)n0 * kb32, rowsB * kb32);
   auto load = [&](int kt, Stage& st) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch = tid + 256 * c;   // 512 chunks: row ch / 4, 16-byte column ch % 4
-      const int off = (ch >> 2) * K + kt * BK + (ch & 3) * 16;
-      st.av[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-      st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + 256 * c;   // row ch / CPR, 16-byte column ch % CPR
+      if (NCH % 256 == 0 || ch < NCH) {
+        const int off = (ch / CPR) * rowb + kt * RBK + (ch % CPR) * 16;
+        st.av[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+        st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+      }
     }
     // thread t: scale pair of A row t (t < 128) or of B row t - 128
     const int r = tid & 127;
@@ -110,10 +145,12 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
   };
   auto store = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < CPT; ++c) {
       const int ch = tid + 256 * c;
-      *(uint4*)(&sA[buf][(ch >> 2) * KST + (ch & 3) * 16]) = st.av[c];
-      *(uint4*)(&sB[buf][(ch >> 2) * KST + (ch & 3) * 16]) = st.bv[c];
+      if (NCH % 256 == 0 || ch < NCH) {
+        *(uint4*)(&sA[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.av[c];
+        *(uint4*)(&sB[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.bv[c];
+      }
     }
     if (tid < 128) sAs[buf][tid] = st.as;
     else sBs[buf][tid - 128] = st.bs;
@@ -127,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
   const int wr = 64 * (w >> 1), wc = 64 * (w & 1);
-  const int nk = K / BK;
+  const int nk = K / 64;
   int sa_prev[2] = {0, 0}, sb_prev[2] = {0, 0};   // scale operands of the last products, pinned
 
   {
@@ -144,17 +181,15 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
     int sa[2], sb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint8_t* pa = sA[cur] + (wr + 32 * i + n) * KST + 16 * g;
-      ao[i] = pack8g(*(const uint4*)pa, *(const uint4*)(pa + 32));
+      ao[i] = load_operand<FMT>(sA[cur] + (wr + 32 * i + n) * KST, g);
       sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
-      const uint8_t* pb = sB[cur] + (wc + 32 * i + n) * KST + 16 * g;
-      bo[i] = pack8g(*(const uint4*)pb, *(const uint4*)(pb + 32));
+      bo[i] = load_operand<FMT>(sB[cur] + (wc + 32 * i + n) * KST, g);
       sb[i] = (int)(sBs[cur][wc + 32 * i + n] >> (8 * g));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<0, 0>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<FMT>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
     keep(sa_prev[0]); keep(sa_prev[1]); keep(sb_prev[0]); keep(sb_prev[1]);
     sa_prev[0] = sa[0]; sa_prev[1] = sa[1]; sb_prev[0] = sb[0]; sb_prev[1] = sb[1];
     store(cur ^ 1, nx);
@@ -258,7 +293,14 @@ hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st) {
   const long ntiles = (long)a.tm * a.tn;
   if (ntiles == 0) return hipSuccess;
   const long grid = (ntiles + 7) / 8 * 8;
-  gemm_quant_kernel<<<dim3((unsigned)grid), dim3(256), 0, st>>>(a);
+  dim3 g((unsigned)grid), b(256);
+  switch (a.fmt) {
+    case 0: gemm_quant_kernel<0><<<g, b, 0, st>>>(a); break;
+    case 2: gemm_quant_kernel<2><<<g, b, 0, st>>>(a); break;
+    case 3: gemm_quant_kernel<3><<<g, b, 0, st>>>(a); break;
+    case 4: gemm_quant_kernel<4><<<g, b, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

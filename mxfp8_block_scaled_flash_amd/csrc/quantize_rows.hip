@@ -1,0 +1,131 @@
+// MX quantization of GEMM operands in any element format of the block-scaled
+// matrix instruction: MXFP8 (E4M3), MXFP6 (E2M3, E3M2) and MXFP4 (E2M1),
+// blocks of 32 along each row (the contraction axis), payload packed as the
+// instruction reads it.  The pages name these formats beside MXFP8 ("Low
+// Precision Flash Attention 4: End-to-End Block-Scaled Attention for
+// Blackwell", paragraph on the block-scaled MMA instructions); the element
+// definitions are the OCP MX ones.
+//
+// One thread per 32-element block: the block's 64 (bf16) or 128 (fp32) bytes
+// are contiguous and neighbouring threads read neighbouring blocks.  The
+// scale is read off amax's exponent field; elements are scaled by an exact
+// power of two and encoded with integer arithmetic (round to nearest even,
+// saturating), so every code is the exactly rounded one.  Packing: element j
+// of a row at bits [w j, w j + w) of a little-endian bitstream (w = 8, 6, 4).
+#include "mx_common.h"
+#include "mx_launch.h"
+
+namespace mxk {
+
+namespace {
+
+// format: exponent bits, mantissa bits, bias, emax (exponent of the largest power of two), largest code
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<0> { static constexpr int EB = 4, MB = 3, BIAS = 7, EMAX = 8, W = 8; static constexpr uint32_t TOP = 0x7E; static constexpr float MAXV = 448.f; };
+template <>
+struct Fmt<2> { static constexpr int EB = 2, MB = 3, BIAS = 1, EMAX = 2, W = 6; static constexpr uint32_t TOP = 0x1F; static constexpr float MAXV = 7.5f; };
+template <>
+struct Fmt<3> { static constexpr int EB = 3, MB = 2, BIAS = 3, EMAX = 4, W = 6; static constexpr uint32_t TOP = 0x1F; static constexpr float MAXV = 28.f; };
+template <>
+struct Fmt<4> { static constexpr int EB = 2, MB = 1, BIAS = 1, EMAX = 2, W = 4; static constexpr uint32_t TOP = 0x7; static constexpr float MAXV = 6.f; };
+
+// y already scaled into the format's range (exactly); returns the element code
+template <int FMT>
+MX_DEV uint32_t encode(float y) {
+  using F = Fmt<FMT>;
+  const float a = fabsf(y);
+  const uint32_t sign = (__float_as_uint(y) >> 31) << (F::EB + F::MB);
+  // binade of a, floored at the subnormal binade (fp32 zero/subnormal inputs give -127: floored too)
+  int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
+  e = max(e, 1 - F::BIAS);
+  float r = rintf(ldexpf(a, F::MB - e));   // a / spacing, round to nearest even (exact scaling)
+  if (r >= (float)(2 << F::MB)) {          // carry into the next binade
+    e += 1;
+    r = (float)(1 << F::MB);
+  }
+  const int ri = (int)r;
+  const bool sub = ri < (1 << F::MB);
+  const uint32_t E = sub ? 0u : (uint32_t)(e + F::BIAS);
+  const uint32_t M = sub ? (uint32_t)ri : (uint32_t)(ri - (1 << F::MB));
+  uint32_t code = (E << F::MB) | M;
+  if (a > F::MAXV || E > (uint32_t)((1 << F::EB) - 1)) code = F::TOP;
+  return code | sign;
+}
+
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, long nblk, uint8_t* __restrict__ data,
+                                                            uint8_t* __restrict__ scale) {
+  using F = Fmt<FMT>;
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;   // block index = row * (K/32) + block in row
+  if (b >= nblk) return;
+  float v[32];
+  if constexpr (sizeof(T) == 2) {
+    const uint4* p = (const uint4*)(x + b * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 u = p[c];
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = bf16_lo(w4[i]);
+        v[8 * c + 2 * i + 1] = bf16_hi(w4[i]);
+      }
+    }
+  } else {
+    const float4* p = (const float4*)(x + b * 32);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float4 f = p[c];
+      v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // E8M0 = clamp(floor(log2 amax) - EMAX + 127, 0, 254); zero and fp32-subnormal amax give 0
+  const int ea = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  const int k = ea == 0 ? 0 : min(max(ea - F::EMAX, 0), 254);
+  const int sh = 127 - k;
+  uint32_t out[F::W] = {};   // 32 codes x W bits = W dwords
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = encode<FMT>(ldexpf(v[i], sh));
+    const int pos = F::W * i, wd = pos >> 5, bit = pos & 31;
+    out[wd] |= c << bit;
+    if (bit + F::W > 32) out[wd + 1] |= c >> (32 - bit);
+  }
+  uint32_t* dst = (uint32_t*)(data + b * (4 * F::W));
+  if constexpr (F::W == 8) {
+    ((uint4*)dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    ((uint4*)dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  } else if constexpr (F::W == 6) {
+    ((uint2*)dst)[0] = make_uint2(out[0], out[1]);
+    ((uint2*)dst)[1] = make_uint2(out[2], out[3]);
+    ((uint2*)dst)[2] = make_uint2(out[4], out[5]);
+  } else {
+    ((uint4*)dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  scale[b] = (uint8_t)k;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int fmt, uint8_t* data, uint8_t* scale,
+                                hipStream_t st) {
+  const long nblk = rows * (K / 32);
+  if (nblk == 0) return hipSuccess;
+  dim3 g((unsigned)((nblk + 255) / 256)), b(256);
+#define MX_QR_CASE(F)                                                                                     \
+  if (fmt == F) {                                                                                         \
+    if (fp32) quantize_rows_kernel<float, F><<<g, b, 0, st>>>((const float*)x, nblk, data, scale);        \
+    else quantize_rows_kernel<uint16_t, F><<<g, b, 0, st>>>((const uint16_t*)x, nblk, data, scale);       \
+    return hipGetLastError();                                                                             \
+  }
+  MX_QR_CASE(0) MX_QR_CASE(2) MX_QR_CASE(3) MX_QR_CASE(4)
+#undef MX_QR_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mxk

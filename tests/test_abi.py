@@ -103,16 +103,17 @@ def test_rmsnorm_quantize_rejects_invalid_shapes():
 
 
 def _gemm(**kw):
-    a = dict(a=16, as_=16, b=16, bs=16, M=64, N=64, K=64, lay=mx.ROW32, rd=16, rs=16, cd=None, cs=None, sd=None,
-             ss=None, c32=None)
+    a = dict(a=16, as_=16, b=16, bs=16, fmt=mx.E4M3, M=64, N=64, K=64, lay=mx.ROW32, rd=16, rs=16, cd=None, cs=None,
+             sd=None, ss=None, c32=None)
     a.update(kw)
-    return mx.lib().mx_gemm_quantize(a["a"], a["as_"], a["b"], a["bs"], a["M"], a["N"], a["K"], a["lay"], a["rd"],
+    return mx.lib().mx_gemm_quantize(a["a"], a["as_"], a["b"], a["bs"], a["fmt"], a["M"], a["N"], a["K"], a["lay"],
+                                     a["rd"],
                                      a["rs"], a["cd"], a["cs"], a["sd"], a["ss"], a["c32"], None)
 
 
 @pytest.mark.parametrize("bad", [dict(K=32), dict(K=0), dict(K=96), dict(N=40), dict(M=-1), dict(N=-16),
                                  dict(lay=8), dict(lay=0), dict(a=None), dict(bs=24), dict(rd=None),
-                                 dict(lay=mx.COL32), dict(c32=20), dict(K=(1 << 20) + 64)])
+                                 dict(lay=mx.COL32), dict(c32=20), dict(K=(1 << 20) + 64), dict(fmt=1), dict(fmt=5)])
 def test_gemm_quantize_rejects_invalid_arguments(bad):
     assert _gemm(**bad) == EINVAL
 
@@ -157,6 +158,20 @@ def test_bf16_backward_validation():
     assert call(a0=None) == EINVAL and call(a5=24) == EINVAL
     assert call(a16=None) == 4 and call(a17=L.mx_attn_bwd_bf16_workspace_bytes(64, 1) - 1) == 4
     assert call(a6=0) == 0
+
+
+def test_quantize_rows_validation():
+    L = mx.lib()
+    ok = dict(x=16, dt=mx.BF16, rows=4, K=64, fmt=mx.E2M1, d=16, s=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mx_quantize_rows(a["x"], a["dt"], a["rows"], a["K"], a["fmt"], a["d"], a["s"], None)
+    for bad in (dict(K=48), dict(K=0), dict(rows=-1), dict(fmt=1), dict(fmt=7), dict(dt=mx.F16), dict(x=None),
+                dict(d=24), dict(s=None)):
+        assert call(**bad) == EINVAL, bad
+    assert call(rows=0) == 0
 
 
 def test_workspace_size():

@@ -116,11 +116,11 @@ def test_gemm_quantize_rejects_bad_arguments():
     c = torch.zeros(64, 64, dtype=torch.uint8, device="cuda")
     cs = torch.zeros(64, 2, dtype=torch.uint8, device="cuda")
     with pytest.raises(mx.MXError):   # K not a multiple of 64
-        mx.mx_gemm_quantize(a, s, a, s, 64, 64, 32, mx.ROW32, c, cs, None, None, None, None, None)
+        mx.mx_gemm_quantize(a, s, a, s, mx.E4M3, 64, 64, 32, mx.ROW32, c, cs, None, None, None, None, None)
     with pytest.raises(mx.MXError):   # N not a multiple of 16
-        mx.mx_gemm_quantize(a, s, a, s, 64, 40, 64, mx.ROW32, c, cs, None, None, None, None, None)
+        mx.mx_gemm_quantize(a, s, a, s, mx.E4M3, 64, 40, 64, mx.ROW32, c, cs, None, None, None, None, None)
     with pytest.raises(mx.MXError):   # nothing to write
-        mx.mx_gemm_quantize(a, s, a, s, 64, 64, 64, 0, None, None, None, None, None, None, None)
+        mx.mx_gemm_quantize(a, s, a, s, mx.E4M3, 64, 64, 64, 0, None, None, None, None, None, None, None)
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 144, 192), (130, 272, 320), (37, 48, 128), (33, 16, 64)])
@@ -136,7 +136,7 @@ def test_gemm_quantize_writes_only_its_outputs(M, N, K):
     bufs = [torch.full((G + s + G,), 0xA5, dtype=torch.uint8, device="cuda") for s in sizes]
     views = [b[G:G + s] for b, s in zip(bufs, sizes)]
     cbuf = torch.full((G + M * N + G,), -7.0, dtype=torch.float32, device="cuda")
-    mx.mx_gemm_quantize(t(ac), t(ak), t(bc), t(bk), M, N, K, ALL, *views, cbuf[G:G + M * N])
+    mx.mx_gemm_quantize(t(ac), t(ak), t(bc), t(bk), mx.E4M3, M, N, K, ALL, *views, cbuf[G:G + M * N])
     torch.cuda.synchronize()
     for b, s in zip(bufs, sizes):
         h = to_np(b)

@@ -1,0 +1,119 @@
+"""GPU parity of the MXFP6 / MXFP4 payload path: the operand quantizer
+(mx_quantize_rows) must give the oracle's packed bytes and scales exactly in
+every element format, and the MX GEMM must accept every format through the
+matrix instruction's format fields: C within the instruction's truncation
+bound of the exact sum of the dequantized products, and the MXFP8 codes of
+C equal to the oracle quantizer applied to the kernel's own C."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_flash_amd as mx
+from oracle import gemm as gm
+from oracle import mx as omx
+from oracle import mxsmall as ms
+
+from mxtest import log, to_np
+
+pytestmark = pytest.mark.gpu
+FMTS = {mx.E4M3: "e4m3", mx.E2M3: "e2m3", mx.E3M2: "e3m2", mx.E2M1: "e2m1"}
+
+
+def _oracle_rows(x, fmt):
+    """(packed bytes, scales, dequantized values, element exponents) of x [rows, K]."""
+    if fmt == mx.E4M3:
+        c, k = omx.quantize_row32(x)
+        return c, k, omx.dequantize_row32(c, k), omx.element_exponent_row32(c, k)
+    name = FMTS[fmt]
+    c, k = ms.quantize_rows(x, name)
+    return ms.pack(c, name), k, ms.dequantize_rows(c, k, name), ms.element_exponent_rows(c, k, name)
+
+
+def _data(rows, K, seed, spread=3.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, K)) * np.exp(rng.standard_normal((rows, 1)) * spread)
+    x[0] = 0.0                                     # an all-zero row
+    x[1, :32] = np.linspace(-7.5, 7.5, 32)         # a block holding every sixteenth-step
+    x[2] = rng.standard_normal(K) * 1e-30          # tiny values (scale clamps at 0)
+    x[3, ::7] = 1e4                                # large values next to small ones
+    return x
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_rows_matches_the_oracle_bit_for_bit(fmt, dtype):
+    rows, K = 300, 256
+    xt = torch.from_numpy(_data(rows, K, 1 + fmt)).to(dtype)
+    x = xt.double().numpy()
+    # exact ties of the format's grid, scaled into a block whose max fixes the scale
+    if fmt != mx.E4M3:
+        name = FMTS[fmt]
+        v = ms.decode(np.arange(2 ** (ms.BITS[name] - 1)), name)
+        mids = (v[1:] + v[:-1]) / 2
+        row = np.zeros(K)
+        row[0] = ms.max_value(name)
+        row[1:1 + len(mids[:31])] = mids[:31]
+        x[5] = row
+        xt = torch.from_numpy(x).to(dtype)
+        x = xt.double().numpy()
+    d, s = mx.quantize_rows(xt.cuda(), fmt)
+    torch.cuda.synchronize()
+    rd, rs, _, _ = _oracle_rows(x, fmt)
+    gd, gs = to_np(d), to_np(s)
+    assert gd.shape == rd.shape and gs.shape == rs.shape
+    nd, ns = int(np.sum(gd != rd)), int(np.sum(gs != rs))
+    if nd:
+        idx = np.argwhere(gd != rd)[:6]
+        log(f"{FMTS[fmt]} mismatches at {idx.tolist()}: gpu {[int(gd[tuple(i)]) for i in idx]} "
+            f"oracle {[int(rd[tuple(i)]) for i in idx]}")
+    assert nd == 0 and ns == 0, f"{FMTS[fmt]} {dtype}: {nd} byte and {ns} scale mismatches"
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
+@pytest.mark.parametrize("M,N,K", [(200, 144, 192), (128, 256, 512), (37, 48, 64)])
+def test_gemm_in_every_element_format(fmt, M, N, K):
+    a = _data(M, K, 10 + fmt, spread=2.0)
+    b = _data(N, K, 20 + fmt, spread=2.0)
+    ad, ak, av, ae = _oracle_rows(a, fmt)
+    bd, bk, bv, be = _oracle_rows(b, fmt)
+    t = lambda z: torch.from_numpy(np.ascontiguousarray(z).astype(np.uint8)).cuda()  # noqa: E731
+    out, c = mx.gemm_quantize((t(ad), t(ak)), (t(bd), t(bk)), mx.ROW32 | mx.COL32 | mx.SQ32, with_f32=True,
+                              fmt=fmt)
+    torch.cuda.synchronize()
+    c = c.double().cpu().numpy()
+    exact = av @ bv.T
+    bound = 2.0 ** -8 * (np.abs(av) @ np.abs(bv).T) + 1e-30
+    assert np.all(np.abs(c - exact) <= bound), (FMTS[fmt], float(np.max(np.abs(c - exact) / bound)))
+    model = gm.matmul_mfma(av, ae, bv, be)
+    eq = float(np.mean(c == model))
+    log(f"gemm {FMTS[fmt]} {M}x{N}x{K}: {100 * eq:.1f}% of C bit-equal to the accumulation model, "
+        f"{100 * float(np.mean(c == exact.astype(np.float32))):.1f}% to fl32(exact)")
+    ulp = np.spacing(np.abs(model).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(c - model) <= 8 * ulp + 1e-30) and eq >= 0.9, (FMTS[fmt], eq)
+    ref = {mx.ROW32: omx.quantize_col32(c, axis=1), mx.COL32: omx.quantize_col32(c, axis=0),
+           mx.SQ32: omx.quantize_sq32(c, 0)}
+    for lay, (dd, ss) in out.items():
+        assert np.array_equal(to_np(dd), ref[lay][0]) and np.array_equal(to_np(ss), ref[lay][1]), (FMTS[fmt], lay)
+
+
+def test_gemm_from_the_gpu_quantizer_end_to_end():
+    """Operands produced by mx_quantize_rows (bf16 input) feed the GEMM directly."""
+    M, N, K = 256, 128, 1024
+    g = torch.Generator().manual_seed(3)
+    a = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    b = torch.randn(N, K, generator=g).to(torch.bfloat16)
+    for fmt in FMTS:
+        qa, qb = mx.quantize_rows(a.cuda(), fmt), mx.quantize_rows(b.cuda(), fmt)
+        _, c = mx.gemm_quantize(qa, qb, 0, with_f32=True, fmt=fmt)
+        torch.cuda.synchronize()
+        _, _, av, _ = _oracle_rows(a.double().numpy(), fmt)
+        _, _, bv, _ = _oracle_rows(b.double().numpy(), fmt)
+        exact = av @ bv.T
+        bound = 2.0 ** -8 * (np.abs(av) @ np.abs(bv).T) + 1e-30
+        err = np.abs(c.double().cpu().numpy() - exact)
+        assert np.all(err <= bound), FMTS[fmt]
+        # the quantized product approximates the bf16 product (looser for fewer bits)
+        full = a.double().numpy() @ b.double().numpy().T
+        rel = float(np.linalg.norm(c.double().cpu().numpy() - full) / np.linalg.norm(full))
+        log(f"end to end {FMTS[fmt]}: rel Frobenius error vs the unquantized product {rel:.3e}")
+        assert rel < {mx.E4M3: 0.05, mx.E2M3: 0.1, mx.E3M2: 0.2, mx.E2M1: 0.4}[fmt]
