@@ -34,7 +34,30 @@ def parse():
     ap.add_argument("--workload", default="llm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="time only quantize + forward")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="for HBM counters: one 1 GiB device copy (calibration), then one mx_attn_bwd call")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mxfp8_attn_bwd_llm_hbm_traffic.txt")
+BWD_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_flash_amd", "csrc", "attn_bwd.hip")
+
+
+def source_digest(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per mx_attn_bwd call from the committed counter summary, or None when the
+    backward's source has changed since the counters were taken."""
+    try:
+        kv = dict(line[2:].split("=", 1) for line in open(TRAFFIC_FILE) if line.startswith("# ") and "=" in line)
+    except OSError:
+        return None
+    if kv.get("source_sha256_16", "").strip() != source_digest(BWD_SOURCE):
+        return None
+    return float(kv["bytes_per_call"])
 
 
 def cpu_baseline(w, sigma):
@@ -80,6 +103,11 @@ def main():
 
     w = synth.workload(args.workload)
     dev = "cuda"
+    if args.traffic_run:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     if not args.no_bwd and mx.mx_attn_bwd_workspace_bytes(1, 1, 128) and not _bwd_available(mx):
         print("note: this build's mx_attn_bwd is not available; timing quantize + forward only", file=sys.stderr)
         args.no_bwd = True
@@ -129,6 +157,14 @@ def main():
         if rec is not None:
             rec.append(e)
 
+    if args.traffic_run:
+        quantize_all()
+        forward()
+        if do_bwd:
+            backward()
+        torch.cuda.synchronize()
+        print("traffic run done", flush=True)
+        return
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
@@ -302,7 +338,7 @@ def main():
         "bwd_ms": round(b_ms, 4) if do_bwd else None,
         "roofline": {"bound": "mfma", "kernel": dom["kernel"], "achieved": round(achieved, 2),
                      "peak": MXFP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MXFP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic() if do_bwd else None},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, sigma)
