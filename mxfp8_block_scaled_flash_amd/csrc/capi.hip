@@ -222,8 +222,6 @@ mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const 
   a.a = a_data; a.as = a_scale; a.b = b_data; a.bs = b_scale;
   a.M = M; a.N = N; a.K = K;
   a.fmt = (int)ab_format;
-  a.tm = (M + 127) / 128;
-  a.tn = (N + 127) / 128;
   a.layouts = layouts;
   a.row_data = c_row32_data; a.row_scale = c_row32_scale;
   a.col_data = c_col32_data; a.col_scale = c_col32_scale;

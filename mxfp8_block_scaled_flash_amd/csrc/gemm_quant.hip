@@ -11,9 +11,14 @@
 // e.g. for the projections that feed the attention operands).
 //
 // gfx950 design:
-//  * workgroup = 4 waves = one 128 x 128 tile of C; wave w holds the 64 x 64
-//    sub-tile (rows 64 (w/2), columns 64 (w%2)) as 2 x 2 accumulators of
-//    v_mfma_scale_f32_32x32x64_f8f6f4;
+//  * workgroup = 4 waves = one 256 x 256 tile of C; wave w holds the 128 x 128
+//    sub-tile (rows 128 (w/2), columns 128 (w%2)) as 4 x 4 accumulators of
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (in AGPRs: one wave per SIMD, up to
+//    512 registers), so 8 operand reads from LDS feed 16 products per
+//    64-deep step and barrier;
+//  * tiles in a grouped order (runs of 8 tile-rows walked column by column),
+//    each XCD (blockIdx % 8) taking a contiguous run of them, so the
+//    workgroups in flight on an XCD share A rows and B rows in its L2;
 //  * K advances 64 per step; A and B tiles (128 rows x 8w bytes for w-bit
 //    elements) and their scale pairs are staged in two LDS buffers, the next
 //    step's buffer loads in flight while the current one is multiplied, one
@@ -30,8 +35,14 @@
 //    consecutive bytes of its row;
 //  * encoding as in the quantizer: exact power-of-two ldexp, clamp to +-448,
 //    round-to-nearest-even fp8 convert.
+#include <type_traits>
+
 #include "mx_common.h"
 #include "mx_launch.h"
+
+#ifndef GEMM_WT
+#define GEMM_WT 4
+#endif
 
 namespace mxk {
 
@@ -71,6 +82,15 @@ MX_DEV v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled at compile time
+template <int N, typename F>
+MX_DEV void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 // bits per element of a matrix-instruction format code (0 E4M3, 2 E2M3, 3 E3M2, 4 E2M1)
 template <int FMT>
 constexpr int fmt_bits() { return FMT == 0 ? 8 : FMT == 4 ? 4 : 6; }
@@ -93,31 +113,35 @@ MX_DEV v8i load_operand(const uint8_t* row, int g) {
 }  // namespace
 
 template <int FMT>
-__global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
-  constexpr int BM = 128, BN = 128;
+__global__ __launch_bounds__(256, 1) void gemm_quant_kernel(GemmArgs a) {
+  constexpr int WT = GEMM_WT;        // 32 x 32 blocks per wave side
+  constexpr int BM = 64 * WT, BN = 64 * WT;
   constexpr int W = fmt_bits<FMT>();
   constexpr int RBK = 8 * W;                        // bytes of one row per 64-deep K step
   constexpr int KST = RBK + (W == 6 ? 32 : 16);     // LDS row stride: 16-byte aligned, rows on distinct banks
   constexpr int CPR = RBK / 16;                     // 16-byte chunks per row and step
   constexpr int NCH = BM * CPR;                     // chunks per tile and step
   constexpr int CPT = (NCH + 255) / 256;            // chunks per thread
+  static_assert(BM <= 256, "one scale row per thread");
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * KST];
   __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // tiles in row-major order, split into 8 contiguous runs, one per XCD (blockIdx % 8), so
-  // neighbouring tiles that share rows of A run on the same XCD
   const int ntiles = a.tm * a.tn;
   const int per = (ntiles + 7) / 8;
   const int tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3));
   if (tile >= ntiles) return;
-  const int m0 = (tile / a.tn) * BM, n0 = (tile % a.tn) * BN;
+  constexpr int GM = 8;   // tile-rows per group
+  const int grp = tile / (GM * a.tn), first_m = grp * GM, gm = min(a.tm - first_m, GM);
+  const int in_grp = tile - grp * GM * a.tn;
+  const int m0 = (first_m + in_grp % gm) * BM, n0 = (in_grp / gm) * BN;
   const int K = a.K, kb32 = K / 32;
   const int rowb = K / 8 * W;   // bytes per packed row
+  const int nk = K / 64;
 
-  // ---- staging: 128 rows x 64 bytes of A and of B per step, 2 chunks of 16 bytes per thread each
+  // ---- staging: BM rows x 8w bytes of A and of B per step, in 16-byte chunks
   struct Stage {
     uint4 av[CPT], bv[CPT];
     uint32_t as, bs;
@@ -137,11 +161,11 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
         st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
       }
     }
-    // thread t: scale pair of A row t (t < 128) or of B row t - 128
-    const int r = tid & 127;
-    const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(tid < 128 ? ras : rbs, r * kb32 + 2 * kt, 0, 0);
-    st.as = s;
-    st.bs = s;
+    // thread t: scale pairs of A row t and B row t (rows past BM: a duplicate, not stored)
+    const int r = tid % BM;
+    // one 16-bit load per row (K/32 is even, so a row's scale pair is 2-byte aligned)
+    st.as = __builtin_amdgcn_raw_buffer_load_b16(ras, r * kb32 + 2 * kt, 0, 0);
+    st.bs = __builtin_amdgcn_raw_buffer_load_b16(rbs, r * kb32 + 2 * kt, 0, 0);
   };
   auto store = [&](int buf, const Stage& st) {
 #pragma unroll
@@ -152,21 +176,47 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
         *(uint4*)(&sB[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.bv[c];
       }
     }
-    if (tid < 128) sAs[buf][tid] = st.as;
-    else sBs[buf][tid - 128] = st.bs;
+    if (tid < BM) {
+      sAs[buf][tid] = st.as;
+      sBs[buf][tid] = st.bs;
+    }
   };
 
-  // acc[i][j]: C block (rows m0 + 64 (w/2) + 32 i, columns n0 + 64 (w%2) + 32 j); element e of
+  // acc[i][j]: C block (rows m0 + wr + 32 i, columns n0 + wc + 32 j); element e of
   // lane (n, g) = row + n, column + 8(e/4) + 4g + e%4
-  v16f acc[2][2];
+  v16f acc[WT][WT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
-  const int wr = 64 * (w >> 1), wc = 64 * (w & 1);
-  const int nk = K / 64;
-  int sa_prev[2] = {0, 0}, sb_prev[2] = {0, 0};   // scale operands of the last products, pinned
+    for (int j = 0; j < WT; ++j) acc[i][j] = v16f{};
+  const int wr = 32 * WT * (w >> 1), wc = 32 * WT * (w & 1);
+  int sa_prev[WT], sb_prev[WT];   // scale operands of the last products, pinned
+#pragma unroll
+  for (int i = 0; i < WT; ++i) sa_prev[i] = sb_prev[i] = 0;
 
+  // one 64-deep step from LDS buffer cur: operands, then the WT x WT products
+  auto compute = [&](const int cur) __attribute__((always_inline)) {
+    v8i ao[WT], bo[WT];
+    int sa[WT], sb[WT];
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+      ao[i] = load_operand<FMT>(sA[cur] + (wr + 32 * i + n) * KST, g);
+      sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
+      bo[i] = load_operand<FMT>(sB[cur] + (wc + 32 * i + n) * KST, g);
+      sb[i] = (int)(sBs[cur][wc + 32 * i + n] >> (8 * g));
+    }
+#pragma unroll
+    for (int i = 0; i < WT; ++i)
+#pragma unroll
+      for (int j = 0; j < WT; ++j) acc[i][j] = mfma<FMT>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+      keep(sa_prev[i]);
+      keep(sb_prev[i]);
+      sa_prev[i] = sa[i];
+      sb_prev[i] = sb[i];
+    }
+  };
   {
     Stage s0;
     load(0, s0);
@@ -177,34 +227,22 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
     const int cur = kt & 1;
     Stage nx;
     load(min(kt + 1, nk - 1), nx);   // past the last step the last one is fetched again
-    v8i ao[2], bo[2];
-    int sa[2], sb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ao[i] = load_operand<FMT>(sA[cur] + (wr + 32 * i + n) * KST, g);
-      sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
-      bo[i] = load_operand<FMT>(sB[cur] + (wc + 32 * i + n) * KST, g);
-      sb[i] = (int)(sBs[cur][wc + 32 * i + n] >> (8 * g));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma<FMT>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
-    keep(sa_prev[0]); keep(sa_prev[1]); keep(sb_prev[0]); keep(sb_prev[1]);
-    sa_prev[0] = sa[0]; sa_prev[1] = sa[1]; sb_prev[0] = sb[0]; sb_prev[1] = sb[1];
+    compute(cur);
     store(cur ^ 1, nx);
     __syncthreads();
   }
-  keep(acc[1][1][0]);
-  keep(sa_prev[0]); keep(sa_prev[1]); keep(sb_prev[0]); keep(sb_prev[1]);
+  keep(acc[WT - 1][WT - 1][0]);
+#pragma unroll
+  for (int i = 0; i < WT; ++i) {
+    keep(sa_prev[i]);
+    keep(sb_prev[i]);
+  }
 
   // ---- epilogue, per 32 x 32 block
   const long ldc = a.N;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const v16f& c = acc[i][j];
+  // one 32 x 32 block (i, j); every call site indexes acc with constants, so the accumulators
+  // stay in registers (a loop over dynamic indices would put the array in scratch memory)
+  auto block = [&](const v16f& c, const int i, const int j) __attribute__((always_inline)) {
       const int row = m0 + wr + 32 * i + n;      // this lane's row
       const int col0 = n0 + wc + 32 * j;         // first column of the block
       const bool row_ok = row < a.M;
@@ -286,10 +324,14 @@ __global__ __launch_bounds__(256, 2) void gemm_quant_kernel(GemmArgs a) {
         if (lane == 0 && m0 + wr + 32 * i < a.M && col0 < a.N)
           a.sq_scale[(long)((m0 + wr + 32 * i) / 32) * nbn + col0 / 32] = (uint8_t)k;
       }
-    }
+  };
+  static_for<WT>([&](auto I) { static_for<WT>([&](auto J) { block(acc[I][J], I, J); }); });
 }
 
-hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm_quantize(GemmArgs a, hipStream_t st) {
+  constexpr int TILE = 64 * GEMM_WT;
+  a.tm = (a.M + TILE - 1) / TILE;
+  a.tn = (a.N + TILE - 1) / TILE;
   const long ntiles = (long)a.tm * a.tn;
   if (ntiles == 0) return hipSuccess;
   const long grid = (ntiles + 7) / 8 * 8;

@@ -34,7 +34,7 @@ struct GemmArgs {
   const uint8_t *a, *as, *b, *bs;   // A [M, K], B [N, K] packed payloads; ROW32 scales [M, K/32], [N, K/32]
   int M, N, K;
   int fmt;                          // element format of A and B (matrix-instruction code: 0, 2, 3, 4)
-  int tm, tn;                       // tiles along M and N
+  int tm, tn;                       // tiles along M and N (set by the launcher)
   unsigned layouts;                 // output layouts of C = A B^T
   uint8_t *row_data, *row_scale, *col_data, *col_scale, *sq_data, *sq_scale;
   float* c32;                       // optional fp32 copy of C [M, N]
@@ -69,6 +69,6 @@ hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st);
 hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int fmt, uint8_t* data, uint8_t* scale,
                                 hipStream_t st);
-hipError_t launch_gemm_quantize(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_quantize(GemmArgs a, hipStream_t st);
 
 }  // namespace mxk
