@@ -12,12 +12,14 @@
 // reduction over 128-key tiles would move about four times the atomic
 // traffic that bounds the MXFP8 backward.  So dQ is not reduced with atomics:
 //  1. bwd_pre_kernel (shared with the MXFP8 path): D_i.
-//  2. dkdv kernel, key-stationary: a workgroup of 4 waves owns 128 keys, each
-//     wave 32 keys whose K and V rows stay in registers; it walks 64-query
-//     steps (Q, dO, LSE, D double-buffered in LDS), computes S = Q K^T and
-//     dP = dO V^T with keys as the output columns (a lane owns one key), and
-//     accumulates dV^T += dO^T P and dK^T += Q^T dS in registers, the
-//     transposed Q and dO operands read with ds_read_b64_tr_b16.
+//  2. dkdv kernel, key-stationary: a workgroup of 8 waves (two per SIMD) owns
+//     128 keys held in LDS; wave w takes key block w % 4 and query block
+//     w / 4 of every 64-query step (Q, dO, LSE, D double-buffered in LDS),
+//     computes S = Q K^T and dP = dO V^T with keys as the output columns (a
+//     lane owns one key), and accumulates dV^T += dO^T P and dK^T += Q^T dS
+//     in registers, the transposed Q and dO operands read with
+//     ds_read_b64_tr_b16; the two waves of a key block add their partials
+//     through LDS at the end.
 //  3. dq kernel, query-stationary (the forward's skeleton): a wave owns 32
 //     queries with Q and dO resident, walks 64-key tiles of K and V staged in
 //     LDS, recomputes S^T and dP^T, and accumulates dQ^T += K^T dS^T in
@@ -87,32 +89,38 @@ MX_DEV void store4(void* base, long off, bool f32, float v0, float v1, float v2,
   }
 }
 
-template <int D>
-struct Step16 {
-  static constexpr int CH = 64 * 2 * D / 16 / 256;   // 16-byte chunks per thread per tensor
-  uint4 q[CH], d[CH];
-  float lse2;   // fl32(LSE log2 e) of query lane (threads 0..63) or D (threads 64..127)
-};
-
 }  // namespace
 
 // ------------------------------------------------------------- dK, dV
+// 8 waves per workgroup of 128 keys (two per SIMD): wave w owns key block w % 4 for query block
+// w / 4 of every 64-query step, so the two waves of a key block split each step's queries and
+// add their partial dK, dV through LDS at the end.  K, V (the workgroup's 128 rows) and the
+// step's Q, dO, LSE, D sit in LDS.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
-  constexpr int BN = 128;       // keys per workgroup (4 waves x 32)
-  constexpr int BQ = 64;        // queries per step
+__global__ __launch_bounds__(512, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int BN = 128;       // keys per workgroup (4 key blocks of 32)
+  constexpr int BQ = 64;        // queries per step (2 query blocks of 32)
   constexpr int NK = D / 16;    // 16-feature steps of the S and dP contractions
   constexpr int ND = D / 32;    // 32-feature chunks of dK, dV
   constexpr int RB = 2 * D;     // bytes per token row of one head
   constexpr int RS = RB + 32;   // LDS row stride
   constexpr int CPR = RB / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * RS];
-  __shared__ __attribute__((aligned(16))) uint8_t sO[2][BQ * RS];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];          // fl32(LSE log2 e)
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];          // D_i
+  constexpr int NT = NW * 64;
+  constexpr int TILE_K = BN * RS, TILE_Q = BQ * RS;
+  constexpr int SMEM = 2 * TILE_K + 4 * TILE_Q;   // K, V, Q[2], dO[2]; reused for the final reduction
+  static_assert(SMEM >= 4 * 2 * ND * 16 * 64 * 4, "the partial dK, dV of four waves fit in the tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];   // fl32(LSE log2 e)
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];   // D_i
+  uint8_t* const sK = smem;
+  uint8_t* const sV = smem + TILE_K;
+  uint8_t* const sQ0 = smem + 2 * TILE_K;   // sQ[buf] = sQ0 + buf * TILE_Q
+  uint8_t* const sO0 = smem + 2 * TILE_K + 2 * TILE_Q;
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = w & 3, qb = w >> 2;
   const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
   const int u = (j / a.nkt) * 8 + xcd;
   if (u >= a.nseq * a.H) return;
@@ -124,60 +132,62 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
   L = __builtin_amdgcn_readfirstlane(L);
   const int k0 = kt * BN;
   if (k0 >= L) return;
-  const int kw0 = k0 + 32 * w;   // this wave's first key
+  const int kw0 = k0 + 32 * kb;   // this wave's first key
   const int key = kw0 + n;
   const long rowH = (long)a.H * D;
   const uint16_t *gq = (const uint16_t*)a.q, *gk = (const uint16_t*)a.k, *gv = (const uint16_t*)a.v;
   const uint16_t* gd = (const uint16_t*)a.dout;
 
-  // own K and V rows: second operands of S = Q K^T and dP = dO V^T (lane (n, g): features 16k + 8g..)
-  uint4 kr[NK], vr[NK];
-  if (key < L) {
-    const long off = (long)(tok0 + key) * rowH + (long)h * D + 8 * g;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      kr[k] = *(const uint4*)(gk + off + 16 * k);
-      vr[k] = *(const uint4*)(gv + off + 16 * k);
+  // ---- K and V rows of the workgroup (zero past the end)
+  {
+    const int rows = min(BN, L - k0);
+    const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
+    const int nrec = ((rows - 1) * (int)rowH + D) * 2;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(gk + tb, nrec), rv = buffer_rsrc(gv + tb, nrec);
+    for (int ch = tid; ch < BN * CPR; ch += NT) {
+      const int off = (ch / CPR) * (int)rowH * 2 + (ch % CPR) * 16;
+      const uint4 kv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      const uint4 vv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      *(uint4*)(sK + (ch / CPR) * RS + (ch % CPR) * 16) = kv;
+      *(uint4*)(sV + (ch / CPR) * RS + (ch % CPR) * 16) = vv;
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < NK; ++k) kr[k] = vr[k] = make_uint4(0, 0, 0, 0);
   }
 
   const int qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
   const int nsteps = (L - qstart + BQ - 1) / BQ;
   const float c = a.c;
-
-  // one 64-query step: rows past the sequence read as zero (and LSE, D as 0)
-  auto load_step = [&](int t, Step16<D>& st) {
+  constexpr int CH = BQ * CPR / NT;   // 16-byte chunks per thread per tensor and step
+  struct Step {
+    uint4 q[CH], d[CH];
+    float x;   // LSE (threads 0..63) or D (threads 64..127)
+  };
+  auto load_step = [&](int t, Step& st) {
     const int q0 = qstart + t * BQ;
     const int rows = min(BQ, L - q0);
     const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
     const int nrec = ((rows - 1) * (int)rowH + D) * 2;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(gq + tb, nrec), rd = buffer_rsrc(gd + tb, nrec);
 #pragma unroll
-    for (int cc = 0; cc < Step16<D>::CH; ++cc) {
-      const int ch = tid + cc * 256;
+    for (int cc = 0; cc < CH; ++cc) {
+      const int ch = tid + cc * NT;
       const int off = (ch / CPR) * (int)rowH * 2 + (ch % CPR) * 16;
       st.q[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
       st.d[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
     }
-    // LSE and D rows of this head: [B, H, S] (fixed) or [H, T] (varlen)
     const long li = a.seq.cu ? (long)h * a.T + tok0 + q0 : ((long)s * a.H + h) * a.seq.S + q0;
     const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.lse + li, rows * 4), rD = buffer_rsrc(a.Dbuf + li, rows * 4);
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(tid < 64 ? rl : rD, (tid & 63) * 4, 0, 0));
-    st.lse2 = tid < 64 ? x * 1.44269504088896340736f : x;
+    st.x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(w == 0 ? rl : rD, lane * 4, 0, 0));
   };
-  auto store_step = [&](int buf, const Step16<D>& st) {
+  auto store_step = [&](int buf, const Step& st) {
 #pragma unroll
-    for (int cc = 0; cc < Step16<D>::CH; ++cc) {
-      const int ch = tid + cc * 256;
+    for (int cc = 0; cc < CH; ++cc) {
+      const int ch = tid + cc * NT;
       const int r = ch / CPR, cx = ch % CPR;
-      *(uint4*)(&sQ[buf][r * RS + cx * 16]) = st.q[cc];
-      *(uint4*)(&sO[buf][r * RS + cx * 16]) = st.d[cc];
+      *(uint4*)(sQ0 + buf * TILE_Q + r * RS + cx * 16) = st.q[cc];
+      *(uint4*)(sO0 + buf * TILE_Q + r * RS + cx * 16) = st.d[cc];
     }
-    if (tid < 64) sL[buf][tid] = st.lse2;
-    else if (tid < 128) sD[buf][tid - 64] = st.lse2;
+    if (w == 0) sL[buf][lane] = st.x * 1.44269504088896340736f;
+    else if (w == 1) sD[buf][lane] = st.x;
   };
 
   v16f dk[ND], dv[ND];
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
   for (int dc = 0; dc < ND; ++dc) dk[dc] = dv[dc] = v16f{};
 
   {
-    Step16<D> s0;
+    Step s0;
     load_step(0, s0);
     store_step(0, s0);
   }
@@ -193,64 +203,84 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_dkdv_kernel(BwdArgs a) {
 
   for (int t = 0; t < nsteps; ++t) {
     const int cur = t & 1;
-    const int q0 = qstart + t * BQ;
-    Step16<D> nx;
+    const int qa0 = qstart + t * BQ + 32 * qb;   // this wave's first query
+    Step nx;
     load_step(min(t + 1, nsteps - 1), nx);
 
-    const bool compute = kw0 < L && !(CAUSAL && q0 + BQ - 1 < kw0);
+    const bool compute = kw0 < L && qa0 < L && !(CAUSAL && qa0 + 31 < kw0);
     if (compute) {
-      const uint8_t* sQc = sQ[cur];
-      const uint8_t* sOc = sO[cur];
-      const bool need_mask = (q0 + BQ > L) || (CAUSAL && q0 < kw0 + 31);
-      uint4 pop[4], sop[4];   // P and dS operands: step k4 holds queries 16 k4 + 8g + 0..7 of key n
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S, dP: element i = query q0 + 32 qb + 8(i/4) + 4g + i%4, key = key
-        v16f S = v16f{}, dP = v16f{};
+      const uint8_t* sQc = sQ0 + cur * TILE_Q;
+      const uint8_t* sOc = sO0 + cur * TILE_Q;
+      const bool need_mask = (qa0 + 32 > L) || (CAUSAL && qa0 < kw0 + 31);
+      // S, dP: element i = query qa0 + 8(i/4) + 4g + i%4, key = key
+      v16f S = v16f{}, dP = v16f{};
+      {
         const uint8_t* qp = sQc + (32 * qb + n) * RS + 16 * g;
         const uint8_t* op = sOc + (32 * qb + n) * RS + 16 * g;
+        const uint8_t* kp = sK + (32 * kb + n) * RS + 16 * g;
+        const uint8_t* vp = sV + (32 * kb + n) * RS + 16 * g;
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
-          S = mfma_bf16(*(const uint4*)(qp + 32 * k), kr[k], S);
-          dP = mfma_bf16(*(const uint4*)(op + 32 * k), vr[k], dP);
+          S = mfma_bf16(*(const uint4*)(qp + 32 * k), *(const uint4*)(kp + 32 * k), S);
+          dP = mfma_bf16(*(const uint4*)(op + 32 * k), *(const uint4*)(vp + 32 * k), dP);
         }
-        float p[16], ds[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 l4 = *(const float4*)&sL[cur][32 * qb + 8 * q + 4 * g];
-          const float4 d4 = *(const float4*)&sD[cur][32 * qb + 8 * q + 4 * g];
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(S[i], c, -lv[e]));
-            if (need_mask) {
-              const int qq = q0 + 32 * qb + 8 * q + 4 * g + e;
-              const bool vis = qq < L && (!CAUSAL || qq >= key);
-              pv = vis ? pv : 0.f;
-            }
-            p[i] = pv;
-            ds[i] = pv * (dP[i] - dvv[e]);
-          }
-        }
-        to_operands(p, &pop[2 * qb]);
-        to_operands(ds, &sop[2 * qb]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS: rows d = 32 dc + ..., columns = key n, contraction = 64 queries
+      float p[16], ds[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 l4 = *(const float4*)&sL[cur][32 * qb + 8 * q + 4 * g];
+        const float4 d4 = *(const float4*)&sD[cur][32 * qb + 8 * q + 4 * g];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q + e;
+          float pv = __builtin_amdgcn_exp2f(fmaf(S[i], c, -lv[e]));
+          if (need_mask) {
+            const int qq = qa0 + 8 * q + 4 * g + e;
+            const bool vis = qq < L && (!CAUSAL || qq >= key);
+            pv = vis ? pv : 0.f;
+          }
+          p[i] = pv;
+          ds[i] = pv * (dP[i] - dvv[e]);
+        }
+      }
+      uint4 pop[2], sop[2];   // step h: queries qa0 + 16h + 8g + 0..7 of key n
+      to_operands(p, pop);
+      to_operands(ds, sop);
+      // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries
 #pragma unroll
       for (int dc = 0; dc < ND; ++dc)
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          dv[dc] = mfma_bf16(tr_operand<RS>(sOc, 16 * k4, 32 * dc, lane), pop[k4], dv[dc]);
-          dk[dc] = mfma_bf16(tr_operand<RS>(sQc, 16 * k4, 32 * dc, lane), sop[k4], dk[dc]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          dv[dc] = mfma_bf16(tr_operand<RS>(sOc, 32 * qb + 16 * h2, 32 * dc, lane), pop[h2], dv[dc]);
+          dk[dc] = mfma_bf16(tr_operand<RS>(sQc, 32 * qb + 16 * h2, 32 * dc, lane), sop[h2], dk[dc]);
         }
     }
     store_step(cur ^ 1, nx);
     __syncthreads();
   }
 
-  // ---- epilogue: lane = key, element i of chunk dc = feature 32 dc + 8(i/4) + 4g + i%4
-  if (key >= L) return;
+  // ---- the two waves of a key block add their partials through LDS (the tiles are free now)
+  float* red = (float*)smem + (size_t)kb * (2 * ND * 16 * 64);   // [wave kb][2 ND][16][64 lanes]
+  if (qb == 1) {
+#pragma unroll
+    for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[((2 * dc) * 16 + e) * 64 + lane] = dk[dc][e];
+        red[((2 * dc + 1) * 16 + e) * 64 + lane] = dv[dc][e];
+      }
+  }
+  __syncthreads();
+  if (qb == 1 || key >= L) return;
+#pragma unroll
+  for (int dc = 0; dc < ND; ++dc)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[dc][e] += red[((2 * dc) * 16 + e) * 64 + lane];
+      dv[dc][e] += red[((2 * dc + 1) * 16 + e) * 64 + lane];
+    }
+  // lane = key, element i of chunk dc = feature 32 dc + 8(i/4) + 4g + i%4
   const long row = (long)(tok0 + key) * rowH + (long)h * D;
   const bool f32 = a.grad_f32 != 0;
 #pragma unroll
@@ -426,7 +456,7 @@ hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipS
     BwdArgs b = a;
     b.nkt = (max_len + 127) / 128;
     const long grid = ((units + 7) / 8) * 8 * b.nkt;
-    dim3 gd((unsigned)grid), bd(256);
+    dim3 gd((unsigned)grid), bd(512);
     if (D == 64 && causal) attn_bwd_bf16_dkdv_kernel<64, true><<<gd, bd, 0, st>>>(b);
     else if (D == 64) attn_bwd_bf16_dkdv_kernel<64, false><<<gd, bd, 0, st>>>(b);
     else if (causal) attn_bwd_bf16_dkdv_kernel<128, true><<<gd, bd, 0, st>>>(b);
