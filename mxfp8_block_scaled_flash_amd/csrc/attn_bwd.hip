@@ -66,9 +66,6 @@ MX_DEV uint32_t ld_scale_word(const uint8_t* p, int nbytes) {
   return nbytes == 4 ? *(const uint32_t*)p : *(const uint16_t*)p;
 }
 
-// p in [0, inf) clamped to lim (one v_med3; p is never NaN)
-MX_DEV float clampp(float p, float lim) { return __builtin_amdgcn_fmed3f(p, 0.f, lim); }
-
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 MX_DEV void atomic_add_h2(_Float16* p, float a, float b) {
@@ -186,6 +183,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sDv[2][BQ];   // D
   __shared__ int sDSs[2][2][NW];               // dS scale code of [step parity][query block][key block]
 
+  saturating_fp8_converts();
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int id = blockIdx.x, xcd = id & 7, jj = id >> 3;
@@ -426,25 +424,18 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         // ---- MX codes (nothing visible: zero codes, scale 1)
         const int kp = max(exp2_scale_code(amax), 1);
         const int ks2 = max(scale_code(smax), 1);
-        const float psc = e8m0_f32(kp), plim = 448.f * psc;
-        const float ssc = e8m0_f32(ks2), slim = 448.f * ssc;
+        const float psc = e8m0_f32(kp), ssc = e8m0_f32(ks2);   // the converts saturate (wave MODE)
         uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           // the two converts fill both halves, so any register serves as the old value
           v2s z = __builtin_bit_cast(v2s, st[4 * q]);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q], plim), clampp(st[4 * q + 1], plim), psc,
-                                                       false);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[4 * q + 2], plim), clampp(st[4 * q + 3], plim),
-                                                       psc, true);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
           pw[q] = __builtin_bit_cast(uint32_t, z);
           v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q], -slim, slim),
-                                                       __builtin_amdgcn_fmed3f(dpt[4 * q + 1], -slim, slim), ssc,
-                                                       false);
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(dpt[4 * q + 2], -slim, slim),
-                                                       __builtin_amdgcn_fmed3f(dpt[4 * q + 3], -slim, slim), ssc,
-                                                       true);
+          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
+          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
           sw[q] = __builtin_bit_cast(uint32_t, y);
         }
         // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order

@@ -20,8 +20,9 @@
 //    (up to the fp32 rounding of the argument t - M).
 //  * P's block amax is 2^(block max of t - M), so its E8M0 scale follows
 //    from the maxima already reduced for M, with no extra exp (and no
-//    dependence on the accuracy of the hardware exp2).  The fp32->fp8 convert (which divides by
-//    the E8M0 scale) does not saturate, so values are clamped to 448*scale.
+//    dependence on the accuracy of the hardware exp2).  The fp32->fp8 convert
+//    (which divides by the E8M0 scale) saturates through the wave's MODE
+//    setting, so no clamp precedes it.
 //  * P is re-packed between lane halves with v_permlane32_swap so each lane
 //    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
 //    through ds_read_b64_tr_b8, in the same key order.
@@ -47,9 +48,6 @@ MX_DEV v8i pack8(uint4 lo, uint4 hi) {
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
   return r;
 }
-
-// p in [0, inf) clamped to lim (one v_med3; p is never NaN)
-MX_DEV float clampp(float p, float lim) { return __builtin_amdgcn_fmed3f(p, 0.f, lim); }
 
 MX_DEV v2i lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
@@ -80,6 +78,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
   __shared__ uint32_t sVs[2][64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
 
+  saturating_fp8_converts();
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
@@ -262,13 +261,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         }
       l_run += psum;
       int kc[2];
-      float sc[2], lim[2];
+      float sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // block amax of p is 2^(block max of t - M): its scale straight from that exponent
         kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
         sc[kb] = e8m0_f32(kc[kb]);
-        lim[kb] = 448.f * sc[kb];
       }
       // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
       uint32_t dw[2][4];
@@ -278,10 +276,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         for (int q = 0; q < 4; ++q) {
           // the two converts fill both halves of z, so any register serves as its old value
           v2s z = __builtin_bit_cast(v2s, st[kb][4 * q]);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q], lim[kb]), clampp(st[kb][4 * q + 1], lim[kb]),
-                                                       sc[kb], false);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, clampp(st[kb][4 * q + 2], lim[kb]),
-                                                       clampp(st[kb][4 * q + 3], lim[kb]), sc[kb], true);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[kb][4 * q], st[kb][4 * q + 1], sc[kb], false);
+          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[kb][4 * q + 2], st[kb][4 * q + 3], sc[kb], true);
           dw[kb][q] = __builtin_bit_cast(uint32_t, z);
         }
       // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order

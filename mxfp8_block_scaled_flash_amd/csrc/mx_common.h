@@ -75,6 +75,13 @@ MX_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
 // 2^(k-127) as an fp32 value, for k in [1, 254].
 MX_DEV float e8m0_f32(int k) { return __uint_as_float((uint32_t)k << 23); }
 
+// Saturating FP8 converts for this wave: with MODE.FP16_OVFL (bit 23) set, v_cvt_pk_fp8_f32 and
+// v_cvt_scalef32_pk_fp8_f32 turn finite values beyond E4M3's range into +-448 (codes 0x7E /
+// 0xFE) instead of NaN, the saturating encoding of the OCP MX rules, so no clamp is needed before
+// them (measured on gfx950: 465, 1000, 1e10 and -500 give 0x7E / 0xFE; with the bit clear, NaN).
+// The bit also makes fp16 results saturate at +-65504 instead of overflowing to infinity.
+MX_DEV void saturating_fp8_converts() { __builtin_amdgcn_s_setreg(/* hwreg(HW_REG_MODE, 23, 1) */ 1473, 1); }
+
 MX_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MX_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
