@@ -53,19 +53,26 @@ MX_DEV v2i lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
 
-// One 64-key tile of K and V in flight between HBM and LDS.
-template <int D, int NT>
+#ifndef FWD_BN
+#define FWD_BN 128
+#endif
+
+// One BN-key tile of K and V in flight between HBM and LDS.
+template <int D, int NT, int BN>
 struct KVStage {
-  static constexpr int CH = 64 * D / 16 / NT;   // 16-byte chunks per thread per tensor
+  static constexpr int CH = BN * D / 16 / NT;   // 16-byte chunks per thread per tensor
+  static constexpr int KH = BN / 64;            // 64-key halves: one scale word per lane and half
   uint4 k[CH], v[CH];
-  uint32_t ks;
-  uint32_t vb[D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
+  uint32_t ks[KH];
+  uint32_t vb[KH][D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
 };
 
 template <int D, int NW, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;   // queries per workgroup
-  constexpr int BN = 64;        // keys per tile
+  constexpr int BN = FWD_BN;    // keys per tile
+  constexpr int KB = BN / 32;   // 32-key blocks per tile
+  constexpr int KH = BN / 64;   // 64-key halves per tile (one P V contraction each)
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
   constexpr int KST = D + 16;   // LDS row stride of the K and V tiles
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][BN * KST];
   __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
-  __shared__ uint32_t sVs[2][64];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
+  __shared__ uint32_t sVs[2][BN];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
 
   saturating_fp8_converts();
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
@@ -108,14 +115,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // wait on the loads before the tile being computed needs them.  Every wave
   // fetches the scales of key `lane`; wave 0 stores the K ones, wave 1 the V ones.
   const int KSB = D / 32;   // bytes per K ROW32 scale word
-  auto load_tile = [&](int t, KVStage<D, NT>& st) {
+  auto load_tile = [&](int t, KVStage<D, NT, BN>& st) {
     const int k0 = t * BN;
     const int rows = min(BN, L - k0);   // >= 1
     const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
     const int nrec = (rows - 1) * (int)rowH + D;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tb, nrec), rv = buffer_rsrc(a.v + tb, nrec);
 #pragma unroll
-    for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
+    for (int c = 0; c < KVStage<D, NT, BN>::CH; ++c) {
       const int ch = tid + c * NT;
       const int off = (ch / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
       st.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
@@ -123,30 +130,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
     const __amdgpu_buffer_rsrc_t rks =
         buffer_rsrc(a.ks + ((long)(srow0 + k0) * a.H + h) * KSB, (rows - 1) * a.H * KSB + KSB);
-    st.ks = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, lane * a.H * KSB, 0, 0)
-                       : __builtin_amdgcn_raw_buffer_load_b16(rks, lane * a.H * KSB, 0, 0);
     const int nblk = (rows + 31) / 32;
     const __amdgpu_buffer_rsrc_t rvs =
-        buffer_rsrc(a.vs + ((long)(sblk0 + 2 * t) * a.H + h) * D, (nblk - 1) * a.H * D + D);
-    const int voff = (lane >> 5) * a.H * D + (lane & 31);
+        buffer_rsrc(a.vs + ((long)(sblk0 + KB * t) * a.H + h) * D, (nblk - 1) * a.H * D + D);
 #pragma unroll
-    for (int dc = 0; dc < ND; ++dc) st.vb[dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
+    for (int hh = 0; hh < KH; ++hh) {
+      const int kk = 64 * hh + lane;   // key of this lane in the tile
+      st.ks[hh] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, kk * a.H * KSB, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b16(rks, kk * a.H * KSB, 0, 0);
+      const int voff = (kk >> 5) * a.H * D + (kk & 31);
+#pragma unroll
+      for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
+    }
   };
-  auto store_tile = [&](int buf, const KVStage<D, NT>& st) {
+  auto store_tile = [&](int buf, const KVStage<D, NT, BN>& st) {
 #pragma unroll
-    for (int c = 0; c < KVStage<D, NT>::CH; ++c) {
+    for (int c = 0; c < KVStage<D, NT, BN>::CH; ++c) {
       const int ch = tid + c * NT;
       const int r = ch / (D / 16), cx = ch % (D / 16);
       *(uint4*)(&sK[buf][r * KST + cx * 16]) = st.k[c];
       *(uint4*)(&sV[buf][r * KST + cx * 16]) = st.v[c];
     }
     if (w == 0) {
-      sKs[buf][lane] = st.ks;
-    } else if (w == 1) {
-      uint32_t vs = 0;
 #pragma unroll
-      for (int dc = 0; dc < ND; ++dc) vs |= st.vb[dc] << (8 * dc);
-      sVs[buf][lane] = vs;
+      for (int hh = 0; hh < KH; ++hh) sKs[buf][64 * hh + lane] = st.ks[hh];
+    } else if (w == 1) {
+#pragma unroll
+      for (int hh = 0; hh < KH; ++hh) {
+        uint32_t vs = 0;
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) vs |= st.vb[hh][dc] << (8 * dc);
+        sVs[buf][64 * hh + lane] = vs;
+      }
     }
   };
 
@@ -174,11 +189,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int dc = 0; dc < ND; ++dc) o[dc] = v16f{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.c;
-  uint32_t vsc_prev = 0;   // scale operands of the last P V products, pinned until they finish
-  int psc_prev = 0;
+  uint32_t vsc_prev[KH];   // scale operands of the last P V products, pinned until they finish
+  int psc_prev[KH];
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh) vsc_prev[hh] = psc_prev[hh] = 0;
 
   {
-    KVStage<D, NT> st0;
+    KVStage<D, NT, BN> st0;
     load_tile(0, st0);
     store_tile(0, st0);
   }
@@ -190,7 +207,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     // the next tile's loads are in flight while this one is computed (past
     // the last tile the last one is fetched again and its buffer rewritten
     // with the same bytes, which keeps the loop free of branches around them)
-    KVStage<D, NT> nxt;
+    KVStage<D, NT, BN> nxt;
     const int tn = min(t + 1, ntiles - 1);
     load_tile(tn, nxt);
 
@@ -199,10 +216,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       const uint8_t* sKc = sK[cur];
       const uint8_t* sVc = sV[cur];
       // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
-      v16f st[2];
-      uint32_t ksc[2];
+      v16f st[KB];
+      uint32_t ksc[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const uint8_t* kp = sKc + (kb * 32 + n) * KST + 16 * g;
         ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
         v16f acc = v16f{};
@@ -216,31 +233,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         // element i is key k0 + 32 kb + 4g + c_i, c_i = 8(i/4) + i%4: visible iff c_i < hi
         const int last = CAUSAL ? min(L - 1, qi) : L - 1;   // last visible key of this query
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
           const int hi = last - k0 - 32 * kb - 4 * g + 1;
 #pragma unroll
           for (int i = 0; i < 16; ++i) st[kb][i] = (8 * (i >> 2) + (i & 3) < hi) ? st[kb][i] : -INFINITY;
         }
       }
       // ---- block maxima, frame update
-      float bm[2];
+      float bm[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         float m = st[kb][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
         bm[kb] = half_swap_max(m);
       }
       // S has been read: this tile's S products and the previous tile's P V products are done
-      keep(ksc[0]);
-      keep(ksc[1]);
-      keep(vsc_prev);
-      keep(psc_prev);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) keep(ksc[kb]);
+#pragma unroll
+      for (int hh = 0; hh < KH; ++hh) {
+        keep(vsc_prev[hh]);
+        keep(psc_prev[hh]);
+      }
       // Lazy frame: M moves (and O, l are rescaled by 2^(M_old - M_new)) only once the tile's
       // ceil(max) exceeds it by more than kLazy, so p stays below 2^kLazy.  In exact arithmetic
       // every frame gives P^ the same codes (its scales absorb the power of two) and the same
       // O and LSE; in fp32 the argument S c - M rounds at the frame's magnitude.
-      const float m_tile = ceilf(fmaxf(bm[0], bm[1]) * c);
+      float tmax = bm[0];
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb) tmax = fmaxf(tmax, bm[kb]);
+      const float m_tile = ceilf(tmax * c);
       if (m_tile > m_run + kLazy) {
         const float alpha = (m_run == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m_run - m_tile));
 #pragma unroll
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       // ---- p = 2^(S c - M), running sum
       float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
@@ -260,18 +283,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
           psum += p;
         }
       l_run += psum;
-      int kc[2];
-      float sc[2];
+      int kc[KB];
+      float sc[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         // block amax of p is 2^(block max of t - M): its scale straight from that exponent
         kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
         sc[kb] = e8m0_f32(kc[kb]);
       }
       // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
-      uint32_t dw[2][4];
+      uint32_t dw[KB][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           // the two converts fill both halves of z, so any register serves as its old value
@@ -280,27 +303,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
           z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[kb][4 * q + 2], st[kb][4 * q + 3], sc[kb], true);
           dw[kb][q] = __builtin_bit_cast(uint32_t, z);
         }
-      // ---- swap lane halves: lane half g then holds keys 16g + 0..15 of each block, in order
-      v8i pb;
+      // ---- per 64-key half hh: swap lane halves so lane half g holds keys 16g + 0..15 of each of
+      // its two blocks, in order; then O^T += V^T P^T (V^T rows d = 32 dc + lane%32, through LDS
+      // transpose reads)
+      const int G = lane >> 4, i16 = lane & 15;
+      const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
+      const int rowofs = 16 * (G >> 1) + (i16 >> 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
-        auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
-        pb[4 * kb + 0] = s02[0];
-        pb[4 * kb + 1] = s02[1];
-        pb[4 * kb + 2] = s13[0];
-        pb[4 * kb + 3] = s13[1];
-      }
-      const int psc = g ? kc[1] : kc[0];
-      const uint32_t vsc = sVs[cur][lane];
-      // ---- O^T += V^T P^T, V^T rows d = 32 dc + lane%32, through LDS transpose reads
-      {
-        const int G = lane >> 4, i16 = lane & 15;
-        const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
-        const int rowofs = 16 * (G >> 1) + (i16 >> 1);
+      for (int hh = 0; hh < KH; ++hh) {
+        v8i pb;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const int kb = 2 * hh + b2;
+          auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
+          auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
+          pb[4 * b2 + 0] = s02[0];
+          pb[4 * b2 + 1] = s02[1];
+          pb[4 * b2 + 2] = s13[0];
+          pb[4 * b2 + 3] = s13[1];
+        }
+        const int psc = g ? kc[2 * hh + 1] : kc[2 * hh];
+        const uint32_t vsc = sVs[cur][64 * hh + lane];
 #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
-          const uint8_t* vp = sVc + rowofs * KST + 32 * dc + colofs;
+          const uint8_t* vp = sVc + (64 * hh + rowofs) * KST + 32 * dc + colofs;
           v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * KST), r2 = lds_tr8(vp + 32 * KST), r3 = lds_tr8(vp + 40 * KST);
           v8i va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
           if (dc == 0) o[0] = mfma32<0, 0>(va, pb, o[0], vsc, psc);
@@ -310,9 +336,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
             if (dc == 3) o[3] = mfma32<3, 0>(va, pb, o[3], vsc, psc);
           }
         }
+        vsc_prev[hh] = vsc;
+        psc_prev[hh] = psc;
       }
-      vsc_prev = vsc;
-      psc_prev = psc;
     }
     store_tile(cur ^ 1, nxt);
     __syncthreads();
@@ -322,8 +348,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // p over its 16 keys of every block: the row sum adds both halves.
   l_run += __shfl_xor(l_run, 32, 64);
   keep(o[ND - 1][0]);
-  keep(vsc_prev);
-  keep(psc_prev);
+#pragma unroll
+  for (int hh = 0; hh < KH; ++hh) {
+    keep(vsc_prev[hh]);
+    keep(psc_prev[hh]);
+  }
   if (qi >= L) return;
   const float inv = 1.f / l_run;
   const long orow = (long)(tok0 + qi) * rowH + (long)h * D;
