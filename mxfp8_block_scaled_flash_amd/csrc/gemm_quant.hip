@@ -40,8 +40,9 @@
 #include "mx_common.h"
 #include "mx_launch.h"
 
-#ifndef GEMM_WT
-#define GEMM_WT 4
+// workgroup tile BT x BT of C; GEMM_NW waves arranged (GEMM_NW / 2) x 2 ... see gemm_quant_kernel
+#ifndef GEMM_NW
+#define GEMM_NW 8
 #endif
 
 namespace mxk {
@@ -113,16 +114,21 @@ MX_DEV v8i load_operand(const uint8_t* row, int g) {
 }  // namespace
 
 template <int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_quant_kernel(GemmArgs a) {
-  constexpr int WT = GEMM_WT;        // 32 x 32 blocks per wave side
-  constexpr int BM = 64 * WT, BN = 64 * WT;
+__global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a) {
+  // 256 x 256 tile of C.  4 waves: 2 x 2 waves of 128 x 128 (4 x 4 blocks, one wave per SIMD);
+  // 8 waves: 2 x 4 waves of 128 x 64 (4 x 2 blocks, two waves per SIMD, so one wave's operand
+  // reads and waits overlap the other's products).
+  constexpr int NW = GEMM_NW, NTH = 64 * NW;
+  constexpr int WM = 4, WN = NW == 4 ? 4 : 2;   // 32 x 32 blocks per wave along M and N
+  constexpr int WCOLS = 256 / (32 * WN);        // waves along N
+  constexpr int BM = 256, BN = 256;
   constexpr int W = fmt_bits<FMT>();
   constexpr int RBK = 8 * W;                        // bytes of one row per 64-deep K step
   constexpr int KST = RBK + (W == 6 ? 32 : 16);     // LDS row stride: 16-byte aligned, rows on distinct banks
   constexpr int CPR = RBK / 16;                     // 16-byte chunks per row and step
   constexpr int NCH = BM * CPR;                     // chunks per tile and step
-  constexpr int CPT = (NCH + 255) / 256;            // chunks per thread
-  static_assert(BM <= 256, "one scale row per thread");
+  constexpr int CPT = (NCH + NTH - 1) / NTH;        // chunks per thread
+  static_assert(BM <= NTH, "one scale row per thread");
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * KST];
   __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
@@ -144,77 +150,99 @@ __global__ __launch_bounds__(256, 1) void gemm_quant_kernel(GemmArgs a) {
   // ---- staging: BM rows x 8w bytes of A and of B per step, in 16-byte chunks
   struct Stage {
     uint4 av[CPT], bv[CPT];
-    uint32_t as, bs;
+    uint32_t sc;   // this thread's row's scale pair (A row tid, or B row tid - BM)
   };
+  static_assert(NTH == BM + BN, "one scale row per thread");
   const int rowsA = min(BM, a.M - m0), rowsB = min(BN, a.N - n0);
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.a + (long)m0 * rowb, rowsA * rowb);
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.b + (long)n0 * rowb, rowsB * rowb);
   const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(a.as + (long)m0 * kb32, rowsA * kb32);
   const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(a.bs + (long)n0 * kb32, rowsB * kb32);
+  const __amdgpu_buffer_rsrc_t rsc = tid < BM ? ras : rbs;   // wave-uniform (waves 0-3: A, 4-7: B)
+  const int srow = tid < BM ? tid : tid - BM;
+  const bool wide_scales = (kb32 & 15) == 0;
+  uint4 scw = make_uint4(0, 0, 0, 0);   // 8 steps of this row's scale pairs
+  int kfirst = 0;                       // the first load always fetches
   auto load = [&](int kt, Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;   // row ch / CPR, 16-byte column ch % CPR
-      if (NCH % 256 == 0 || ch < NCH) {
+      const int ch = tid + NTH * c;   // row ch / CPR, 16-byte column ch % CPR
+      if (NCH % NTH == 0 || ch < NCH) {
         const int off = (ch / CPR) * rowb + kt * RBK + (ch % CPR) * 16;
         st.av[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
         st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
       }
     }
-    // thread t: scale pairs of A row t and B row t (rows past BM: a duplicate, not stored)
-    const int r = tid % BM;
-    // one 16-bit load per row (K/32 is even, so a row's scale pair is 2-byte aligned)
-    st.as = __builtin_amdgcn_raw_buffer_load_b16(ras, r * kb32 + 2 * kt, 0, 0);
-    st.bs = __builtin_amdgcn_raw_buffer_load_b16(rbs, r * kb32 + 2 * kt, 0, 0);
+    // thread t: the scale pair of A row t (t < BM) or B row t - BM.  When a row's scales are
+    // 16-byte aligned (K/32 a multiple of 16) they are fetched 8 steps at a time; otherwise one
+    // 16-bit load per step (K/32 is even, so a pair is 2-byte aligned).
+    const int off = srow * kb32 + 2 * kt;
+    if (wide_scales) {
+      if ((kt & 7) == 0 || kt == kfirst) {
+        scw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off - 2 * (kt & 7), 0, 0));
+        kfirst = -1;
+      }
+      const int sub = kt & 7;
+      const uint32_t wd = sub < 4 ? (sub < 2 ? scw.x : scw.y) : (sub < 6 ? scw.z : scw.w);
+      st.sc = (wd >> (16 * (sub & 1))) & 0xFFFFu;
+    } else {
+      st.sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
+    }
   };
   auto store = [&](int buf, const Stage& st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;
-      if (NCH % 256 == 0 || ch < NCH) {
+      const int ch = tid + NTH * c;
+      if (NCH % NTH == 0 || ch < NCH) {
         *(uint4*)(&sA[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.av[c];
         *(uint4*)(&sB[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.bv[c];
       }
     }
-    if (tid < BM) {
-      sAs[buf][tid] = st.as;
-      sBs[buf][tid] = st.bs;
-    }
+    if (tid < BM) sAs[buf][tid] = st.sc;
+    else sBs[buf][tid - BM] = st.sc;
   };
 
   // acc[i][j]: C block (rows m0 + wr + 32 i, columns n0 + wc + 32 j); element e of
   // lane (n, g) = row + n, column + 8(e/4) + 4g + e%4
-  v16f acc[WT][WT];
+  v16f acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < WT; ++j) acc[i][j] = v16f{};
-  const int wr = 32 * WT * (w >> 1), wc = 32 * WT * (w & 1);
-  int sa_prev[WT], sb_prev[WT];   // scale operands of the last products, pinned
+    for (int j = 0; j < WN; ++j) acc[i][j] = v16f{};
+  const int wr = 32 * WM * (w / WCOLS), wc = 32 * WN * (w % WCOLS);
+  int sa_prev[WM], sb_prev[WN];   // scale operands of the last products, pinned
 #pragma unroll
-  for (int i = 0; i < WT; ++i) sa_prev[i] = sb_prev[i] = 0;
+  for (int i = 0; i < WM; ++i) sa_prev[i] = 0;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) sb_prev[j] = 0;
 
-  // one 64-deep step from LDS buffer cur: operands, then the WT x WT products
+  // one 64-deep step from LDS buffer cur: operands, then the WM x WN products
   auto compute = [&](const int cur) __attribute__((always_inline)) {
-    v8i ao[WT], bo[WT];
-    int sa[WT], sb[WT];
+    v8i ao[WM], bo[WN];
+    int sa[WM], sb[WN];
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+    for (int i = 0; i < WM; ++i) {
       ao[i] = load_operand<FMT>(sA[cur] + (wr + 32 * i + n) * KST, g);
       sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
-      bo[i] = load_operand<FMT>(sB[cur] + (wc + 32 * i + n) * KST, g);
-      sb[i] = (int)(sBs[cur][wc + 32 * i + n] >> (8 * g));
     }
 #pragma unroll
-    for (int i = 0; i < WT; ++i)
+    for (int j = 0; j < WN; ++j) {
+      bo[j] = load_operand<FMT>(sB[cur] + (wc + 32 * j + n) * KST, g);
+      sb[j] = (int)(sBs[cur][wc + 32 * j + n] >> (8 * g));
+    }
 #pragma unroll
-      for (int j = 0; j < WT; ++j) acc[i][j] = mfma<FMT>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+      for (int j = 0; j < WN; ++j) acc[i][j] = mfma<FMT>(bo[j], ao[i], acc[i][j], sb[j], sa[i]);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
       keep(sa_prev[i]);
-      keep(sb_prev[i]);
       sa_prev[i] = sa[i];
-      sb_prev[i] = sb[i];
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      keep(sb_prev[j]);
+      sb_prev[j] = sb[j];
     }
   };
   {
@@ -231,12 +259,11 @@ __global__ __launch_bounds__(256, 1) void gemm_quant_kernel(GemmArgs a) {
     store(cur ^ 1, nx);
     __syncthreads();
   }
-  keep(acc[WT - 1][WT - 1][0]);
+  keep(acc[WM - 1][WN - 1][0]);
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
-    keep(sa_prev[i]);
-    keep(sb_prev[i]);
-  }
+  for (int i = 0; i < WM; ++i) keep(sa_prev[i]);
+#pragma unroll
+  for (int j = 0; j < WN; ++j) keep(sb_prev[j]);
 
   // ---- epilogue, per 32 x 32 block
   const long ldc = a.N;
@@ -325,17 +352,17 @@ __global__ __launch_bounds__(256, 1) void gemm_quant_kernel(GemmArgs a) {
           a.sq_scale[(long)((m0 + wr + 32 * i) / 32) * nbn + col0 / 32] = (uint8_t)k;
       }
   };
-  static_for<WT>([&](auto I) { static_for<WT>([&](auto J) { block(acc[I][J], I, J); }); });
+  static_for<WM>([&](auto I) { static_for<WN>([&](auto J) { block(acc[I][J], I, J); }); });
 }
 
 hipError_t launch_gemm_quantize(GemmArgs a, hipStream_t st) {
-  constexpr int TILE = 64 * GEMM_WT;
+  constexpr int TILE = 256;
   a.tm = (a.M + TILE - 1) / TILE;
   a.tn = (a.N + TILE - 1) / TILE;
   const long ntiles = (long)a.tm * a.tn;
   if (ntiles == 0) return hipSuccess;
   const long grid = (ntiles + 7) / 8 * 8;
-  dim3 g((unsigned)grid), b(256);
+  dim3 g((unsigned)grid), b(64 * GEMM_NW);
   switch (a.fmt) {
     case 0: gemm_quant_kernel<0><<<g, b, 0, st>>>(a); break;
     case 2: gemm_quant_kernel<2><<<g, b, 0, st>>>(a); break;
