@@ -194,22 +194,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh) vsc_prev[hh] = psc_prev[hh] = 0;
 
-  {
-    KVStage<D, NT, BN> st0;
-    load_tile(0, st0);
-    store_tile(0, st0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
+  // one tile's products and softmax from LDS buffer cur
+  auto tile_body = [&](const int t, const int cur) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    const int cur = t & 1;
-    // the next tile's loads are in flight while this one is computed (past
-    // the last tile the last one is fetched again and its buffer rewritten
-    // with the same bytes, which keeps the loop free of branches around them)
-    KVStage<D, NT, BN> nxt;
-    const int tn = min(t + 1, ntiles - 1);
-    load_tile(tn, nxt);
 
     const bool compute = q0 < L && !(CAUSAL && k0 > q0 + 31);   // skip tiles above this wave's diagonal
     if (compute) {
@@ -340,7 +327,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         psc_prev[hh] = psc;
       }
     }
-    store_tile(cur ^ 1, nxt);
+  };
+  {
+    KVStage<D, NT, BN> st0;
+    load_tile(0, st0);
+    store_tile(0, st0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    // the next tile's loads are in flight while this one is computed (past
+    // the last tile the last one is fetched again and its buffer rewritten
+    // with the same bytes, which keeps the loop free of branches around them)
+    KVStage<D, NT, BN> nxt;
+    load_tile(min(t + 1, ntiles - 1), nxt);
+    tile_body(t, t & 1);
+    store_tile((t & 1) ^ 1, nxt);
     __syncthreads();
   }
 
