@@ -165,6 +165,51 @@ def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False
     return {"dQ": dQ, "dK": dK, "dV": dV, "p": p, "dS": dS, "D": Dv, "S": S, "dP": dP}
 
 
+def backward_head_blocks(q, k, v, o, do, lse, sigma, causal, q_blocks=(), k_blocks=()):
+    """backward_head (MX quantization, the instruction's accumulation for S and dP) for selected
+    32-row blocks only: dQ of the query blocks in q_blocks and dK, dV of the key blocks in
+    k_blocks.  Every step is local to such a block: the square [32 x 32] dS blocks of one query
+    block need only that block's rows against all keys, and P's 32-query blocks and dS's blocks of
+    one key block need all queries against only that block's keys.  The MX operands, D and the
+    frame are formed exactly as in backward_head, so each returned block equals the corresponding
+    rows of its full result.  Returns {"dQ": {qb: [rows, D]}, "dK": {kb: ...}, "dV": {kb: ...}}."""
+    q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    L = q.shape[0]
+    (qc, qk), (kc, kk), (dc, dk_) = mx.quantize_sq32(q, 0), mx.quantize_sq32(k, 0), mx.quantize_sq32(do, 0)
+    vc, vk = mx.quantize_row32(v)
+    qs, ks, dos = mx.dequantize_sq32(qc, qk, 0), mx.dequantize_sq32(kc, kk, 0), mx.dequantize_sq32(dc, dk_, 0)
+    vr = mx.dequantize_row32(vc, vk)
+    qe, ke, de = (mx.element_exponent_sq32(c_, k_, 0) for c_, k_ in ((qc, qk), (kc, kk), (dc, dk_)))
+    ve = mx.element_exponent_row32(vc, vk)
+    c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
+    Dv = fl32(np.sum(do * o, axis=1))
+
+    def p_ds(ri, cj):
+        vis = visible(L, L, causal)[np.ix_(ri, cj)] if causal else np.ones((len(ri), len(cj)), bool)
+        S = gm.matmul_mfma(qs[ri], qe[ri], ks[cj], ke[cj])
+        with np.errstate(over="ignore"):
+            p = np.where(vis, fl32(np.exp2(fl32(S * c - L2[ri, None]))), 0.0)
+        dP = gm.matmul_mfma(dos[ri], de[ri], vr[cj], ve[cj])
+        return p, np.where(vis, fl32(p * fl32(dP - Dv[ri, None])), 0.0)
+
+    everything = np.arange(L)
+    out = {"dQ": {}, "dK": {}, "dV": {}}
+    for qb in q_blocks:
+        ri = np.arange(32 * qb, min(L, 32 * qb + 32))
+        _, dS = p_ds(ri, everything)
+        dSh = mx.dequantize_sq32(*mx.quantize_sq32(dS, 0), 0)          # one query block, all key blocks
+        out["dQ"][qb] = sigma * (dSh @ ks)
+    for kb in k_blocks:
+        cj = np.arange(32 * kb, min(L, 32 * kb + 32))
+        p, dS = p_ds(everything, cj)
+        dSh = mx.dequantize_sq32(*mx.quantize_sq32(dS, 0), 0)          # all query blocks, one key block
+        pb = mx.dequantize_col32(*mx.quantize_col32(p, axis=0), axis=0)  # 32 queries per key
+        out["dV"][kb] = pb.T @ dos
+        out["dK"][kb] = sigma * (dSh.T @ qs)
+    return out
+
+
 # -------------------------------------------------------- textbook, float64
 def attention_fp64(q, k, v, sigma, causal):
     """softmax(sigma q k^T) v in float64, no quantization; returns (O, LSE)."""

@@ -265,3 +265,22 @@ def test_varlen_forward_equals_per_sequence():
             r = at.forward_head(q[cu[s]:cu[s + 1], h], k[cu[s]:cu[s + 1], h], v[cu[s]:cu[s + 1], h], 0.125, True)
             assert np.array_equal(O[cu[s]:cu[s + 1], h], r["O"])
             assert np.array_equal(LSE[h, cu[s]:cu[s + 1]], r["LSE"])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_blocks_equal_the_full_backward(causal):
+    """The block-subset backward (used to check full-size kernels on sampled blocks) returns
+    exactly the rows of the full quantized backward, including a short tail block."""
+    rng = np.random.default_rng(21)
+    L, D, sigma = 150, 64, 0.125
+    q, k, v, do = (rng.standard_normal((L, D)).astype(np.float32).astype(np.float64) for _ in range(4))
+    f = at.forward_head(q, k, v, sigma, causal, gemm="exact")
+    o, lse = f["O"].astype(np.float32).astype(np.float64), f["LSE"].astype(np.float32).astype(np.float64)
+    full = at.backward_head(q, k, v, o, do, lse, sigma, causal)
+    blocks = [0, 2, 4]   # block 4 holds rows 128..149
+    part = at.backward_head_blocks(q, k, v, o, do, lse, sigma, causal, q_blocks=blocks, k_blocks=blocks)
+    for b in blocks:
+        rows = slice(32 * b, min(L, 32 * b + 32))
+        assert np.array_equal(part["dQ"][b], full["dQ"][rows])
+        assert np.array_equal(part["dK"][b], full["dK"][rows])
+        assert np.array_equal(part["dV"][b], full["dV"][rows])
