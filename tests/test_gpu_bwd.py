@@ -156,3 +156,44 @@ def test_backward_is_finite_and_repeatable():
         assert np.all(np.isfinite(x))
     # dK and dV are reduced in registers in a fixed order: bitwise repeatable
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+def test_backward_llm_shape_sampled_blocks():
+    """The metric shape (B8 H32 S8192 D128, causal) in the call bench.py times.  One sampled
+    (batch, head) carries O and LSE from the oracle forward; every other head holds an inert
+    filler (O = 0, LSE = 30, so its p is ~0), since only the sampled head is compared.  dQ of
+    sampled query blocks and dK, dV of sampled key blocks (first, last and random ones) are
+    checked against the oracle's block-subset backward, within the same 5e-3 bar."""
+    w = synth.workload("llm")
+    B, S, H, D = w.B, w.S, w.H, w.D
+    sigma = 1 / math.sqrt(D)
+    (b, h), = synth.draw_sample_pairs(w.seed, B, H, 1)
+    log(f"bwd llm {w.shape()} head {(b, h)}")
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+    f = at.forward_head(qn, kn, vn, sigma, True, gemm="exact")
+    o_h = torch.from_numpy(f["O"].astype(np.float32)).to(torch.bfloat16)
+    lse_h = torch.from_numpy(f["LSE"].astype(np.float32))
+    o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, S), 30.0, device="cuda")
+    o[b, :, h, :] = o_h.cuda()
+    lse[b, h, :] = lse_h.cuda()
+    qs = mx.quantize(x["q"], mx.SQ32)[mx.SQ32]
+    ks = mx.quantize(x["k"], mx.SQ32)[mx.SQ32]
+    dos = mx.quantize(x["do"], mx.SQ32)[mx.SQ32]
+    vr = mx.quantize(x["v"], mx.ROW32)[mx.ROW32]
+    dq, dk, dv = mx.attn_bwd(qs, ks, vr, dos, o, x["do"], lse, sigma, True, 8, torch.float32)
+    torch.cuda.synchronize()
+    gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
+    del dq, dk, dv, qs, ks, dos, vr, x, o, lse
+    rng = np.random.default_rng(4)
+    nb = S // 32
+    qb = sorted({0, 1, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+    kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+    ref = at.backward_head_blocks(qn, kn, vn, o_h.double().numpy(), dn, lse_h.double().numpy(), sigma, True,
+                                  q_blocks=qb, k_blocks=kb)
+    rows = lambda bl: np.concatenate([np.arange(32 * i, 32 * i + 32) for i in bl])  # noqa: E731
+    for name, g_, bl, key in (("dQ", gq, qb, "dQ"), ("dK", gk, kb, "dK"), ("dV", gv, kb, "dV")):
+        e = rel_fro(g_[rows(bl)], np.concatenate([ref[key][i] for i in bl]))
+        log(f"  llm {name} blocks {bl}: rel Frobenius {e:.2e}")
+        assert e <= TOL, f"llm {name}: rel Frobenius {e:.3e} > {TOL}"
