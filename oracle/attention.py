@@ -107,7 +107,8 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None
         S = r(qh @ kh.T)
     Smax = np.max(np.where(vis, S, -np.inf), axis=1)
     M = np.ceil(r(Smax * c))
-    p = r(np.exp2(r(S * c - M[:, None])))
+    with np.errstate(over="ignore"):                  # masked entries may overflow; they are dropped
+        p = r(np.exp2(r(S * c - M[:, None])))
     p = np.where(vis, p, 0.0)
     l = p.sum(axis=1)
     if quantize:
@@ -148,7 +149,8 @@ def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False
         c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
     vis = visible(q.shape[0], k.shape[0], causal)
     S = gm.matmul_mfma(qs, qe, ks, ke) if use_mfma else r(qs @ ks.T)
-    p = np.where(vis, r(np.exp2(r(S * c - L2[:, None]))), 0.0)
+    with np.errstate(over="ignore"):                  # masked entries may overflow; they are dropped
+        p = np.where(vis, r(np.exp2(r(S * c - L2[:, None]))), 0.0)
     dP = gm.matmul_mfma(dos, de, vr, ve) if use_mfma else r(dos @ vr.T)
     Dv = r(np.sum(do * o, axis=1))
     dS = np.where(vis, r(p * r(dP - Dv[:, None])), 0.0)

@@ -115,3 +115,32 @@ def test_bf16_backward_rejects_bad_arguments():
         mx.mx_attn_bwd_bf16(x, x, x, x, x, lse, 1, 8, 1, 64, 0.1, True, x, x, x, ws[:16])
     with pytest.raises(mx.MXError):   # D
         mx.mx_attn_bwd_bf16(x, x, x, x, x, lse, 1, 8, 1, 80, 0.1, True, x, x, x, ws)
+
+
+def test_bf16_backward_llm_shape_sampled_head():
+    """The metric shape (B8 H32 S8192 D128, causal, bf16 gradients) in the call bench.py times.
+    One sampled (batch, head) carries O and LSE from the oracle's BF16 forward; every other head
+    holds an inert filler (O = 0, LSE = 30, so its p is ~0).  The sampled head's whole dQ, dK and
+    dV are compared with the oracle's BF16 backward."""
+    w = synth.workload("llm")
+    B, S, H, D = w.B, w.S, w.H, w.D
+    sigma = 1 / math.sqrt(D)
+    (b, h), = synth.draw_sample_pairs(w.seed + 1, B, H, 1)
+    log(f"bf16 bwd llm {w.shape()} head {(b, h)}")
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+    f = at.forward_head(qn, kn, vn, sigma, True, quantize=False, p_round="bf16")
+    o_h = torch.from_numpy(f["O"].astype(np.float32)).to(torch.bfloat16)
+    lse_h = torch.from_numpy(f["LSE"].astype(np.float32))
+    del f
+    o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, S), 30.0, device="cuda")
+    o[b, :, h, :] = o_h.cuda()
+    lse[b, h, :] = lse_h.cuda()
+    dq, dk, dv = mx.attn_bwd_bf16(x["q"], x["k"], x["v"], o, x["do"], lse, sigma, True, torch.bfloat16)
+    torch.cuda.synchronize()
+    gpu = [t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv)]
+    del dq, dk, dv, x, o, lse
+    r = at.backward_head(qn, kn, vn, o_h.double().numpy(), dn, lse_h.double().numpy(), sigma, True,
+                         quantize=False, p_round="bf16")
+    _check(gpu, (r["dQ"], r["dK"], r["dV"]), f"llm b{b} h{h}")
