@@ -260,16 +260,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       const float negM = -m_run;
       // ---- p = 2^(S c - M), running sum
-      float psum = 0.f;
+      // four partial sums: independent add chains (one chain held every p live until its add,
+      // which pushed the kernel past its register budget)
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
           st[kb][i] = p;
-          psum += p;
+          ps[i & 3] += p;
         }
-      l_run += psum;
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       int kc[KB];
       float sc[KB];
 #pragma unroll
