@@ -42,6 +42,7 @@ import numpy as np
 
 from . import gemm as gm
 from . import mx
+from . import mxsmall as ms
 
 LOG2E32 = float(np.float32(math.log2(math.e)))
 
@@ -71,7 +72,19 @@ def visible(Lq: int, Lk: int, causal: bool) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- forward
-def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None, gemm="mfma", p_round=None):
+def _quantize_qk(x, qk_fmt):
+    """(dequantized values, element exponents) of a Q or K head [L, D] in ROW32 blocks: MXFP8
+    E4M3, or MXFP6 / MXFP4 (qk_fmt "e2m3", "e3m2", "e2m1"; [News], paragraph on the block-scaled
+    MMA's formats, read as the OCP MX v1.0 elements, see oracle/mxsmall.py)."""
+    if qk_fmt == "e4m3":
+        c, k = mx.quantize_row32(x)
+        return mx.dequantize_row32(c, k), mx.element_exponent_row32(c, k)
+    c, k = ms.quantize_rows(x, qk_fmt)
+    return ms.dequantize_rows(c, k, qk_fmt), ms.element_exponent_rows(c, k, qk_fmt)
+
+
+def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None, gemm="mfma", p_round=None,
+                 qk_fmt="e4m3"):
     """One (batch, head): q, k, v are [L, D] source values (fp32 or bf16 upcast).
 
     Returns a dict with O [L, D] (float64, before the output cast), LSE [L]
@@ -82,16 +95,16 @@ def forward_head(q, k, v, sigma, causal, quantize=True, exact=False, q_rows=None
     step is row-wise, so each returned row equals the full computation's.
     ``p_round="bf16"`` (with ``quantize=False``): the BF16 attention baseline, in
     which P enters P V rounded to bfloat16 and l still sums the fp32 p.
+    ``qk_fmt``: element format of Q and K ("e4m3", or MXFP6 "e2m3" / "e3m2", MXFP4
+    "e2m1"); P and V stay MXFP8 and every later step is unchanged.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
     if quantize:
-        qc, qk = mx.quantize_row32(q)
-        kc, kk = mx.quantize_row32(k)
-        qh, kh = mx.dequantize_row32(qc, qk), mx.dequantize_row32(kc, kk)
-        qe, ke = mx.element_exponent_row32(qc, qk), mx.element_exponent_row32(kc, kk)
+        qh, qe = _quantize_qk(q, qk_fmt)
+        kh, ke = _quantize_qk(k, qk_fmt)
         vh = mx.dequantize_col32(*mx.quantize_col32(v, axis=0), axis=0)
     else:
         qh, kh, vh = q, k, v
@@ -252,12 +265,13 @@ def _heads(x, cu_seqlens):
                 yield (s, h), x[cu_seqlens[s]:cu_seqlens[s + 1], h, :]
 
 
-def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=False):
+def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=False, qk_fmt="e4m3"):
     """Forward over [B, S, H, D] (or packed [T, H, D] with cu_seqlens).
 
     Returns O (float64, q's shape) and LSE ([B, H, S] or [H, T], float64).
     ``bf16_baseline``: no MX step, P rounded to bfloat16 before P V (the BF16
     attention the pages compare against, [News] headline figures).
+    ``qk_fmt``: element format of Q and K (see forward_head).
     """
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     O = np.zeros_like(q)
@@ -270,7 +284,7 @@ def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=
         if qh.shape[0] == 0:
             continue
         res = (forward_head(qh, ks[key], vs[key], sigma, causal, quantize=False, p_round="bf16")
-               if bf16_baseline else forward_head(qh, ks[key], vs[key], sigma, causal))
+               if bf16_baseline else forward_head(qh, ks[key], vs[key], sigma, causal, qk_fmt=qk_fmt))
         a, h = key
         if cu_seqlens is None:
             O[a, :, h, :] = res["O"]

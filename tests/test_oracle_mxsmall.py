@@ -1,5 +1,7 @@
 """Pins of the MXFP6 / MXFP4 codec (oracle/mxsmall.py) against the OCP MX
 format definitions and brute force, independent of any kernel."""
+import math
+
 import numpy as np
 import pytest
 
@@ -74,3 +76,69 @@ def test_pack_unpack_and_bit_order(fmt):
         assert ms.pack(np.array([[1, 0, 0, 0]], np.uint8), fmt).tolist() == [[1, 0, 0]]
         assert ms.pack(np.array([[0, 1, 0, 0]], np.uint8), fmt).tolist() == [[0x40, 0, 0]]
         assert ms.pack(np.array([[0, 0, 0, 63]], np.uint8), fmt).tolist() == [[0, 0, 0xFC]]
+
+
+# ---------------------------------------------------------------- Q and K in MXFP6 / MXFP4 inside attention
+def _grid_qk(L, D, seed):
+    """Q or K whose every 32-element block holds values from {1, 1.5, 2, 3, 4, 6} (signed, with
+    zeros) times one power of two, and reaches 6 times that power: exactly representable in E2M3,
+    E3M2, E2M1 and E4M3 under each format's own scale rule, with no subnormal element."""
+    rng = np.random.default_rng(seed)
+    vals = np.array([0.0, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    x = rng.choice(vals, size=(L, D)) * rng.choice([-1.0, 1.0], size=(L, D))
+    x[:, ::32] = 6.0
+    return x * np.exp2(rng.integers(-3, 4, size=(L, D // 32))).repeat(32, axis=1)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2", "e2m1"])
+@pytest.mark.parametrize("gemm", ["exact", "mfma"])
+def test_attention_qk_formats_agree_on_representable_operands(fmt, gemm):
+    from oracle import attention as at
+    L, D = 80, 64
+    q, k = _grid_qk(L, D, 1), _grid_qk(L, D, 2)
+    v = np.random.default_rng(3).standard_normal((L, D))
+    a = at.forward_head(q, k, v, 0.125, True, gemm=gemm, qk_fmt=fmt)
+    b = at.forward_head(q, k, v, 0.125, True, gemm=gemm)
+    assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["O"], b["O"]) and np.array_equal(a["LSE"], b["LSE"])
+
+
+def _e2m1_brute(x):
+    """E2M1 quantization by search: per 32-block scale 2^(floor(log2 amax) - 2), each element the
+    nearest of the eight magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even code), sign kept,
+    6 above the top."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    out = np.zeros_like(x)
+    for r in range(x.shape[0]):
+        for b0 in range(0, x.shape[1], 32):
+            blk = x[r, b0:b0 + 32]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                continue
+            s = 2.0 ** (math.floor(math.log2(amax)) - 2)
+            for i, y in enumerate(blk):
+                d = np.abs(np.abs(y) / s - mags)
+                best = np.flatnonzero(d == d.min())
+                code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+                out[r, b0 + i] = math.copysign(mags[code] * s, y)
+    return out
+
+
+def test_attention_e2m1_logits_match_a_brute_force_quantizer():
+    from oracle import attention as at
+    rng = np.random.default_rng(4)
+    L, D = 40, 64
+    q, k, v = (rng.standard_normal((L, D)) * 3 for _ in range(3))
+    S = at.forward_head(q, k, v, 0.125, False, gemm="exact", qk_fmt="e2m1")["S"]
+    ref = (_e2m1_brute(q) @ _e2m1_brute(k).T).astype(np.float32).astype(np.float64)
+    assert np.array_equal(S, ref)
+
+
+@pytest.mark.parametrize("fmt,floor", [("e2m3", 0.99), ("e3m2", 0.99), ("e2m1", 0.97)])
+def test_attention_qk_formats_stay_close_to_float64_attention(fmt, floor):
+    from oracle import attention as at
+    rng = np.random.default_rng(5)
+    L, D = 96, 64
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    ref = at.forward_head(q, k, v, 0.125, True, quantize=False, exact=True)["O"]
+    o = at.forward_head(q, k, v, 0.125, True, qk_fmt=fmt)["O"]
+    assert np.sum(o * ref) / np.linalg.norm(o) / np.linalg.norm(ref) >= floor
