@@ -249,6 +249,28 @@ def main():
         del qa, qb
     del hid, wgt
 
+    # the forward with Q and K in MXFP6 / MXFP4 (P and V MXFP8) on the same inputs, timed alone
+    fwd_fmt = {}
+    of = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+    for name, fmt in (("mxfp6_e2m3", mx.E2M3), ("mxfp6_e3m2", mx.E3M2), ("mxfp4_e2m1", mx.E2M1)):
+        qf, kf = mx.quantize_rows(x["q"].view(-1, D), fmt), mx.quantize_rows(x["k"].view(-1, D), fmt)
+
+        def fwd_f(qf=qf, kf=kf, fmt=fmt):
+            mx.mx_attn_fwd_fmt(qf[0], qf[1], kf[0], kf[1], qz["v"][COL][0], qz["v"][COL][1], B, S, H, D, sigma,
+                               True, fmt, of, lse)
+
+        fwd_f()
+        r0, r1 = ev(), ev()
+        r0.record(stream)
+        for _ in range(5):
+            fwd_f()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        ms_ = r0.elapsed_time(r1) / 5
+        fwd_fmt[name] = {"ms": round(ms_, 4), "tflops": round(4.0 * D * B * H * S * (S + 1) / 2 / (ms_ * 1e-3) / 1e12, 2)}
+        del qf, kf
+    del of
+
     # BF16 attention forward on the same inputs (the baseline of the MX speed-up), timed alone
     o16 = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
 
@@ -328,6 +350,7 @@ def main():
         "gemm_quantize": {"M": gM, "N": gN, "K": gK, "layouts": "row32+sq32", "ms": round(g_ms, 4),
                           "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2),
                           **g_fmt},
+        "fwd_qk_formats": fwd_fmt,
         "bf16_fwd": {"ms": round(f16_ms, 4), "tflops": round(f_flop / (f16_ms * 1e-3) / 1e12, 2),
                      "pct_bf16_peak": round(100 * f_flop / (f16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
                      "mx_speedup": round(f16_ms / f_ms, 3)},

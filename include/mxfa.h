@@ -267,6 +267,28 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
 
 /*
+ * mx_attn_fwd_fmt -- mx_attn_fwd with Q and K in MXFP6 or MXFP4.
+ * Defines: [News], paragraph on Blackwell's block-scaled MMA instructions (MXFP8,
+ * MXFP6 and MXFP4 operands of the same block-scaled product), applied to the
+ * forward's S = Q^ K^T of [Blog], "1. End-to-End Block-Scaled GEMM Fusion".
+ * Reading (the pages define neither format): the OCP MX v1.0 elements, as for
+ * mx_quantize_rows; P and V stay MXFP8 and every later step is mx_attn_fwd's.
+ *   qk_format   MX_E4M3 (identical to mx_attn_fwd), MX_E2M3, MX_E3M2 or MX_E2M1
+ *   q_data, k_data   packed payload [B, S, H, D*w/8] bytes (w = 8, 6, 6, 4): each
+ *               (token, head) row is the little-endian bitstream of its D
+ *               elements (mx_quantize_rows' layout with rows = B*S*H, K = D)
+ *   q_scale, k_scale ROW32 E8M0 scales [B, S, H, D/32] (the format's scale rule)
+ *   other arguments, outputs and errors as mx_attn_fwd; MX_EINVAL also for an
+ *   unknown qk_format.  Device pointers 16-byte aligned; async on `stream`.
+ */
+mx_status mx_attn_fwd_fmt(const uint8_t* q_data, const uint8_t* q_scale,
+                          const uint8_t* k_data, const uint8_t* k_scale,
+                          const uint8_t* v_data, const uint8_t* v_scale,
+                          int B, int S, int H, int D, float softmax_scale, int causal,
+                          mx_elem qk_format, void* o, mx_dtype o_dtype, float* lse,
+                          hipStream_t stream);
+
+/*
  * mx_attn_fwd_bf16 -- BF16 attention forward, the baseline of the pages'
  * speed-up figures ([News], headline comparison with BF16 FlashAttention-4).
  * Reading (the pages do not define it): mx_attn_fwd with every MX step

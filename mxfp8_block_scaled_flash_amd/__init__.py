@@ -43,6 +43,7 @@ _SIGS = {
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
+    "mx_attn_fwd_fmt": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_bf16": ([_vp] * 3 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_bf16_varlen": ([_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
@@ -180,6 +181,13 @@ def mx_attn_fwd_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seq
                                     _ptr(v_scale), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq, total_tokens,
                                     max_seqlen, H, D, float(softmax_scale), int(bool(causal)), _ptr(o),
                                     _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_varlen")
+
+
+def mx_attn_fwd_fmt(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal,
+                    qk_format, o, lse, stream=None):
+    _check(lib().mx_attn_fwd_fmt(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                                 _ptr(v_scale), B, S, H, D, float(softmax_scale), int(bool(causal)), int(qk_format),
+                                 _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_fmt")
 
 
 def mx_attn_fwd_bf16(q, k, v, B, S, H, D, softmax_scale, causal, o, lse, stream=None):
@@ -349,6 +357,16 @@ def attn_fwd(q, k, v, softmax_scale, causal, out_dtype=torch.bfloat16, with_lse=
     o = torch.empty((B, S, H, D), dtype=out_dtype, device=q[0].device)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q[0].device) if with_lse else None
     mx_attn_fwd(q[0], q[1], k[0], k[1], v[0], v[1], B, S, H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_fwd_fmt(q, k, v, shape, softmax_scale, causal, qk_format, out_dtype=torch.bfloat16, with_lse=True):
+    """q, k: (packed data, ROW32 scales) in element format qk_format, as quantize_rows gives them for
+    the [B*S*H, D] view; v: (data, scale) COL32; shape = (B, S, H, D).  Returns (O, LSE)."""
+    B, S, H, D = shape
+    o = torch.empty((B, S, H, D), dtype=out_dtype, device=v[0].device)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=v[0].device) if with_lse else None
+    mx_attn_fwd_fmt(q[0], q[1], k[0], k[1], v[0], v[1], B, S, H, D, softmax_scale, causal, qk_format, o, lse)
     return o, lse
 
 

@@ -37,9 +37,9 @@
 
 namespace mxk {
 
-template <int OA, int OB>
+template <int OA, int OB, int FMT = 0>
 MX_DEV v16f mfma32(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, OA, sa, OB, sb);
 }
 
 MX_DEV v8i pack8(uint4 lo, uint4 hi) {
@@ -47,6 +47,28 @@ MX_DEV v8i pack8(uint4 lo, uint4 hi) {
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
   return r;
+}
+
+// Bits per element of the Q / K payload: E4M3 (code 0), E2M3 / E3M2 (2, 3), E2M1 (4).
+template <int QF>
+constexpr int qk_bits() { return QF == 0 ? 8 : QF == 4 ? 4 : 6; }
+
+// Operand of one QK^T product (64 contraction indices = 32-element blocks 2c, 2c + 1) for lane half
+// g, from a packed Q or K row.  E4M3: bytes 16g..16g+15 and 32+16g..32+16g+15 of the chunk.  MXFP6 /
+// MXFP4: the whole block 2c + g as the instruction's little-endian bitstream (24 or 16 bytes in the
+// first dwords; measured layout of the scaled instruction's format fields).
+template <int QF>
+MX_DEV v8i qk_operand(const uint8_t* row, int c, int g) {
+  if constexpr (QF == 0) {
+    return pack8(*(const uint4*)(row + 64 * c + 16 * g), *(const uint4*)(row + 64 * c + 32 + 16 * g));
+  } else if constexpr (qk_bits<QF>() == 6) {
+    const uint2* p = (const uint2*)(row + 24 * (2 * c + g));
+    const uint2 x = p[0], y = p[1], z = p[2];
+    return v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
+  } else {
+    const uint4 x = *(const uint4*)(row + 16 * (2 * c + g));
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  }
 }
 
 MX_DEV v2i lds_tr8(const uint8_t* p) {
@@ -57,17 +79,19 @@ MX_DEV v2i lds_tr8(const uint8_t* p) {
 #define FWD_BN 128
 #endif
 
-// One BN-key tile of K and V in flight between HBM and LDS.
-template <int D, int NT, int BN>
+// One BN-key tile of K and V in flight between HBM and LDS (K rows of KRB payload bytes).
+template <int D, int NT, int BN, int KRB>
 struct KVStage {
-  static constexpr int CH = BN * D / 16 / NT;   // 16-byte chunks per thread per tensor
-  static constexpr int KH = BN / 64;            // 64-key halves: one scale word per lane and half
-  uint4 k[CH], v[CH];
+  static constexpr int NCHK = BN * KRB / 16;             // 16-byte chunks of the K tile
+  static constexpr int CHK = (NCHK + NT - 1) / NT;       // per thread (threads past NCHK idle)
+  static constexpr int CH = BN * D / 16 / NT;            // 16-byte chunks of V per thread
+  static constexpr int KH = BN / 64;                     // 64-key halves: one scale word per lane and half
+  uint4 k[CHK], v[CH];
   uint32_t ks[KH];
   uint32_t vb[KH][D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
 };
 
-template <int D, int NW, bool CAUSAL, bool OUT_BF16>
+template <int D, int NW, bool CAUSAL, bool OUT_BF16, int QF>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;   // queries per workgroup
   constexpr int BN = FWD_BN;    // keys per tile
@@ -75,12 +99,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int KH = BN / 64;   // 64-key halves per tile (one P V contraction each)
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
-  constexpr int KST = D + 16;   // LDS row stride of the K and V tiles
+  constexpr int KRB = D * qk_bits<QF>() / 8;   // payload bytes of one Q or K row
+  constexpr int KST = D + 16;   // LDS row stride of the V tile
+  constexpr int KSK = KRB + 16; // LDS row stride of the K tile
   constexpr float kLazy = 8.f;  // largest log2 of p before the frame moves
   constexpr int NT = NW * 64;
   static_assert(BN * D / 16 % NT == 0, "tile chunks must divide among the threads");
   // two buffers: the tile being computed and the next one, written while it is computed
-  __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * KSK];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][BN * KST];
   __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
   __shared__ uint32_t sVs[2][BN];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
@@ -107,7 +133,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   if (qbase >= L) return;
   const int q0 = qbase + 32 * w;
   const int qi = q0 + n;
-  const long rowH = (long)a.H * D;
+  const long rowH = (long)a.H * D;       // V and O row stride
+  const long rowHk = (long)a.H * KRB;    // Q and K payload row stride
 
   // ---- staging of one K/V tile: buffer loads into registers, then LDS stores.
   // Each tile gets scalar buffer resources that end with the sequence, so rows
@@ -115,17 +142,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // wait on the loads before the tile being computed needs them.  Every wave
   // fetches the scales of key `lane`; wave 0 stores the K ones, wave 1 the V ones.
   const int KSB = D / 32;   // bytes per K ROW32 scale word
-  auto load_tile = [&](int t, KVStage<D, NT, BN>& st) {
+  using Stage = KVStage<D, NT, BN, KRB>;
+  auto load_tile = [&](int t, Stage& st) {
     const int k0 = t * BN;
     const int rows = min(BN, L - k0);   // >= 1
     const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
-    const int nrec = (rows - 1) * (int)rowH + D;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tb, nrec), rv = buffer_rsrc(a.v + tb, nrec);
+    const long tbk = (long)(tok0 + k0) * rowHk + (long)h * KRB;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tbk, (rows - 1) * (int)rowHk + KRB);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + tb, (rows - 1) * (int)rowH + D);
 #pragma unroll
-    for (int c = 0; c < KVStage<D, NT, BN>::CH; ++c) {
+    for (int c = 0; c < Stage::CHK; ++c) {
+      const int ch = tid + c * NT;
+      const int off = (ch / (KRB / 16)) * (int)rowHk + (ch % (KRB / 16)) * 16;
+      if (Stage::NCHK % NT == 0 || ch < Stage::NCHK)
+        st.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < Stage::CH; ++c) {
       const int ch = tid + c * NT;
       const int off = (ch / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
-      st.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
       st.v[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
     const __amdgpu_buffer_rsrc_t rks =
@@ -143,13 +178,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
     }
   };
-  auto store_tile = [&](int buf, const KVStage<D, NT, BN>& st) {
+  auto store_tile = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int c = 0; c < KVStage<D, NT, BN>::CH; ++c) {
+    for (int c = 0; c < Stage::CHK; ++c) {
       const int ch = tid + c * NT;
-      const int r = ch / (D / 16), cx = ch % (D / 16);
-      *(uint4*)(&sK[buf][r * KST + cx * 16]) = st.k[c];
-      *(uint4*)(&sV[buf][r * KST + cx * 16]) = st.v[c];
+      if (Stage::NCHK % NT == 0 || ch < Stage::NCHK)
+        *(uint4*)(&sK[buf][(ch / (KRB / 16)) * KSK + (ch % (KRB / 16)) * 16]) = st.k[c];
+    }
+#pragma unroll
+    for (int c = 0; c < Stage::CH; ++c) {
+      const int ch = tid + c * NT;
+      *(uint4*)(&sV[buf][(ch / (D / 16)) * KST + (ch % (D / 16)) * 16]) = st.v[c];
     }
     if (w == 0) {
 #pragma unroll
@@ -169,10 +208,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   v8i qa[NC];
   uint32_t qsc = 0;
   if (qi < L) {
-    const uint8_t* qp = a.q + (long)(tok0 + qi) * rowH + (long)h * D;
+    const uint8_t* qp = a.q + (long)(tok0 + qi) * rowHk + (long)h * KRB;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qa[c] = pack8(*(const uint4*)(qp + 64 * c + 16 * g), *(const uint4*)(qp + 64 * c + 32 + 16 * g));
+    for (int c = 0; c < NC; ++c) qa[c] = qk_operand<QF>(qp, c, g);
     const long srow = ((long)(srow0 + qi) * a.H + h);
     uint32_t wq = (D == 128) ? *(const uint32_t*)(a.qs + srow * 4) : *(const uint16_t*)(a.qs + srow * 2);
     qsc = wq >> (8 * g);
@@ -207,12 +245,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       uint32_t ksc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const uint8_t* kp = sKc + (kb * 32 + n) * KST + 16 * g;
+        const uint8_t* kp = sKc + (kb * 32 + n) * KSK;
         ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
         v16f acc = v16f{};
-        acc = mfma32<0, 0>(pack8(*(const uint4*)(kp), *(const uint4*)(kp + 32)), qa[0], acc, ksc[kb], qsc);
-        if constexpr (NC > 1)
-          acc = mfma32<2, 2>(pack8(*(const uint4*)(kp + 64), *(const uint4*)(kp + 96)), qa[NC - 1], acc, ksc[kb], qsc);
+        acc = mfma32<0, 0, QF>(qk_operand<QF>(kp, 0, g), qa[0], acc, ksc[kb], qsc);
+        if constexpr (NC > 1) acc = mfma32<2, 2, QF>(qk_operand<QF>(kp, 1, g), qa[NC - 1], acc, ksc[kb], qsc);
         st[kb] = acc;
       }
       const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
@@ -331,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   };
   {
-    KVStage<D, NT, BN> st0;
+    Stage st0;
     load_tile(0, st0);
     store_tile(0, st0);
   }
@@ -340,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     // the next tile's loads are in flight while this one is computed (past
     // the last tile the last one is fetched again and its buffer rewritten
     // with the same bytes, which keeps the loop free of branches around them)
-    KVStage<D, NT, BN> nxt;
+    Stage nxt;
     load_tile(min(t + 1, ntiles - 1), nxt);
     tile_body(t, t & 1);
     store_tile((t & 1) ^ 1, nxt);
@@ -379,17 +416,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st) {
+hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, int qk_fmt, FwdArgs a, int max_len, hipStream_t st) {
   constexpr int NW = 4;
   a.nqt = (max_len + 32 * NW - 1) / (32 * NW);
   const long units = (long)a.nseq * a.H;
   const long grid = ((units + 7) / 8) * 8 * a.nqt;
   if (grid == 0) return hipSuccess;
   dim3 g((unsigned)grid), b(NW * 64);
-#define MX_FWD_CASE(DD, CC, OB) \
-  if (D == DD && causal == CC && out_bf16 == OB) { attn_fwd_kernel<DD, NW, CC, OB><<<g, b, 0, st>>>(a); return hipGetLastError(); }
-  MX_FWD_CASE(64, false, false) MX_FWD_CASE(64, false, true) MX_FWD_CASE(64, true, false) MX_FWD_CASE(64, true, true)
-  MX_FWD_CASE(128, false, false) MX_FWD_CASE(128, false, true) MX_FWD_CASE(128, true, false) MX_FWD_CASE(128, true, true)
+#define MX_FWD_CASE(DD, CC, OB, QF)                                            \
+  if (D == DD && causal == CC && out_bf16 == OB && qk_fmt == QF) {              \
+    attn_fwd_kernel<DD, NW, CC, OB, QF><<<g, b, 0, st>>>(a);                    \
+    return hipGetLastError();                                                   \
+  }
+#define MX_FWD_FMTS(DD, CC, OB) \
+  MX_FWD_CASE(DD, CC, OB, 0) MX_FWD_CASE(DD, CC, OB, 2) MX_FWD_CASE(DD, CC, OB, 3) MX_FWD_CASE(DD, CC, OB, 4)
+  MX_FWD_FMTS(64, false, false) MX_FWD_FMTS(64, false, true) MX_FWD_FMTS(64, true, false) MX_FWD_FMTS(64, true, true)
+  MX_FWD_FMTS(128, false, false) MX_FWD_FMTS(128, false, true) MX_FWD_FMTS(128, true, false) MX_FWD_FMTS(128, true, true)
+#undef MX_FWD_FMTS
 #undef MX_FWD_CASE
   return hipErrorInvalidValue;
 }

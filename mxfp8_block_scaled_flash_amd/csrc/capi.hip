@@ -244,9 +244,11 @@ static mx_status fwd_common(const uint8_t* q_data, const uint8_t* q_scale, const
   return MX_OK;
 }
 
-mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data, const uint8_t* k_scale,
-                      const uint8_t* v_data, const uint8_t* v_scale, int B, int S, int H, int D,
-                      float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse, hipStream_t stream) {
+static mx_status attn_fwd_fixed(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                                const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale, int B, int S,
+                                int H, int D, float softmax_scale, int causal, int qk_fmt, void* o,
+                                mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  if (!valid_elem(qk_fmt)) return MX_EINVAL;
   if (B < 0 || S < 0) return MX_EINVAL;
   if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
@@ -262,14 +264,30 @@ mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8
   a.nseq = B;
   a.T = B * S;
   a.lse = lse;
-  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, a, S, stream));
+  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, qk_fmt, a, S, stream));
 }
 
-mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
-                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
-                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq, int total_tokens,
-                             int max_seqlen, int H, int D, float softmax_scale, int causal, void* o,
-                             mx_dtype o_dtype, float* lse, hipStream_t stream) {
+mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data, const uint8_t* k_scale,
+                      const uint8_t* v_data, const uint8_t* v_scale, int B, int S, int H, int D,
+                      float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  return attn_fwd_fixed(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal, MX_E4M3,
+                        o, o_dtype, lse, stream);
+}
+
+mx_status mx_attn_fwd_fmt(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                          const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale, int B, int S, int H,
+                          int D, float softmax_scale, int causal, mx_elem qk_format, void* o, mx_dtype o_dtype,
+                          float* lse, hipStream_t stream) {
+  return attn_fwd_fixed(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, D, softmax_scale, causal,
+                        (int)qk_format, o, o_dtype, lse, stream);
+}
+
+static mx_status attn_fwd_jagged(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                                 const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                                 int max_seqlen, int H, int D, float softmax_scale, int causal, int qk_fmt, void* o,
+                                 mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  if (!valid_elem(qk_fmt)) return MX_EINVAL;
   if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
   if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
   if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
@@ -285,7 +303,16 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, cons
   a.nseq = nseq;
   a.T = total_tokens;
   a.lse = lse;
-  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, a, max_seqlen, stream));
+  return from_hip(mxk::launch_attn_fwd(D, causal != 0, o_dtype == MX_BF16, qk_fmt, a, max_seqlen, stream));
+}
+
+mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                             const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                             int max_seqlen, int H, int D, float softmax_scale, int causal, void* o,
+                             mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  return attn_fwd_jagged(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seqlens, cu_scale_rows, nseq,
+                         total_tokens, max_seqlen, H, D, softmax_scale, causal, MX_E4M3, o, o_dtype, lse, stream);
 }
 
 static mx_status fwd_bf16_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int D,

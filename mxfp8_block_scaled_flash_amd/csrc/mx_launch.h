@@ -62,7 +62,7 @@ struct BwdArgs {
 
 hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const QuantArgs& a, hipStream_t st);
 hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipStream_t st);
-hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
+hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, int qk_fmt, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_fwd_bf16(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st);

@@ -67,6 +67,20 @@ def test_forward_rejects_invalid_arguments(bad):
     assert _fwd(**bad) == EINVAL
 
 
+@pytest.mark.parametrize("fmt", [1, 5, -1])
+def test_forward_fmt_rejects_unknown_formats(fmt):
+    # qk_format is checked before anything touches the device
+    assert mx.lib().mx_attn_fwd_fmt(*([16] * 6), 1, 64, 1, 128, 0.1, 1, fmt, 16, mx.BF16, None, None) == EINVAL
+
+
+@pytest.mark.parametrize("bad", [dict(D=32), dict(H=0), dict(S=-1), dict(sc=0.0), dict(o=None), dict(q=None)])
+def test_forward_fmt_rejects_invalid_arguments(bad):
+    a = dict(q=16, B=1, S=64, H=1, D=128, sc=0.1, o=16)
+    a.update(bad)
+    assert mx.lib().mx_attn_fwd_fmt(a["q"], 16, 16, 16, 16, 16, a["B"], a["S"], a["H"], a["D"], a["sc"], 1, mx.E2M1,
+                                    a["o"], mx.BF16, None, None) == EINVAL
+
+
 def test_varlen_rejects_invalid_arguments():
     L = mx.lib()
     # total_scale_rows not a multiple of 128, and smaller than the token count
