@@ -289,6 +289,22 @@ mx_status mx_attn_fwd_fmt(const uint8_t* q_data, const uint8_t* q_scale,
                           hipStream_t stream);
 
 /*
+ * mx_attn_fwd_fmt_varlen -- mx_attn_fwd_fmt over packed sequences (the jagged
+ * layout of mx_attn_fwd_varlen): Q, K payload rows [T, H, D*w/8] at cu_seqlens
+ * token offsets; Q, K ROW32 scale rows [Tp, H, D/32] at the 128-aligned
+ * cu_scale_rows offsets (mx_varlen_scale_offsets), pad rows ignored; V as for
+ * mx_attn_fwd_varlen; lse [H, T].  Errors as mx_attn_fwd_varlen, and MX_EINVAL
+ * for an unknown qk_format.
+ */
+mx_status mx_attn_fwd_fmt_varlen(const uint8_t* q_data, const uint8_t* q_scale,
+                                 const uint8_t* k_data, const uint8_t* k_scale,
+                                 const uint8_t* v_data, const uint8_t* v_scale,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                                 int total_tokens, int max_seqlen, int H, int D,
+                                 float softmax_scale, int causal, mx_elem qk_format,
+                                 void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
+
+/*
  * mx_attn_fwd_bf16 -- BF16 attention forward, the baseline of the pages'
  * speed-up figures ([News], headline comparison with BF16 FlashAttention-4).
  * Reading (the pages do not define it): mx_attn_fwd with every MX step

@@ -44,6 +44,8 @@ _SIGS = {
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
                            _c_int),
     "mx_attn_fwd_fmt": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _c_int, _vp, _c_int, _vp, _vp], _c_int),
+    "mx_attn_fwd_fmt_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _c_int, _vp, _c_int, _vp,
+                                                                      _vp], _c_int),
     "mx_attn_fwd_bf16": ([_vp] * 3 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_bf16_varlen": ([_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
@@ -188,6 +190,15 @@ def mx_attn_fwd_fmt(q_data, q_scale, k_data, k_scale, v_data, v_scale, B, S, H, 
     _check(lib().mx_attn_fwd_fmt(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
                                  _ptr(v_scale), B, S, H, D, float(softmax_scale), int(bool(causal)), int(qk_format),
                                  _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)), "mx_attn_fwd_fmt")
+
+
+def mx_attn_fwd_fmt_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seqlens, cu_scale_rows, nseq,
+                           total_tokens, max_seqlen, H, D, softmax_scale, causal, qk_format, o, lse, stream=None):
+    _check(lib().mx_attn_fwd_fmt_varlen(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                                        _ptr(v_scale), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq, total_tokens,
+                                        max_seqlen, H, D, float(softmax_scale), int(bool(causal)), int(qk_format),
+                                        _ptr(o), _dtype_code(o.dtype), _ptr(lse), _stream(stream)),
+           "mx_attn_fwd_fmt_varlen")
 
 
 def mx_attn_fwd_bf16(q, k, v, B, S, H, D, softmax_scale, causal, o, lse, stream=None):
@@ -336,6 +347,22 @@ def quantize_varlen(x, cu_seqlens, seqlens, layouts=ROW32 | COL32 | SQ32):
     return out, csr
 
 
+def quantize_rows_varlen(x, seqlens, fmt=E4M3):
+    """Row quantization (element format fmt) of a packed [T, H, D] tensor with its scale rows at
+    the 128-aligned per-sequence offsets of the jagged layout (one mx_quantize_rows call per
+    sequence; pad rows zero).  Returns (packed data [T, H, D w/8], scales [Tp, H, D/32])."""
+    T, H, D = x.shape
+    data = torch.empty((T, H, D * ELEM_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
+    scale = torch.zeros((padded_scale_rows(seqlens), H, D // 32), dtype=torch.uint8, device=x.device)
+    tok = srow = 0
+    for L in (int(v) for v in seqlens):
+        if L:
+            mx_quantize_rows(x[tok:tok + L], L * H, D, fmt, data[tok:tok + L], scale[srow:srow + L])
+        tok += L
+        srow += (L + 127) // 128 * 128
+    return data, scale
+
+
 def rmsnorm_quantize_varlen(x, gamma, cu_seqlens, seqlens, eps=1e-6, layouts=ROW32 | COL32 | SQ32):
     """Fused RMSNorm + MX quantization of a packed [T, H, D] tensor; returns
     ({layout: (data, scale)}, cu_scale_rows)."""
@@ -415,6 +442,19 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, 
     lse = torch.empty((H, T), dtype=torch.float32, device=q[0].device) if with_lse else None
     mx_attn_fwd_varlen(q[0], q[1], k[0], k[1], v[0], v[1], cu_seqlens, cu_scale_rows, len(seqlens), T,
                        max(seqlens), H, D, softmax_scale, causal, o, lse)
+    return o, lse
+
+
+def attn_fwd_fmt_varlen(q, k, v, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal, qk_format,
+                        out_dtype=torch.bfloat16, with_lse=True):
+    """q, k: (data, scales) from quantize_rows_varlen in element format qk_format; v: (data, scale)
+    COL32 from quantize_varlen.  Returns (O [T, H, D], LSE [H, T])."""
+    T, H = q[0].shape[:2]
+    D = q[1].shape[2] * 32
+    o = torch.empty((T, H, D), dtype=out_dtype, device=q[0].device)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q[0].device) if with_lse else None
+    mx_attn_fwd_fmt_varlen(q[0], q[1], k[0], k[1], v[0], v[1], cu_seqlens, cu_scale_rows, len(seqlens), T,
+                           max(seqlens), H, D, softmax_scale, causal, qk_format, o, lse)
     return o, lse
 
 

@@ -315,6 +315,16 @@ mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, cons
                          total_tokens, max_seqlen, H, D, softmax_scale, causal, MX_E4M3, o, o_dtype, lse, stream);
 }
 
+mx_status mx_attn_fwd_fmt_varlen(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                                 const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                                 int max_seqlen, int H, int D, float softmax_scale, int causal, mx_elem qk_format,
+                                 void* o, mx_dtype o_dtype, float* lse, hipStream_t stream) {
+  return attn_fwd_jagged(q_data, q_scale, k_data, k_scale, v_data, v_scale, cu_seqlens, cu_scale_rows, nseq,
+                         total_tokens, max_seqlen, H, D, softmax_scale, causal, (int)qk_format, o, o_dtype, lse,
+                         stream);
+}
+
 static mx_status fwd_bf16_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int D,
                                  float softmax_scale, void* o, mx_dtype o_dtype, float* lse, mxk::FwdArgs& a) {
   if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;

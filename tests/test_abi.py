@@ -73,6 +73,12 @@ def test_forward_fmt_rejects_unknown_formats(fmt):
     assert mx.lib().mx_attn_fwd_fmt(*([16] * 6), 1, 64, 1, 128, 0.1, 1, fmt, 16, mx.BF16, None, None) == EINVAL
 
 
+@pytest.mark.parametrize("fmt", [1, 5])
+def test_forward_fmt_varlen_rejects_unknown_formats(fmt):
+    assert mx.lib().mx_attn_fwd_fmt_varlen(*([16] * 6), 16, 16, 1, 10, 10, 1, 128, 0.1, 1, fmt, 16, mx.BF16, None,
+                                           None) == EINVAL
+
+
 @pytest.mark.parametrize("bad", [dict(D=32), dict(H=0), dict(S=-1), dict(sc=0.0), dict(o=None), dict(q=None)])
 def test_forward_fmt_rejects_invalid_arguments(bad):
     a = dict(q=16, B=1, S=64, H=1, D=128, sc=0.1, o=16)

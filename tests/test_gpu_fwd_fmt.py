@@ -85,3 +85,29 @@ def test_forward_fmt_with_e4m3_is_the_mxfp8_forward():
     o2, l2 = mx.attn_fwd(qq, kq, vq, 0.088, True, torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", [mx.E3M2, mx.E2M1])
+def test_forward_qk_format_varlen_sampled(fmt):
+    """Jagged layout: packed sequences (lengths 256..8192), Q, K scale rows at 128-aligned offsets."""
+    w = synth.workload("varlen")
+    sigma = 1 / math.sqrt(w.D)
+    cu = w.cu_seqlens()
+    log(f"fwd {FMTS[fmt]} varlen T={cu[-1]}")
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v")}
+    cu_d = torch.from_numpy(cu).cuda()
+    qf = mx.quantize_rows_varlen(x["q"], w.seqlens, fmt)
+    kf = mx.quantize_rows_varlen(x["k"], w.seqlens, fmt)
+    vq, csr = mx.quantize_varlen(x["v"], cu_d, w.seqlens, mx.COL32)
+    o, lse = mx.attn_fwd_fmt_varlen(qf, kf, vq[mx.COL32], cu_d, csr, w.seqlens, sigma, True, fmt, torch.float32)
+    torch.cuda.synchronize()
+    xn = {t: x[t].double().cpu().numpy() for t in x}
+    rng = np.random.default_rng(3 + fmt)
+    for s in range(len(w.seqlens)):
+        h = int(rng.integers(w.H))
+        a, b = cu[s], cu[s + 1]
+        rows = np.unique(np.concatenate([np.arange(min(40, b - a)), rng.choice(b - a, 48, replace=False)]))
+        r = at.forward_head(xn["q"][a:b, h], xn["k"][a:b, h], xn["v"][a:b, h], sigma, True, q_rows=rows,
+                            qk_fmt=FMTS[fmt])
+        check_out(o[a:b, h][rows].double().cpu().numpy(), r["O"], f"{FMTS[fmt]} varlen seq{s} h{h}")
+        check_lse(lse[h, a:b][rows].cpu().numpy(), r["LSE"], f"{FMTS[fmt]} varlen seq{s} h{h}")
