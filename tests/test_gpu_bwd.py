@@ -197,3 +197,53 @@ def test_backward_llm_shape_sampled_blocks():
         e = rel_fro(g_[rows(bl)], np.concatenate([ref[key][i] for i in bl]))
         log(f"  llm {name} blocks {bl}: rel Frobenius {e:.2e}")
         assert e <= TOL, f"llm {name}: rel Frobenius {e:.3e} > {TOL}"
+
+
+def test_backward_long_context_sampled_blocks():
+    """The long-context backward (B4 H16 S4096 D128, causal; every (tensor, head) scaled by
+    10^U(-1, 1), which stresses the E8M0 range).  Two sampled heads carry O and LSE from the oracle
+    forward, the other heads an inert filler (O = 0, LSE = 1e4: with logits up to a few hundred here,
+    their p underflows to 0 instead of overflowing).  The static dQ scale follows the
+    headroom rule from the float64 textbook dQ of the sampled heads.  dQ of sampled query blocks
+    and dK, dV of sampled key blocks are checked against the oracle's block-subset backward."""
+    w = synth.workload("long")
+    B, S, H, D = w.B, w.S, w.H, w.D
+    sigma = 1 / math.sqrt(D)
+    pairs = synth.draw_sample_pairs(w.seed, B, H, 2)
+    log(f"bwd long {w.shape()} heads {pairs}")
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, S), 1e4, device="cuda")
+    heads, mq = {}, 0.0
+    for b, h in pairs:
+        qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+        f = at.forward_head(qn, kn, vn, sigma, True, gemm="exact")
+        o_h = torch.from_numpy(f["O"].astype(np.float32)).to(torch.bfloat16)
+        lse_h = torch.from_numpy(f["LSE"].astype(np.float32))
+        o[b, :, h, :] = o_h.cuda()
+        lse[b, h, :] = lse_h.cuda()
+        on, ln = o_h.double().numpy(), lse_h.double().numpy()
+        ideal = at.backward_head(qn, kn, vn, on, dn, ln, sigma, True, quantize=False, exact=True)
+        mq = max(mq, float(np.max(np.abs(ideal["dQ"]))))
+        heads[(b, h)] = (qn, kn, vn, dn, on, ln)
+    s = dq_scale_rule(mq)
+    log(f"  max|dQ| = {mq:.3e}; static scale 2^{s}")
+    qs = mx.quantize(x["q"], mx.SQ32)[mx.SQ32]
+    ks = mx.quantize(x["k"], mx.SQ32)[mx.SQ32]
+    dos = mx.quantize(x["do"], mx.SQ32)[mx.SQ32]
+    vr = mx.quantize(x["v"], mx.ROW32)[mx.ROW32]
+    dq, dk, dv = mx.attn_bwd(qs, ks, vr, dos, o, x["do"], lse, sigma, True, s, torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    nb = S // 32
+    rows = lambda bl: np.concatenate([np.arange(32 * i, 32 * i + 32) for i in bl])  # noqa: E731
+    for (b, h), (qn, kn, vn, dn, on, ln) in heads.items():
+        gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
+        qb = sorted({0, 1, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        ref = at.backward_head_blocks(qn, kn, vn, on, dn, ln, sigma, True, q_blocks=qb, k_blocks=kb)
+        for name, g_, bl in (("dQ", gq, qb), ("dK", gk, kb), ("dV", gv, kb)):
+            e = rel_fro(g_[rows(bl)], np.concatenate([ref[name][i] for i in bl]))
+            log(f"  long b{b} h{h} {name} blocks {bl}: rel Frobenius {e:.2e}")
+            assert np.all(np.isfinite(g_[rows(bl)])), f"long {name}: non-finite values"
+            assert e <= TOL, f"long b{b} h{h} {name}: rel Frobenius {e:.3e} > {TOL}"
