@@ -118,8 +118,10 @@ def test_backward_small_causal_outliers():
     _compare_heads(gpu, ref, "small bf16")
 
 
-def test_backward_varlen():
-    seqlens = [5, 130, 300, 77, 1, 64]
+@pytest.mark.parametrize("seqlens", [[5, 130, 300, 77, 1, 64], [0, 33, 0, 200, 1, 0]])
+def test_backward_varlen(seqlens):
+    """Jagged layout; the second batch holds empty sequences (first, middle and last) and a
+    one-token one."""
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
     H, D = 2, 128
     sigma = 1 / math.sqrt(D)

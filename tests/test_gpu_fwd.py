@@ -120,3 +120,25 @@ def test_forward_is_deterministic():
     o1, l1 = _gpu_fwd(q, k, v, 0.088, True, torch.bfloat16)
     o2, l2 = _gpu_fwd(q, k, v, 0.088, True, torch.bfloat16)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("seqlens", [[1, 31, 32, 33, 200], [0, 33, 0, 200, 1, 0]])
+def test_forward_varlen_short_and_empty_sequences(seqlens):
+    """Jagged layout with tail blocks of every size, one-token and empty sequences (first, middle
+    and last): every O row and LSE entry against the oracle."""
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    H, D = 3, 64
+    sigma = 1 / math.sqrt(D)
+    g = torch.Generator().manual_seed(21)
+    q, k, v = (torch.randn(int(cu[-1]), H, D, generator=g).to(torch.bfloat16) for _ in range(3))
+    log(f"fwd varlen {seqlens}")
+    cu_d = torch.from_numpy(cu).cuda()
+    qq, csr = mx.quantize_varlen(q.cuda(), cu_d, seqlens, mx.ROW32)
+    kq, _ = mx.quantize_varlen(k.cuda(), cu_d, seqlens, mx.ROW32)
+    vq, _ = mx.quantize_varlen(v.cuda(), cu_d, seqlens, mx.COL32)
+    o, lse = mx.attn_fwd_varlen(qq[mx.ROW32], kq[mx.ROW32], vq[mx.COL32], cu_d, csr, seqlens, sigma, True,
+                                torch.float32)
+    torch.cuda.synchronize()
+    O, LSE = at.mx_attention_forward(*(t.double().numpy() for t in (q, k, v)), sigma, True, cu_seqlens=cu)
+    check_out(o.double().cpu().numpy(), O, f"varlen {seqlens}")
+    check_lse(lse.cpu().numpy(), LSE, f"varlen {seqlens}")
