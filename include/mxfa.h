@@ -61,6 +61,8 @@
  * unspecified, but no call faults.  Integer device inputs (cu_seqlens,
  * cu_scale_rows) must be consistent with the host sizes passed beside them;
  * this is the caller's responsibility (the device does not validate them).
+ * Size limits (MX_EINVAL beyond them): at most 2^40 elements per tensor,
+ * 2^31 - 1 tokens per call (B * S or total_tokens) and 2^16 heads.
  */
 #ifndef MXFA_H
 #define MXFA_H

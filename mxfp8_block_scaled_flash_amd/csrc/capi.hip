@@ -52,6 +52,10 @@ bool all_aligned(std::initializer_list<const void*> ps) {
 float log2_scale(float softmax_scale) { return softmax_scale * 1.44269504088896340736f; }
 
 constexpr long kMaxElems = 1L << 40;
+// Token indices and per-tile byte spans are 32-bit inside the kernels: at most 2^31 - 1 tokens
+// per call, and at most 2^16 heads (so a 128-row tile of one head spans less than 2^31 bytes).
+constexpr long kMaxTokens = (1L << 31) - 1;
+constexpr int kMaxHeads = 1 << 16;
 
 }  // namespace
 
@@ -78,10 +82,10 @@ namespace {
 mx_status quantize_fixed(const void* x, mx_dtype x_dtype, const float* gamma, float eps, int B, int S, int H, int D,
                          unsigned layouts, uint8_t* row32_data, uint8_t* row32_scale, uint8_t* col32_data,
                          uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
-  if (B < 0 || S < 0 || H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (B < 0 || S < 0 || H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
   if (!valid_layouts(layouts)) return MX_EINVAL;
-  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
   if (!x || !aligned16(x)) return MX_EINVAL;
   if (!layout_ptrs_ok(layouts, row32_data, row32_scale, col32_data, col32_scale, sq32_data, sq32_scale))
@@ -110,7 +114,7 @@ mx_status quantize_jagged(const void* x, mx_dtype x_dtype, const float* gamma, f
                           uint8_t* col32_scale, uint8_t* sq32_data, uint8_t* sq32_scale, hipStream_t stream) {
   if (nseq < 1 || total_tokens < 0 || total_scale_rows < 0 || total_scale_rows % 128 != 0) return MX_EINVAL;
   if (total_scale_rows < total_tokens) return MX_EINVAL;
-  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
   if (!valid_layouts(layouts)) return MX_EINVAL;
   if (!cu_seqlens || !cu_scale_rows) return MX_EINVAL;
@@ -233,7 +237,7 @@ mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const 
 static mx_status fwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
                             const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale, int H, int D,
                             float softmax_scale, void* o, mx_dtype o_dtype, mxk::FwdArgs& a) {
-  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if (o_dtype != MX_BF16 && o_dtype != MX_F32) return MX_EINVAL;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
   if (!all_aligned({q_data, q_scale, k_data, k_scale, v_data, v_scale, o})) return MX_EINVAL;
@@ -250,7 +254,7 @@ static mx_status attn_fwd_fixed(const uint8_t* q_data, const uint8_t* q_scale, c
                                 mx_dtype o_dtype, float* lse, hipStream_t stream) {
   if (!valid_elem(qk_fmt)) return MX_EINVAL;
   if (B < 0 || S < 0) return MX_EINVAL;
-  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
   mxk::FwdArgs a{};
   if (mx_status st = fwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, H, D, softmax_scale, o, o_dtype, a))
@@ -327,7 +331,7 @@ mx_status mx_attn_fwd_fmt_varlen(const uint8_t* q_data, const uint8_t* q_scale, 
 
 static mx_status fwd_bf16_common(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int D,
                                  float softmax_scale, void* o, mx_dtype o_dtype, float* lse, mxk::FwdArgs& a) {
-  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if (o_dtype != MX_BF16 && o_dtype != MX_F32) return MX_EINVAL;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
   if (!all_aligned({q, k, v, o})) return MX_EINVAL;
@@ -344,7 +348,7 @@ mx_status mx_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float softmax_scale, int causal, void* o, mx_dtype o_dtype, float* lse,
                            hipStream_t stream) {
   if (B < 0 || S < 0) return MX_EINVAL;
-  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
   mxk::FwdArgs a{};
   if (mx_status st = fwd_bf16_common(q, k, v, H, D, softmax_scale, o, o_dtype, lse, a)) return st;
@@ -385,7 +389,7 @@ static mx_status bwd_common(const uint8_t* q_data, const uint8_t* q_scale, const
                             mx_dtype io_dtype, const float* lse, int H, int D, float softmax_scale, int dq_scale_log2,
                             void* dq, void* dk, void* dv, mx_dtype grad_dtype, void* workspace,
                             size_t workspace_bytes, int tokens, mxk::BwdArgs& a) {
-  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if ((io_dtype != MX_BF16 && io_dtype != MX_F32) || (grad_dtype != MX_BF16 && grad_dtype != MX_F32)) return MX_EINVAL;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
   if (dq_scale_log2 < -15 || dq_scale_log2 > 15) return MX_EINVAL;
@@ -418,7 +422,7 @@ static mx_status bwd_bf16_common(const uint16_t* q, const uint16_t* k, const uin
                                  const uint16_t* dout, const float* lse, int H, int D, float softmax_scale, void* dq,
                                  void* dk, void* dv, mx_dtype grad_dtype, void* workspace, size_t workspace_bytes,
                                  int tokens, mxk::BwdArgs& a) {
-  if (H < 1 || (D != 64 && D != 128)) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128)) return MX_EINVAL;
   if (grad_dtype != MX_BF16 && grad_dtype != MX_F32) return MX_EINVAL;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MX_EINVAL;
   if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return MX_EINVAL;
@@ -441,7 +445,7 @@ mx_status mx_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int causal, void* dq, void* dk, void* dv, mx_dtype grad_dtype, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || S < 0) return MX_EINVAL;
-  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
   mxk::BwdArgs a{};
   if (mx_status st = bwd_bf16_common(q, k, v, o, dout, lse, H, D, softmax_scale, dq, dk, dv, grad_dtype, workspace,
@@ -481,7 +485,7 @@ mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale, const uint8
                       float softmax_scale, int causal, int dq_scale_log2, void* dq, void* dk, void* dv,
                       mx_dtype grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || S < 0) return MX_EINVAL;
-  if ((long)B * S * H * D > kMaxElems) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
   if ((long)B * S == 0) return MX_OK;
   mxk::BwdArgs a{};
   if (mx_status st = bwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout,

@@ -60,6 +60,12 @@ def _fwd(**kw):
                                 a["sc"], a["causal"], a["o"], a["odt"], a["lse"], None)
 
 
+@pytest.mark.parametrize("bad", [dict(B=2, S=1 << 30), dict(H=(1 << 16) + 1, S=32)])
+def test_forward_rejects_sizes_past_the_index_range(bad):
+    # 2^31 tokens, or more heads than a tile's 32-bit byte span allows: rejected on the host
+    assert _fwd(**bad) == EINVAL
+
+
 @pytest.mark.parametrize("bad", [dict(D=32), dict(H=0), dict(S=-1), dict(sc=0.0), dict(sc=-1.0),
                                  dict(sc=float("nan")), dict(sc=float("inf")), dict(odt=mx.F16), dict(o=None),
                                  dict(q=None), dict(vs=4), dict(lse=4)])
