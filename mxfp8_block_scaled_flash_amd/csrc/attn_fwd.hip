@@ -26,10 +26,12 @@
 //  * P is re-packed between lane halves with v_permlane32_swap so each lane
 //    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
 //    through ds_read_b64_tr_b8, in the same key order.
-//  * K and V tiles of 64 keys are staged in LDS and shared by the
-//    workgroup's waves; two LDS buffers, the next tile's global loads in
-//    flight while the current one is computed, one barrier per tile, and
-//    two workgroups per CU so one's softmax overlaps the other's MFMAs.  Workgroups are ordered so that each XCD works
+//  * K and V tiles of 128 keys go from HBM straight into LDS (16-byte buffer
+//    loads with the LDS as destination, no staging registers), into rows
+//    whose 16-byte chunks are XOR-swizzled by row so the operand reads spread
+//    over the banks; two LDS buffers, the next tile's loads in flight while
+//    the current one is computed, one barrier per tile, and two workgroups
+//    per CU so one's softmax overlaps the other's MFMAs.  Workgroups are ordered so that each XCD works
 //    through whole heads, longest (causal) query tiles first, keeping a
 //    head's K/V in that XCD's L2.
 #include "mx_common.h"
@@ -71,6 +73,22 @@ MX_DEV v8i qk_operand(const uint8_t* row, int c, int g) {
   }
 }
 
+// Operand of one QK^T product read from a K row held in LDS (layout of qk_operand), where 16-byte
+// chunk j of row r sits in slot j ^ (r & SWZ).
+template <int QF, int SWZ>
+MX_DEV v8i qk_operand_lds(const uint8_t* row, int r, int c, int g) {
+  const int x = r & SWZ;
+  if constexpr (QF == 0) {
+    return pack8(*(const uint4*)(row + 16 * ((4 * c + g) ^ x)), *(const uint4*)(row + 16 * ((4 * c + 2 + g) ^ x)));
+  } else if constexpr (qk_bits<QF>() == 6) {
+    static_assert(SWZ == 0, "MXFP6 rows are padded, not swizzled");
+    return qk_operand<QF>(row, c, g);
+  } else {
+    const uint4 v = *(const uint4*)(row + 16 * ((2 * c + g) ^ x));
+    return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  }
+}
+
 MX_DEV v2i lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
@@ -79,14 +97,10 @@ MX_DEV v2i lds_tr8(const uint8_t* p) {
 #define FWD_BN 128
 #endif
 
-// One BN-key tile of K and V in flight between HBM and LDS (K rows of KRB payload bytes).
-template <int D, int NT, int BN, int KRB>
-struct KVStage {
-  static constexpr int NCHK = BN * KRB / 16;             // 16-byte chunks of the K tile
-  static constexpr int CHK = (NCHK + NT - 1) / NT;       // per thread (threads past NCHK idle)
-  static constexpr int CH = BN * D / 16 / NT;            // 16-byte chunks of V per thread
-  static constexpr int KH = BN / 64;                     // 64-key halves: one scale word per lane and half
-  uint4 k[CHK], v[CH];
+// The E8M0 scales of one BN-key tile in flight between HBM and LDS (the payload goes by DMA).
+template <int D, int BN>
+struct ScaleStage {
+  static constexpr int KH = BN / 64;   // 64-key halves: one scale word per lane and half
   uint32_t ks[KH];
   uint32_t vb[KH][D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
 };
@@ -100,14 +114,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
   constexpr int KRB = D * qk_bits<QF>() / 8;   // payload bytes of one Q or K row
-  constexpr int KST = D + 16;   // LDS row stride of the V tile
-  constexpr int KSK = KRB + 16; // LDS row stride of the K tile
+  // K and V tiles arrive by 16-byte DMA (buffer loads straight into LDS, no staging registers).
+  // Rows of a power-of-two number of 16-byte chunks are stored unpadded with chunk j of row r in
+  // slot j ^ (r mod chunks), so the operand reads spread over the banks; MXFP6 K rows (3 or 6
+  // chunks) get one spare slot instead (a copy of the last chunk, never read), which staggers
+  // the rows across the banks.
+  constexpr int CPRV = D / 16;                        // chunks per V row
+  constexpr int CPRK = KRB / 16;                      // chunks of payload per K row
+  constexpr bool KPOW2 = (CPRK & (CPRK - 1)) == 0;
+  constexpr int SLK = KPOW2 ? CPRK : CPRK + 1;        // K row slots (MXFP6: one spare slot)
+  constexpr int KRS = 16 * SLK;                       // LDS row stride of the K tile
+  constexpr int SWZV = CPRV - 1, SWZK = KPOW2 ? SLK - 1 : 0;
+  constexpr int NBK = BN * KRS / 1024, NBV = BN * D / 1024;   // 1 KB DMA blocks (one wave instruction each)
+  static_assert(BN * KRS % 1024 == 0 && BN * D % 1024 == 0, "tiles must be whole DMA blocks");
   constexpr float kLazy = 8.f;  // largest log2 of p before the frame moves
   constexpr int NT = NW * 64;
   static_assert(BN * D / 16 % NT == 0, "tile chunks must divide among the threads");
   // two buffers: the tile being computed and the next one, written while it is computed
-  __shared__ __attribute__((aligned(16))) uint8_t sK[2][BN * KSK];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][BN * KST];
+  // one array per buffer: the LDS reads of one buffer stay independent of the DMA into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[BN * KRS];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[BN * KRS];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[BN * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[BN * D];
   __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
   __shared__ uint32_t sVs[2][BN];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
 
@@ -142,8 +170,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // wait on the loads before the tile being computed needs them.  Every wave
   // fetches the scales of key `lane`; wave 0 stores the K ones, wave 1 the V ones.
   const int KSB = D / 32;   // bytes per K ROW32 scale word
-  using Stage = KVStage<D, NT, BN, KRB>;
-  auto load_tile = [&](int t, Stage& st) {
+  using Scales = ScaleStage<D, BN>;
+  // lane l of a DMA instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block (measured)
+  auto dma_tile = [&](int t, uint8_t* dK, uint8_t* dV) {
     const int k0 = t * BN;
     const int rows = min(BN, L - k0);   // >= 1
     const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
@@ -151,18 +180,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tbk, (rows - 1) * (int)rowHk + KRB);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + tb, (rows - 1) * (int)rowH + D);
 #pragma unroll
-    for (int c = 0; c < Stage::CHK; ++c) {
-      const int ch = tid + c * NT;
-      const int off = (ch / (KRB / 16)) * (int)rowHk + (ch % (KRB / 16)) * 16;
-      if (Stage::NCHK % NT == 0 || ch < Stage::NCHK)
-        st.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    for (int j = 0; j < (NBK + NW - 1) / NW; ++j) {
+      const int blk = w + NW * j;
+      if (NBK % NW == 0 || blk < NBK) {
+        const int ch = blk * 64 + lane, r = ch / SLK;
+        const int lc = (ch % SLK) ^ (r & SWZK);   // chunk this slot holds
+        const int off = r * (int)rowHk + 16 * min(lc, CPRK - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dK + 1024 * blk), 16,
+                                                 off, 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int c = 0; c < Stage::CH; ++c) {
-      const int ch = tid + c * NT;
-      const int off = (ch / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
-      st.v[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    for (int j = 0; j < NBV / NW; ++j) {
+      const int blk = w + NW * j;
+      const int ch = blk * 64 + lane, r = ch / CPRV;
+      const int off = r * (int)rowH + 16 * ((ch % CPRV) ^ (r & SWZV));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dV + 1024 * blk), 16,
+                                               off, 0, 0, 0);
     }
+  };
+  auto load_scales = [&](int t, Scales& st) {
+    const int k0 = t * BN;
+    const int rows = min(BN, L - k0);
     const __amdgpu_buffer_rsrc_t rks =
         buffer_rsrc(a.ks + ((long)(srow0 + k0) * a.H + h) * KSB, (rows - 1) * a.H * KSB + KSB);
     const int nblk = (rows + 31) / 32;
@@ -178,18 +217,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
     }
   };
-  auto store_tile = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int c = 0; c < Stage::CHK; ++c) {
-      const int ch = tid + c * NT;
-      if (Stage::NCHK % NT == 0 || ch < Stage::NCHK)
-        *(uint4*)(&sK[buf][(ch / (KRB / 16)) * KSK + (ch % (KRB / 16)) * 16]) = st.k[c];
-    }
-#pragma unroll
-    for (int c = 0; c < Stage::CH; ++c) {
-      const int ch = tid + c * NT;
-      *(uint4*)(&sV[buf][(ch / (D / 16)) * KST + (ch % (D / 16)) * 16]) = st.v[c];
-    }
+  auto store_scales = [&](int buf, const Scales& st) {
     if (w == 0) {
 #pragma unroll
       for (int hh = 0; hh < KH; ++hh) sKs[buf][64 * hh + lane] = st.ks[hh];
@@ -238,18 +266,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 
     const bool compute = q0 < L && !(CAUSAL && k0 > q0 + 31);   // skip tiles above this wave's diagonal
     if (compute) {
-      const uint8_t* sKc = sK[cur];
-      const uint8_t* sVc = sV[cur];
+      const uint8_t* sKc = cur ? sK1 : sK0;
+      const uint8_t* sVc = cur ? sV1 : sV0;
       // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
       v16f st[KB];
       uint32_t ksc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const uint8_t* kp = sKc + (kb * 32 + n) * KSK;
+        const int kr = kb * 32 + n;
+        const uint8_t* kp = sKc + kr * KRS;
         ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
         v16f acc = v16f{};
-        acc = mfma32<0, 0, QF>(qk_operand<QF>(kp, 0, g), qa[0], acc, ksc[kb], qsc);
-        if constexpr (NC > 1) acc = mfma32<2, 2, QF>(qk_operand<QF>(kp, 1, g), qa[NC - 1], acc, ksc[kb], qsc);
+        acc = mfma32<0, 0, QF>(qk_operand_lds<QF, SWZK>(kp, kr, 0, g), qa[0], acc, ksc[kb], qsc);
+        if constexpr (NC > 1)
+          acc = mfma32<2, 2, QF>(qk_operand_lds<QF, SWZK>(kp, kr, 1, g), qa[NC - 1], acc, ksc[kb], qsc);
         st[kb] = acc;
       }
       const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
@@ -333,7 +363,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       // its two blocks, in order; then O^T += V^T P^T (V^T rows d = 32 dc + lane%32, through LDS
       // transpose reads)
       const int G = lane >> 4, i16 = lane & 15;
-      const int colofs = 16 * (G & 1) + 8 * (i16 & 1);
       const int rowofs = 16 * (G >> 1) + (i16 >> 1);
 #pragma unroll
       for (int hh = 0; hh < KH; ++hh) {
@@ -352,8 +381,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         const uint32_t vsc = sVs[cur][64 * hh + lane];
 #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
-          const uint8_t* vp = sVc + (64 * hh + rowofs) * KST + 32 * dc + colofs;
-          v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * KST), r2 = lds_tr8(vp + 32 * KST), r3 = lds_tr8(vp + 40 * KST);
+          // rows vrow, +8, +32, +40 share vrow's swizzle; chunk 2 dc + (G & 1), half i16 & 1
+          const int vrow = 64 * hh + rowofs;
+          const uint8_t* vp = sVc + vrow * D + 16 * ((2 * dc + (G & 1)) ^ (vrow & SWZV)) + 8 * (i16 & 1);
+          v2i r0 = lds_tr8(vp), r1 = lds_tr8(vp + 8 * D), r2 = lds_tr8(vp + 32 * D), r3 = lds_tr8(vp + 40 * D);
           v8i va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
           if (dc == 0) o[0] = mfma32<0, 0>(va, pb, o[0], vsc, psc);
           if (dc == 1) o[1] = mfma32<1, 0>(va, pb, o[1], vsc, psc);
@@ -368,21 +399,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   };
   {
-    Stage st0;
-    load_tile(0, st0);
-    store_tile(0, st0);
+    Scales s0;
+    load_scales(0, s0);
+    dma_tile(0, sK0, sV0);
+    store_scales(0, s0);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    // the next tile's loads are in flight while this one is computed (past
-    // the last tile the last one is fetched again and its buffer rewritten
-    // with the same bytes, which keeps the loop free of branches around them)
-    Stage nxt;
-    load_tile(min(t + 1, ntiles - 1), nxt);
-    tile_body(t, t & 1);
-    store_tile((t & 1) ^ 1, nxt);
+  // the next tile's DMA and scale loads are in flight while this one is computed (past the last
+  // tile the last one is fetched again into the free buffer, which keeps the loop free of branches
+  // around them); two tiles per iteration so each buffer is named at compile time
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    Scales s1;
+    load_scales(t + 1, s1);
+    dma_tile(t + 1, sK1, sV1);
+    tile_body(t, 0);
+    store_scales(1, s1);
+    __syncthreads();
+    const int tn = min(t + 2, ntiles - 1);
+    Scales s2;
+    load_scales(tn, s2);
+    dma_tile(tn, sK0, sV0);
+    tile_body(t + 1, 1);
+    store_scales(0, s2);
     __syncthreads();
   }
+  if (t < ntiles) tile_body(t, 0);
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (M + log2 l).  Each lane half summed
   // p over its 16 keys of every block: the row sum adds both halves.
