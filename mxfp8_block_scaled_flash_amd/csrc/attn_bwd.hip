@@ -168,13 +168,15 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int KST = D + 16;   // LDS row stride of K, V, Q, dO tiles
   constexpr int SST = BQ + 16;  // LDS row stride of the dS code tile [key][query]
   constexpr int NT = NW * 64;
-  constexpr int QCH = BQ * D / 16;    // 16-byte chunks of one Q (or dO) tile
-  constexpr int CPT = 2 * QCH / NT;   // chunks of Q and dO per thread per step
-  static_assert(2 * QCH % NT == 0, "chunks must divide among the threads");
+  constexpr int SLQ = KST / 16;                 // 16-byte slots per padded Q / dO row
+  constexpr int NBQ = BQ * KST / 1024;          // 1 KB DMA blocks per tile (one wave instruction each)
+  static_assert(BQ * KST % 1024 == 0, "tiles must be whole DMA blocks");
   __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDO[2][BQ * KST];
+  // Q^ and dO^ step tiles arrive by 16-byte DMA (buffer loads straight into LDS): a padded row
+  // is KST / 16 slots, the last one a copy of the row's last chunk (never read)
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][BQ * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][BQ * KST];
   __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * SST];   // [step parity]
   __shared__ uint32_t sKs[NW];                 // K SQ32 scale word (bytes = feature blocks) per key block
   __shared__ uint32_t sVs[BN];                 // V ROW32 scale word per key
@@ -225,7 +227,6 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
 
   // ---- staging of one query step
   struct Stage {
-    uint4 x[CPT];
     float l, d;
     uint32_t qs, dos;
   };
@@ -234,16 +235,25 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   };
   // Per-step buffer resources end with the sequence: rows, LSE/D entries and
   // scale blocks past its end read as zero (masked later), with no clamps.
-  auto load_step = [&](int q0, Stage& st) {
+  // the step's Q^ / dO^ tiles go to LDS buffer buf by DMA (lane l of an instruction fills bytes
+  // 16 l .. 16 l + 15 of its 1 KB block); LSE, D and the scales are loaded into registers
+  auto load_step = [&](int q0, int buf, Stage& st) {
     const int rows = min(BQ, L - q0);   // >= 1
     const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
     const int nrec = (rows - 1) * (int)rowH + D;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + tb, nrec), rdo = buffer_rsrc(a.dob + tb, nrec);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;   // Q chunks first, then dO (the split falls between waves)
-      const int off = ((ch % QCH) / (D / 16)) * (int)rowH + (ch % (D / 16)) * 16;
-      st.x[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(c * NT + 64 * w < QCH ? rq : rdo, off, 0, 0));
+    for (int j = 0; j < (2 * NBQ + NW - 1) / NW; ++j) {
+      const int blk = w + NW * j;               // Q blocks first, then dO
+      if (2 * NBQ % NW == 0 || blk < 2 * NBQ) {
+        const bool isq = blk < NBQ;
+        const int b = isq ? blk : blk - NBQ;
+        const int ch = b * 64 + lane, r = ch / SLQ;
+        const int off = r * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+        uint8_t* dst = (isq ? sQ[buf] : sDO[buf]) + 1024 * b;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isq ? rq : rdo, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 off, 0, 0, 0);
+      }
     }
     const long li = lse_index(q0);
     st.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + li, rows * 4), lane * 4, 0, 0));
@@ -260,13 +270,6 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     }
   };
   auto store_step = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      const int r = (ch % QCH) / (D / 16), cx = ch % (D / 16);
-      uint8_t* dst = (ch < QCH ? sQ[buf] : sDO[buf]) + r * KST + cx * 16;
-      *(uint4*)dst = st.x[c];
-    }
     if (w == 0) {
       sL[buf][lane] = st.l * 1.44269504088896340736f;
       sDv[buf][lane] = st.d;
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
 
   {
     Stage st0;
-    load_step(qstart, st0);
+    load_step(qstart, 0, st0);
     store_step(0, st0);
   }
   __syncthreads();
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     // the last step, the last one is fetched again and its buffer rewritten)
     const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
     Stage nx;
-    load_step(qn, nx);
+    load_step(qn, buf ^ 1, nx);
     if (j > 0 && w >= 4) phase_c(q0 - BQ, buf ^ 1);
     store_step(buf ^ 1, nx);
     __syncthreads();
