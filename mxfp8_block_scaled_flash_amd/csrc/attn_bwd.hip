@@ -151,9 +151,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //     every wave finished before this step began; the dS tile is
 //     double-buffered by step) and adds it to the fp16 accumulator with
 //     packed atomics.
-// The next step's Q^ / dO^ tiles, scales, LSE and D are loaded into registers
-// during the step and written to the other LDS buffer at its end: one barrier
-// per step.  Waves 0-3 run C at the start of the step and waves 4-7 at its
+// The next step's Q^ / dO^ tiles go by DMA (buffer loads with the LDS as
+// destination) into the other LDS buffer during the step, its scales, LSE and
+// D through registers stored at the step's end: one barrier per step.  Waves 0-3 run C at the start of the step and waves 4-7 at its
 // end: the two waves sharing a SIMD (w and w + 4) are then in different
 // phases, so one's matrix products overlap the other's elementwise work
 // instead of both waiting on the same unit (measured: 10.9 -> 10.0 ms).
