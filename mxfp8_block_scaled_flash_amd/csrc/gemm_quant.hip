@@ -126,11 +126,18 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   constexpr int RBK = 8 * W;                        // bytes of one row per 64-deep K step
   constexpr int KST = RBK + (W == 6 ? 32 : 16);     // LDS row stride: 16-byte aligned, rows on distinct banks
   constexpr int CPR = RBK / 16;                     // 16-byte chunks per row and step
-  constexpr int NCH = BM * CPR;                     // chunks per tile and step
-  constexpr int CPT = (NCH + NTH - 1) / NTH;        // chunks per thread
+  constexpr int SL = KST / 16;                      // 16-byte slots per padded LDS row
+  constexpr int NB = BM * KST / 1024;               // 1 KB DMA blocks per tile and step
+  static_assert(BM == BN && BM * KST % 1024 == 0 && 2 * NB % NW == 0, "tiles must be whole DMA blocks");
   static_assert(BM <= NTH, "one scale row per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * KST];
+  // A and B step tiles arrive by 16-byte DMA (buffer loads straight into LDS; lane l of an
+  // instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block): a padded row is SL slots, the
+  // ones past the payload a copy of its last chunk (never read).  One array per buffer keeps the
+  // LDS reads of one buffer independent of the DMA into the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * KST];
   __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
@@ -147,9 +154,8 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   const int rowb = K / 8 * W;   // bytes per packed row
   const int nk = K / 64;
 
-  // ---- staging: BM rows x 8w bytes of A and of B per step, in 16-byte chunks
+  // ---- staging: BM rows x 8w bytes of A and of B per step by DMA; the scale pairs in registers
   struct Stage {
-    uint4 av[CPT], bv[CPT];
     uint32_t sc;   // this thread's row's scale pair (A row tid, or B row tid - BM)
   };
   static_assert(NTH == BM + BN, "one scale row per thread");
@@ -163,16 +169,20 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   const bool wide_scales = (kb32 & 15) == 0;
   uint4 scw = make_uint4(0, 0, 0, 0);   // 8 steps of this row's scale pairs
   int kfirst = 0;                       // the first load always fetches
-  auto load = [&](int kt, Stage& st) {
+  auto dma = [&](int kt, uint8_t* dA, uint8_t* dB) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + NTH * c;   // row ch / CPR, 16-byte column ch % CPR
-      if (NCH % NTH == 0 || ch < NCH) {
-        const int off = (ch / CPR) * rowb + kt * RBK + (ch % CPR) * 16;
-        st.av[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-        st.bv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-      }
+    for (int j = 0; j < 2 * NB / NW; ++j) {
+      const int blk = w + NW * j;   // A blocks first, then B
+      const bool isa = blk < NB;
+      const int b = isa ? blk : blk - NB;
+      const int ch = b * 64 + lane, r = ch / SL;
+      const int off = r * rowb + kt * RBK + 16 * min(ch % SL, CPR - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb,
+                                               (__attribute__((address_space(3))) void*)((isa ? dA : dB) + 1024 * b),
+                                               16, off, 0, 0, 0);
     }
+  };
+  auto load = [&](int kt, Stage& st) {
     // thread t: the scale pair of A row t (t < BM) or B row t - BM.  When a row's scales are
     // 16-byte aligned (K/32 a multiple of 16) they are fetched 8 steps at a time; otherwise one
     // 16-bit load per step (K/32 is even, so a pair is 2-byte aligned).
@@ -190,14 +200,6 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
     }
   };
   auto store = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + NTH * c;
-      if (NCH % NTH == 0 || ch < NCH) {
-        *(uint4*)(&sA[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.av[c];
-        *(uint4*)(&sB[buf][(ch / CPR) * KST + (ch % CPR) * 16]) = st.bv[c];
-      }
-    }
     if (tid < BM) sAs[buf][tid] = st.sc;
     else sBs[buf][tid - BM] = st.sc;
   };
@@ -222,12 +224,12 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
     int sa[WM], sb[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      ao[i] = load_operand<FMT>(sA[cur] + (wr + 32 * i + n) * KST, g);
+      ao[i] = load_operand<FMT>((cur ? sA1 : sA0) + (wr + 32 * i + n) * KST, g);
       sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      bo[j] = load_operand<FMT>(sB[cur] + (wc + 32 * j + n) * KST, g);
+      bo[j] = load_operand<FMT>((cur ? sB1 : sB0) + (wc + 32 * j + n) * KST, g);
       sb[j] = (int)(sBs[cur][wc + 32 * j + n] >> (8 * g));
     }
 #pragma unroll
@@ -248,17 +250,29 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   {
     Stage s0;
     load(0, s0);
+    dma(0, sA0, sB0);
     store(0, s0);
   }
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    Stage nx;
-    load(min(kt + 1, nk - 1), nx);   // past the last step the last one is fetched again
-    compute(cur);
-    store(cur ^ 1, nx);
+  // two steps per iteration so each buffer is named at compile time; past the last step the last
+  // one is fetched again into the free buffer
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    Stage s1;
+    load(kt + 1, s1);
+    dma(kt + 1, sA1, sB1);
+    compute(0);
+    store(1, s1);
+    __syncthreads();
+    const int kn = min(kt + 2, nk - 1);
+    Stage s2;
+    load(kn, s2);
+    dma(kn, sA0, sB0);
+    compute(1);
+    store(0, s2);
     __syncthreads();
   }
+  if (kt < nk) compute(0);
   keep(acc[WM - 1][WN - 1][0]);
 #pragma unroll
   for (int i = 0; i < WM; ++i) keep(sa_prev[i]);
