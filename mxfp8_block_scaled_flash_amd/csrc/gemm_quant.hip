@@ -19,10 +19,11 @@
 //  * tiles in a grouped order (runs of 8 tile-rows walked column by column),
 //    each XCD (blockIdx % 8) taking a contiguous run of them, so the
 //    workgroups in flight on an XCD share A rows and B rows in its L2;
-//  * K advances 64 per step; A and B tiles (128 rows x 8w bytes for w-bit
-//    elements) and their scale pairs are staged in two LDS buffers, the next
-//    step's buffer loads in flight while the current one is multiplied, one
-//    barrier per step;
+//  * K advances 64 per step; A and B tiles (256 rows x 8w bytes for w-bit
+//    elements) go by 16-byte DMA (buffer loads with the LDS as destination)
+//    into two LDS buffers, their scale pairs through registers, the next
+//    step's loads in flight while the current one is multiplied, one barrier
+//    per step;
 //  * operand layout (measured): for E4M3 a lane of half g supplies bytes
 //    16g..16g+15 and 32+16g..32+16g+15 of its row's 64 K values; for the 6-
 //    and 4-bit formats it supplies the whole K block g (K values 32g..32g+31)
