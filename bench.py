@@ -44,8 +44,15 @@ BWD_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_flash_amd", "csrc", "attn_bw
 
 
 def source_digest(path):
+    """Digest of a source file's code: line comments, trailing blanks and empty lines removed, so
+    that an edit to the comments does not void counters taken on the same code."""
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    lines = []
+    for line in open(path).read().split("\n"):
+        line = line.split("//", 1)[0].rstrip()
+        if line.strip():
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def measured_traffic():
@@ -55,7 +62,7 @@ def measured_traffic():
         kv = dict(line[2:].split("=", 1) for line in open(TRAFFIC_FILE) if line.startswith("# ") and "=" in line)
     except OSError:
         return None
-    if kv.get("source_sha256_16", "").strip() != source_digest(BWD_SOURCE):
+    if kv.get("code_sha256_16", "").strip() != source_digest(BWD_SOURCE):
         return None
     return float(kv["bytes_per_call"])
 

@@ -136,9 +136,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ main kernel
 // One workgroup of eight waves per (sequence, head, 256-key tile), walking
-// 64-query steps.  The dQ atomics execute at the memory side (device-scope
-// atomics bypass the per-XCD L2s), so their volume -- one fp16 partial per
-// key tile and query -- bounds this kernel; 256-key tiles halve it.
+// 64-query steps.  The dQ atomics execute at the memory side (the counters
+// show none performed in the per-XCD L2s); their volume -- one fp16 partial
+// per key tile and query -- bounded this kernel at 128-key tiles; 256-key
+// tiles halve it, and the staggered dQ phase hides most of what remains.
 // Wave w owns key block w (32 keys; lane = one key) for the whole walk:
 //  A. per query block t = 0, 1: S = Q^ K^T and dP = dO^ V^T (keys as the
 //     output columns), p and dS, their MX codes (P: one scale per key and 32
