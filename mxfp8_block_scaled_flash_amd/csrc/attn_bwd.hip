@@ -158,6 +158,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // end: the two waves sharing a SIMD (w and w + 4) are then in different
 // phases, so one's matrix products overlap the other's elementwise work
 // instead of both waiting on the same unit (measured: 10.9 -> 10.0 ms).
+// The two halves run separate copies of the step loop, and only waves 0-3
+// issue the next step's loads: a wave's waits on its own loads also wait on
+// the atomics it issued after them, so waves 4-7, whose atomics come last,
+// load nothing and reach the barrier without waiting on memory.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int NW = 8;
@@ -238,15 +242,16 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   // scale blocks past its end read as zero (masked later), with no clamps.
   // the step's Q^ / dO^ tiles go to LDS buffer buf by DMA (lane l of an instruction fills bytes
   // 16 l .. 16 l + 15 of its 1 KB block); LSE, D and the scales are loaded into registers
-  auto load_step = [&](int q0, int buf, Stage& st) {
+  auto load_step = [&](int q0, int buf, Stage& st, auto dma_waves) {
+    constexpr int DW = decltype(dma_waves)::value;   // waves 0 .. DW-1 share the DMA
     const int rows = min(BQ, L - q0);   // >= 1
     const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
     const int nrec = (rows - 1) * (int)rowH + D;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + tb, nrec), rdo = buffer_rsrc(a.dob + tb, nrec);
 #pragma unroll
-    for (int j = 0; j < (2 * NBQ + NW - 1) / NW; ++j) {
-      const int blk = w + NW * j;               // Q blocks first, then dO
-      if (2 * NBQ % NW == 0 || blk < 2 * NBQ) {
+    for (int j = 0; j < (2 * NBQ + DW - 1) / DW; ++j) {
+      const int blk = w + DW * j;               // Q blocks first, then dO
+      if (w < DW && (2 * NBQ % DW == 0 || blk < 2 * NBQ)) {
         const bool isq = blk < NBQ;
         const int b = isq ? blk : blk - NBQ;
         const int ch = b * 64 + lane, r = ch / SLQ;
@@ -256,18 +261,23 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
                                                  off, 0, 0, 0);
       }
     }
-    const long li = lse_index(q0);
-    st.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + li, rows * 4), lane * 4, 0, 0));
-    st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.Dbuf + li, rows * 4), lane * 4, 0, 0));
-    const long so = ((long)(sblk0 + q0 / 32) * a.H + h) * NB;
-    const int snrec = ((rows + 31) / 32 - 1) * a.H * NB + NB;
-    const int soff = (lane & 1) * a.H * NB;
-    if constexpr (NB == 4) {
-      st.qs = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
-      st.dos = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
-    } else {
-      st.qs = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
-      st.dos = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
+    // LSE and D by wave 0, the scales by wave 1: the waves that store them
+    st = Stage{0.f, 0.f, 0u, 0u};
+    if (w == 0) {
+      const long li = lse_index(q0);
+      st.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.lse + li, rows * 4), lane * 4, 0, 0));
+      st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.Dbuf + li, rows * 4), lane * 4, 0, 0));
+    } else if (w == 1) {
+      const long so = ((long)(sblk0 + q0 / 32) * a.H + h) * NB;
+      const int snrec = ((rows + 31) / 32 - 1) * a.H * NB + NB;
+      const int soff = (lane & 1) * a.H * NB;
+      if constexpr (NB == 4) {
+        st.qs = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
+        st.dos = __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
+      } else {
+        st.qs = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.qs + so, snrec), soff, 0, 0);
+        st.dos = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(a.dos + so, snrec), soff, 0, 0);
+      }
     }
   };
   auto store_step = [&](int buf, const Stage& st) {
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
 
   {
     Stage st0;
-    load_step(qstart, 0, st0);
+    load_step(qstart, 0, st0, std::integral_constant<int, NW>{});
     store_step(0, st0);
   }
   __syncthreads();
@@ -354,143 +364,154 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
 
   };
 
-  for (int j = 0; j < nsteps; ++j) {
-    const int q0 = qstart + j * BQ, buf = j & 1;
-    const uint8_t* sQb = sQ[buf];
-    const uint8_t* sDOb = sDO[buf];
-    if (j > 0 && w < 4) phase_c(q0 - BQ, buf ^ 1);   // half the waves: the previous step's dQ first
-    // ---- A. S and dP for (key block w, query block t): element e = query q0 + 32t + 8(e/4) + 4g + e%4
-    v8i pB, sB;        // P and dS codes as B operands: bytes 16t + 0..15 = queries 32t + 16g + 0..15
-    int kpc[2], ksc2[2];
-    const bool live = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);   // a key of the block sees a query
-    if (live) {
-      const uint8_t* kr = sK + (32 * w + n) * KST + 16 * g;
-      const uint8_t* vr = sV + (32 * w + n) * KST + 16 * g;
-      const uint32_t ksc = sKs[w] >> (8 * g), vsc = sVs[32 * w + n] >> (8 * g);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int qa0 = q0 + 32 * t;
-        const bool act = qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
-        const bool edge = !act || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
-        // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
-        const int lo = (!act || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
-        const int hi = L - qa0 - 4 * g;
-        const uint32_t qsa = sQs[buf][t] >> (8 * g), dsa = sDOs[buf][t] >> (8 * g);
-        // computed for every block (rows past either end are zero, so the values are
-        // finite); the mask zeroes p and dS where nothing is visible
-        const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
-        const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
-        v16f st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
-                                pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), v16f{}, qsa, ksc);
-        v16f dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
-                                 pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), v16f{}, dsa, vsc);
-        if constexpr (NC > 1) {
-          st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
-                             pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
-          dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
-                              pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
-        }
-        // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D); two copies of the
-        // pass: with the mask (diagonal, edge or empty blocks) and without.  LSE and D are read
-        // four queries at a time, in two halves fenced off from each other (fewer live registers).
-        float am = -INFINITY, sm = 0.f;
-        auto pass = [&](auto masked) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q == 2) __builtin_amdgcn_sched_barrier(0);
-            const float4 l4 = *(const float4*)(&sL[buf][32 * t + 8 * q + 4 * g]);
-            const float4 d4 = *(const float4*)(&sDv[buf][32 * t + 8 * q + 4 * g]);
-            const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 4 * q + r;
-              float arg = fmaf(st[e], cl, -lq[r]);
-              if constexpr (decltype(masked)::value) {
-                const int ce = 8 * q + r;
-                arg = (ce >= lo && ce < hi) ? arg : -INFINITY;
-              }
-              const float p = __builtin_amdgcn_exp2f(arg);
-              const float ds = p * (dpt[e] - dq[r]);
-              st[e] = p;
-              dpt[e] = ds;
-              am = fmaxf(am, arg);
-              sm = fmaxf(sm, fabsf(ds));
-            }
+  // The step loop in two copies, one per half of the workgroup: waves 0-3 (EARLY) run C first and
+  // issue every load of the next step; waves 4-7 run C last and load nothing, so no wait for a
+  // load of theirs can hold them behind their own atomics.
+  auto walk = [&](auto early) {
+    constexpr bool EARLY = decltype(early)::value;
+    for (int j = 0; j < nsteps; ++j) {
+      const int q0 = qstart + j * BQ, buf = j & 1;
+      const uint8_t* sQb = sQ[buf];
+      const uint8_t* sDOb = sDO[buf];
+      if (EARLY && j > 0) phase_c(q0 - BQ, buf ^ 1);   // half the waves: the previous step's dQ first
+      // ---- A. S and dP for (key block w, query block t): element e = query q0 + 32t + 8(e/4) + 4g + e%4
+      v8i pB, sB;        // P and dS codes as B operands: bytes 16t + 0..15 = queries 32t + 16g + 0..15
+      int kpc[2], ksc2[2];
+      const bool live = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);   // a key of the block sees a query
+      if (live) {
+        const uint8_t* kr = sK + (32 * w + n) * KST + 16 * g;
+        const uint8_t* vr = sV + (32 * w + n) * KST + 16 * g;
+        const uint32_t ksc = sKs[w] >> (8 * g), vsc = sVs[32 * w + n] >> (8 * g);
+  #pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int qa0 = q0 + 32 * t;
+          const bool act = qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
+          const bool edge = !act || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
+          // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
+          const int lo = (!act || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
+          const int hi = L - qa0 - 4 * g;
+          const uint32_t qsa = sQs[buf][t] >> (8 * g), dsa = sDOs[buf][t] >> (8 * g);
+          // computed for every block (rows past either end are zero, so the values are
+          // finite); the mask zeroes p and dS where nothing is visible
+          const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
+          const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
+          v16f st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
+                                  pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), v16f{}, qsa, ksc);
+          v16f dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
+                                   pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), v16f{}, dsa, vsc);
+          if constexpr (NC > 1) {
+            st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
+                               pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
+            dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
+                                pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
           }
-        };
-        if (edge) pass(std::true_type{});
-        else pass(std::false_type{});
-        const float amax = half_swap_max(am);   // 32 queries of this key
-        const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
-        // S and dP have been read: their products (and every earlier one) are done
-        keep(qsa); keep(dsa); keep(ksc); keep(vsc);
-        keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
-        // ---- MX codes (nothing visible: zero codes, scale 1)
-        const int kp = max(exp2_scale_code(amax), 1);
-        const int ks2 = max(scale_code(smax), 1);
-        const float psc = e8m0_f32(kp), ssc = e8m0_f32(ks2);   // the converts saturate (wave MODE)
-        uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // the two converts fill both halves, so any register serves as the old value
-          v2s z = __builtin_bit_cast(v2s, st[4 * q]);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
-          z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
-          pw[q] = __builtin_bit_cast(uint32_t, z);
-          v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
-          y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
-          sw[q] = __builtin_bit_cast(uint32_t, y);
+          // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D); two copies of the
+          // pass: with the mask (diagonal, edge or empty blocks) and without.  LSE and D are read
+          // four queries at a time, in two halves fenced off from each other (fewer live registers).
+          float am = -INFINITY, sm = 0.f;
+          auto pass = [&](auto masked) {
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (q == 2) __builtin_amdgcn_sched_barrier(0);
+              const float4 l4 = *(const float4*)(&sL[buf][32 * t + 8 * q + 4 * g]);
+              const float4 d4 = *(const float4*)(&sDv[buf][32 * t + 8 * q + 4 * g]);
+              const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int e = 4 * q + r;
+                float arg = fmaf(st[e], cl, -lq[r]);
+                if constexpr (decltype(masked)::value) {
+                  const int ce = 8 * q + r;
+                  arg = (ce >= lo && ce < hi) ? arg : -INFINITY;
+                }
+                const float p = __builtin_amdgcn_exp2f(arg);
+                const float ds = p * (dpt[e] - dq[r]);
+                st[e] = p;
+                dpt[e] = ds;
+                am = fmaxf(am, arg);
+                sm = fmaxf(sm, fabsf(ds));
+              }
+            }
+          };
+          if (edge) pass(std::true_type{});
+          else pass(std::false_type{});
+          const float amax = half_swap_max(am);   // 32 queries of this key
+          const float smax = wave_max_nonneg(sm);  // 32 queries x 32 keys
+          // S and dP have been read: their products (and every earlier one) are done
+          keep(qsa); keep(dsa); keep(ksc); keep(vsc);
+          keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
+          // ---- MX codes (nothing visible: zero codes, scale 1)
+          const int kp = max(exp2_scale_code(amax), 1);
+          const int ks2 = max(scale_code(smax), 1);
+          const float psc = e8m0_f32(kp), ssc = e8m0_f32(ks2);   // the converts saturate (wave MODE)
+          uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // the two converts fill both halves, so any register serves as the old value
+            v2s z = __builtin_bit_cast(v2s, st[4 * q]);
+            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
+            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
+            pw[q] = __builtin_bit_cast(uint32_t, z);
+            v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
+            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
+            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
+            sw[q] = __builtin_bit_cast(uint32_t, y);
+          }
+          // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
+          auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+          auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+          auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+          auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+          pB[4 * t + 0] = a02[0]; pB[4 * t + 1] = a02[1]; pB[4 * t + 2] = a13[0]; pB[4 * t + 3] = a13[1];
+          sB[4 * t + 0] = b02[0]; sB[4 * t + 1] = b02[1]; sB[4 * t + 2] = b13[0]; sB[4 * t + 3] = b13[1];
+          *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+          if (lane == 0) sDSs[buf][t][w] = ks2;
+          kpc[t] = kp;
+          ksc2[t] = ks2;
         }
-        // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
-        auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-        auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-        auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
-        auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
-        pB[4 * t + 0] = a02[0]; pB[4 * t + 1] = a02[1]; pB[4 * t + 2] = a13[0]; pB[4 * t + 3] = a13[1];
-        sB[4 * t + 0] = b02[0]; sB[4 * t + 1] = b02[1]; sB[4 * t + 2] = b13[0]; sB[4 * t + 3] = b13[1];
-        *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
-        if (lane == 0) sDSs[buf][t][w] = ks2;
-        kpc[t] = kp;
-        ksc2[t] = ks2;
-      }
-      // ---- B. dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries;
-      // lane half g supplies the scale of query block g)
-      const int pscale = g ? kpc[1] : kpc[0];
-      const int sscale = g ? ksc2[1] : ksc2[0];
-      const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
-#pragma unroll
-      for (int dc = 0; dc < ND; ++dc) {
-        const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
-        const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
-        if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, sB, dkt[0], qw, sscale); }
-        if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, sB, dkt[1], qw, sscale); }
-        if constexpr (ND > 2) {
-          if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pB, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, sB, dkt[2], qw, sscale); }
-          if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pB, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, sB, dkt[3], qw, sscale); }
+        // ---- B. dV^T += dO^T P^ and dK^T += Q^T dS^ (rows: features, contraction: the 64 queries;
+        // lane half g supplies the scale of query block g)
+        const int pscale = g ? kpc[1] : kpc[0];
+        const int sscale = g ? ksc2[1] : ksc2[0];
+        const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
+  #pragma unroll
+        for (int dc = 0; dc < ND; ++dc) {
+          const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
+          const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
+          if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, sB, dkt[0], qw, sscale); }
+          if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, sB, dkt[1], qw, sscale); }
+          if constexpr (ND > 2) {
+            if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pB, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, sB, dkt[2], qw, sscale); }
+            if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pB, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, sB, dkt[3], qw, sscale); }
+          }
+        }
+        dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
+      } else {
+        // every key of the block comes after every query of the step: dS is zero
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        uint8_t* rowp = sDS[buf] + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
+        *(uint4*)rowp = z;
+        *(uint4*)(rowp + 16) = z;
+        if (lane == 0) {
+          sDSs[buf][0][w] = 1;
+          sDSs[buf][1][w] = 1;
         }
       }
-      dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
-    } else {
-      // every key of the block comes after every query of the step: dS is zero
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      uint8_t* rowp = sDS[buf] + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
-      *(uint4*)rowp = z;
-      *(uint4*)(rowp + 16) = z;
-      if (lane == 0) {
-        sDSs[buf][0][w] = 1;
-        sDSs[buf][1][w] = 1;
+      // waves 0-3 fetch the next step's operands while waves 4-7 form their dQ tiles (after
+      // the last step, the last one is fetched again and its buffer rewritten)
+      const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
+      if constexpr (EARLY) {
+        Stage nx;
+        load_step(qn, buf ^ 1, nx, std::integral_constant<int, 4>{});
+        store_step(buf ^ 1, nx);
+      } else {
+        if (j > 0) phase_c(q0 - BQ, buf ^ 1);
       }
+      __syncthreads();
     }
-    // the next step's operands are in flight during the dQ products and atomics (after
-    // the last step, the last one is fetched again and its buffer rewritten)
-    const int qn = qstart + min(j + 1, nsteps - 1) * BQ;
-    Stage nx;
-    load_step(qn, buf ^ 1, nx);
-    if (j > 0 && w >= 4) phase_c(q0 - BQ, buf ^ 1);
-    store_step(buf ^ 1, nx);
-    __syncthreads();
-  }
+  };
+  if (w < 4) walk(std::true_type{});
+  else walk(std::false_type{});
   phase_c(qstart + (nsteps - 1) * BQ, (nsteps - 1) & 1);
 
   // ---- epilogue: dK = softmax_scale * dK^T, dV = dV^T, features 32 dc + 8q + 4g + 0..3 of key kj
