@@ -44,14 +44,17 @@ BWD_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_flash_amd", "csrc", "attn_bw
 
 
 def source_digest(path):
-    """Digest of a source file's code: line comments, trailing blanks and empty lines removed, so
-    that an edit to the comments does not void counters taken on the same code."""
+    """Digest of a source file's code and of the extra flags it is built with: line comments,
+    trailing blanks and empty lines removed, so that an edit to the comments does not void counters
+    taken on the same code, while a change of its build flags does."""
     import hashlib
+    from mxfp8_block_scaled_flash_amd import build as mxbuild
     lines = []
     for line in open(path).read().split("\n"):
         line = line.split("//", 1)[0].rstrip()
         if line.strip():
             lines.append(line)
+    lines.append("flags: " + " ".join(mxbuild.FILE_FLAGS.get(os.path.basename(path), [])))
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
