@@ -172,13 +172,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   const int KSB = D / 32;   // bytes per K ROW32 scale word
   using Scales = ScaleStage<D, BN>;
   // lane l of a DMA instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block (measured)
-  auto dma_tile = [&](int t, uint8_t* dK, uint8_t* dV) {
-    const int k0 = t * BN;
-    const int rows = min(BN, L - k0);   // >= 1
-    const long tb = (long)(tok0 + k0) * rowH + (long)h * D;
-    const long tbk = (long)(tok0 + k0) * rowHk + (long)h * KRB;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.k + tbk, (rows - 1) * (int)rowHk + KRB);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + tb, (rows - 1) * (int)rowH + D);
+  const int kend = CAUSAL ? min(L, qbase + BM) : L;   // keys this workgroup visits
+  const int ntiles = (kend + BN - 1) / BN;
+  // The next tile to load: its index and wave-uniform pointers to its K, V rows and scales of this
+  // head, advanced by one tile per load with 64-bit scalar adds (a product of tile index and row
+  // stride per load would be computed on the vector unit and moved back to scalar registers).
+  // Tiles load in order 0, 1, ..., the last one possibly twice.
+  struct NextTile {
+    const uint8_t *k, *v, *ks, *vs;
+    int t;
+  };
+  NextTile nt{a.k + (long)tok0 * rowHk + (long)h * KRB, a.v + (long)tok0 * rowH + (long)h * D,
+              a.ks + ((long)srow0 * a.H + h) * KSB, a.vs + ((long)sblk0 * a.H + h) * D, 0};
+  const long kstep = (long)BN * rowHk, vstep = (long)BN * rowH;
+  const long ksstep = (long)BN * a.H * KSB, vsstep = (long)KB * a.H * D;
+  auto advance = [&]() {
+    if (nt.t + 1 < ntiles) {
+      ++nt.t;
+      nt.k += kstep;
+      nt.v += vstep;
+      nt.ks += ksstep;
+      nt.vs += vsstep;
+    }
+  };
+  auto dma_tile = [&](uint8_t* dK, uint8_t* dV) {
+    const int rows = min(BN, L - nt.t * BN);   // >= 1
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(nt.k, (rows - 1) * (int)rowHk + KRB);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(nt.v, (rows - 1) * (int)rowH + D);
 #pragma unroll
     for (int j = 0; j < (NBK + NW - 1) / NW; ++j) {
       const int blk = w + NW * j;
@@ -199,14 +219,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                                                off, 0, 0, 0);
     }
   };
-  auto load_scales = [&](int t, Scales& st) {
-    const int k0 = t * BN;
-    const int rows = min(BN, L - k0);
-    const __amdgpu_buffer_rsrc_t rks =
-        buffer_rsrc(a.ks + ((long)(srow0 + k0) * a.H + h) * KSB, (rows - 1) * a.H * KSB + KSB);
+  auto load_scales = [&](Scales& st) {
+    const int rows = min(BN, L - nt.t * BN);
+    const __amdgpu_buffer_rsrc_t rks = buffer_rsrc(nt.ks, (rows - 1) * a.H * KSB + KSB);
     const int nblk = (rows + 31) / 32;
-    const __amdgpu_buffer_rsrc_t rvs =
-        buffer_rsrc(a.vs + ((long)(sblk0 + KB * t) * a.H + h) * D, (nblk - 1) * a.H * D + D);
+    const __amdgpu_buffer_rsrc_t rvs = buffer_rsrc(nt.vs, (nblk - 1) * a.H * D + D);
 #pragma unroll
     for (int hh = 0; hh < KH; ++hh) {
       const int kk = 64 * hh + lane;   // key of this lane in the tile
@@ -247,8 +264,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int c = 0; c < NC; ++c) qa[c] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
-  const int kend = CAUSAL ? min(L, qbase + BM) : L;
-  const int ntiles = (kend + BN - 1) / BN;
 
   v16f o[ND];
 #pragma unroll
@@ -400,8 +415,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   };
   {
     Scales s0;
-    load_scales(0, s0);
-    dma_tile(0, sK0, sV0);
+    load_scales(s0);
+    dma_tile(sK0, sV0);
+    advance();
     store_scales(0, s0);
   }
   __syncthreads();
@@ -411,15 +427,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
     Scales s1;
-    load_scales(t + 1, s1);
-    dma_tile(t + 1, sK1, sV1);
+    load_scales(s1);
+    dma_tile(sK1, sV1);
+    advance();
     tile_body(t, 0);
     store_scales(1, s1);
     __syncthreads();
-    const int tn = min(t + 2, ntiles - 1);
     Scales s2;
-    load_scales(tn, s2);
-    dma_tile(tn, sK0, sV0);
+    load_scales(s2);
+    dma_tile(sK0, sV0);
+    advance();
     tile_body(t + 1, 1);
     store_scales(0, s2);
     __syncthreads();
