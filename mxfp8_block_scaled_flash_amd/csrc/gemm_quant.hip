@@ -165,7 +165,11 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.b + (long)n0 * rowb, rowsB * rowb);
   const __amdgpu_buffer_rsrc_t ras = buffer_rsrc(a.as + (long)m0 * kb32, rowsA * kb32);
   const __amdgpu_buffer_rsrc_t rbs = buffer_rsrc(a.bs + (long)n0 * kb32, rowsB * kb32);
-  const __amdgpu_buffer_rsrc_t rsc = tid < BM ? ras : rbs;   // wave-uniform (waves 0-3: A, 4-7: B)
+  // waves 0 .. BM/64 - 1 load A scales, the rest B scales: chosen by the scalar wave index, so the
+  // resource stays in scalar registers (chosen by tid, it is per-lane to the compiler, and every
+  // load through it becomes a loop over the distinct resources followed by a wait for the data)
+  static_assert(BM % 64 == 0, "A and B scale rows split at a wave boundary");
+  const __amdgpu_buffer_rsrc_t rsc = w < BM / 64 ? ras : rbs;
   const int srow = tid < BM ? tid : tid - BM;
   const bool wide_scales = (kb32 & 15) == 0;
   uint4 scw = make_uint4(0, 0, 0, 0);   // 8 steps of this row's scale pairs
