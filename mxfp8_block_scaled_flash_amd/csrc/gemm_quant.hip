@@ -21,9 +21,9 @@
 //    workgroups in flight on an XCD share A rows and B rows in its L2;
 //  * K advances 64 per step; A and B tiles (256 rows x 8w bytes for w-bit
 //    elements) go by 16-byte DMA (buffer loads with the LDS as destination)
-//    into two LDS buffers, their scale pairs through registers, the next
-//    step's loads in flight while the current one is multiplied, one barrier
-//    per step;
+//    into three LDS buffers, their scale pairs through registers; the DMA for
+//    step k + 2 is in flight while step k is multiplied, and each step ends
+//    with a wait that leaves that DMA outstanding, then a barrier;
 //  * operand layout (measured): for E4M3 a lane of half g supplies bytes
 //    16g..16g+15 and 32+16g..32+16g+15 of its row's 64 K values; for the 6-
 //    and 4-bit formats it supplies the whole K block g (K values 32g..32g+31)
@@ -139,7 +139,9 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * KST];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * KST];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * KST];
-  __shared__ uint32_t sAs[2][BM], sBs[2][BN];   // the two scale bytes of a row for this K step
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[BM * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[BN * KST];
+  __shared__ uint32_t sAs[3][BM], sBs[3][BN];   // the two scale bytes of a row for this K step
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
 
   // ---- staging: BM rows x 8w bytes of A and of B per step by DMA; the scale pairs in registers
   struct Stage {
-    uint32_t sc;   // this thread's row's scale pair (A row tid, or B row tid - BM)
+    uint32_t sc;   // this thread's row's scale pair (A row tid, or B row tid - BM), or with
+    int sub;       // wide scales, the step's position in the 16 bytes held in scw
   };
   static_assert(NTH == BM + BN, "one scale row per thread");
   const int rowsA = min(BM, a.M - m0), rowsB = min(BN, a.N - n0);
@@ -197,16 +200,25 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
         scw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsc, off - 2 * (kt & 7), 0, 0));
         kfirst = -1;
       }
-      const int sub = kt & 7;
-      const uint32_t wd = sub < 4 ? (sub < 2 ? scw.x : scw.y) : (sub < 6 ? scw.z : scw.w);
-      st.sc = (wd >> (16 * (sub & 1))) & 0xFFFFu;
+      st.sub = kt & 7;   // the pair is taken from scw when stored (no wait on the load here)
     } else {
       st.sc = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
     }
   };
   auto store = [&](int buf, const Stage& st) {
-    if (tid < BM) sAs[buf][tid] = st.sc;
-    else sBs[buf][tid - BM] = st.sc;
+    uint32_t sc = st.sc;
+    if (wide_scales) {
+      // pair `sub` of scw.  The words pass through an empty asm statement as separate values: a
+      // selection among elements of one vector is folded into an indexed read, which the compiler
+      // serves from a copy of the vector in memory.
+      const int sub = st.sub;
+      uint32_t w0 = scw.x, w1 = scw.y, w2 = scw.z, w3 = scw.w;
+      asm("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+      const uint32_t lo = (sub & 4) ? w2 : w0, hi = (sub & 4) ? w3 : w1;
+      sc = (uint32_t)(((uint64_t)hi << 32 | lo) >> (16 * (sub & 3))) & 0xFFFFu;
+    }
+    if (tid < BM) sAs[buf][tid] = sc;
+    else sBs[buf][tid - BM] = sc;
   };
 
   // acc[i][j]: C block (rows m0 + wr + 32 i, columns n0 + wc + 32 j); element e of
@@ -223,18 +235,22 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
 #pragma unroll
   for (int j = 0; j < WN; ++j) sb_prev[j] = 0;
 
+  // the three step buffers, each its own array (named by a constant at every use, so the LDS reads
+  // of one buffer carry no dependence on the DMA into another)
+  auto bufA = [&](int c) -> uint8_t* { return c == 0 ? sA0 : (c == 1 ? sA1 : sA2); };
+  auto bufB = [&](int c) -> uint8_t* { return c == 0 ? sB0 : (c == 1 ? sB1 : sB2); };
   // one 64-deep step from LDS buffer cur: operands, then the WM x WN products
   auto compute = [&](const int cur) __attribute__((always_inline)) {
     v8i ao[WM], bo[WN];
     int sa[WM], sb[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      ao[i] = load_operand<FMT>((cur ? sA1 : sA0) + (wr + 32 * i + n) * KST, g);
+      ao[i] = load_operand<FMT>(bufA(cur) + (wr + 32 * i + n) * KST, g);
       sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      bo[j] = load_operand<FMT>((cur ? sB1 : sB0) + (wc + 32 * j + n) * KST, g);
+      bo[j] = load_operand<FMT>(bufB(cur) + (wc + 32 * j + n) * KST, g);
       sb[j] = (int)(sBs[cur][wc + 32 * j + n] >> (8 * g));
     }
 #pragma unroll
@@ -252,32 +268,54 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
       sb_prev[j] = sb[j];
     }
   };
+  // Three buffers, two steps of DMA in flight: step kt computes from buffer kt % 3 while the DMA for
+  // step kt + 2 fills buffer (kt + 2) % 3 (read last in step kt - 1, before the barrier that ended
+  // it).  A step ends with a wait for everything but its own DMA (so the DMA for step kt + 1 and
+  // the scale loads have landed, and its LDS accesses are done) and a barrier; a __syncthreads()
+  // there would also wait for this step's DMA, one step of prefetch only (measured: 30% of the
+  // kernel's time is then DMA latency).
+  constexpr int NDMA = 2 * NB / NW;   // DMA instructions per wave and step
+  static_assert(NDMA < 64, "vmcnt field");
+  auto end_step = [&](bool dma_in_flight) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no LDS access moves across the barrier
+    // s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4 (not waited), lgkmcnt 11:8 (0)
+    if (dma_in_flight) __builtin_amdgcn_s_waitcnt((NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4));
+    else __builtin_amdgcn_s_waitcnt(7 << 4);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
   {
-    Stage s0;
+    Stage s0, s1;
     load(0, s0);
     dma(0, sA0, sB0);
+    if (nk > 1) {
+      load(1, s1);
+      dma(1, sA1, sB1);
+    }
     store(0, s0);
+    if (nk > 1) store(1, s1);
   }
   __syncthreads();
-  // two steps per iteration so each buffer is named at compile time; past the last step the last
-  // one is fetched again into the free buffer
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    Stage s1;
-    load(kt + 1, s1);
-    dma(kt + 1, sA1, sB1);
-    compute(0);
-    store(1, s1);
-    __syncthreads();
-    const int kn = min(kt + 2, nk - 1);
+  auto step = [&](int kt, auto cur_c) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value, NXT = (CUR + 2) % 3;
+    const bool ahead = kt + 2 < nk;
     Stage s2;
-    load(kn, s2);
-    dma(kn, sA0, sB0);
-    compute(1);
-    store(0, s2);
-    __syncthreads();
+    if (ahead) {
+      load(kt + 2, s2);
+      dma(kt + 2, bufA(NXT), bufB(NXT));
+    }
+    compute(CUR);
+    if (ahead) store(NXT, s2);
+    end_step(ahead);
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 3) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
   }
-  if (kt < nk) compute(0);
+  if (kt < nk) step(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   keep(acc[WM - 1][WN - 1][0]);
 #pragma unroll
   for (int i = 0; i < WM; ++i) keep(sa_prev[i]);
