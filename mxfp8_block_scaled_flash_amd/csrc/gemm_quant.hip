@@ -11,11 +11,11 @@
 // e.g. for the projections that feed the attention operands).
 //
 // gfx950 design:
-//  * workgroup = 4 waves = one 256 x 256 tile of C; wave w holds the 128 x 128
-//    sub-tile (rows 128 (w/2), columns 128 (w%2)) as 4 x 4 accumulators of
-//    v_mfma_scale_f32_32x32x64_f8f6f4 (in AGPRs: one wave per SIMD, up to
-//    512 registers), so 8 operand reads from LDS feed 16 products per
-//    64-deep step and barrier;
+//  * workgroup = 8 waves = one 256 x 256 tile of C, two waves per SIMD; wave w
+//    holds the 128 x 64 sub-tile (rows 128 (w/4), columns 64 (w%4)) as 4 x 2
+//    accumulators of v_mfma_scale_f32_32x32x64_f8f6f4, so 6 operand reads
+//    from LDS feed 8 products per 64-deep step, and one wave's reads and
+//    waits overlap the other's products on the SIMD;
 //  * tiles in a grouped order (runs of 8 tile-rows walked column by column),
 //    each XCD (blockIdx % 8) taking a contiguous run of them, so the
 //    workgroups in flight on an XCD share A rows and B rows in its L2;
@@ -41,10 +41,8 @@
 #include "mx_common.h"
 #include "mx_launch.h"
 
-// workgroup tile BT x BT of C; GEMM_NW waves arranged (GEMM_NW / 2) x 2 ... see gemm_quant_kernel
-#ifndef GEMM_NW
+// waves per workgroup: one thread per scale row of the A and B tiles (256 + 256)
 #define GEMM_NW 8
-#endif
 
 namespace mxk {
 
@@ -116,11 +114,10 @@ MX_DEV v8i load_operand(const uint8_t* row, int g) {
 
 template <int FMT>
 __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a) {
-  // 256 x 256 tile of C.  4 waves: 2 x 2 waves of 128 x 128 (4 x 4 blocks, one wave per SIMD);
-  // 8 waves: 2 x 4 waves of 128 x 64 (4 x 2 blocks, two waves per SIMD, so one wave's operand
-  // reads and waits overlap the other's products).
+  // 256 x 256 tile of C: 2 x 4 waves of 128 x 64 (4 x 2 blocks, two waves per SIMD, so one
+  // wave's operand reads and waits overlap the other's products).
   constexpr int NW = GEMM_NW, NTH = 64 * NW;
-  constexpr int WM = 4, WN = NW == 4 ? 4 : 2;   // 32 x 32 blocks per wave along M and N
+  constexpr int WM = 4, WN = 2;   // 32 x 32 blocks per wave along M and N
   constexpr int WCOLS = 256 / (32 * WN);        // waves along N
   constexpr int BM = 256, BN = 256;
   constexpr int W = fmt_bits<FMT>();
