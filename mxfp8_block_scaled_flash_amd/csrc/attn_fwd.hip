@@ -73,18 +73,18 @@ MX_DEV v8i qk_operand(const uint8_t* row, int c, int g) {
   }
 }
 
-// Operand of one QK^T product read from a K row held in LDS (layout of qk_operand), where 16-byte
-// chunk j of row r sits in slot j ^ (r & SWZ).
-template <int QF, int SWZ>
-MX_DEV v8i qk_operand_lds(const uint8_t* row, int r, int c, int g) {
-  const int x = r & SWZ;
+// Operand of one QK^T product read from a K tile in LDS at precomputed lane byte offsets (o0: the
+// first chunk or the whole operand, o1: the second E4M3 chunk).
+template <int QF>
+MX_DEV v8i qk_operand_at(const uint8_t* tile, int o0, int o1) {
   if constexpr (QF == 0) {
-    return pack8(*(const uint4*)(row + 16 * ((4 * c + g) ^ x)), *(const uint4*)(row + 16 * ((4 * c + 2 + g) ^ x)));
+    return pack8(*(const uint4*)(tile + o0), *(const uint4*)(tile + o1));
   } else if constexpr (qk_bits<QF>() == 6) {
-    static_assert(SWZ == 0, "MXFP6 rows are padded, not swizzled");
-    return qk_operand<QF>(row, c, g);
+    const uint2* p = (const uint2*)(tile + o0);
+    const uint2 x = p[0], y = p[1], z = p[2];
+    return v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
   } else {
-    const uint4 v = *(const uint4*)(row + 16 * ((2 * c + g) ^ x));
+    const uint4 v = *(const uint4*)(tile + o0);
     return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 }
@@ -249,6 +249,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // lane byte offsets of the QK operand chunks in a K tile (row n of key block 0): key block kb adds
+  // 32 kb rows, a whole number of swizzle periods, so its chunks sit at a constant distance.  An
+  // empty asm statement hides their arithmetic, so each tile's reads use these four registers plus
+  // constant offsets (otherwise every read's full address is kept or recomputed).
+  static_assert(32 % (SWZK + 1) == 0, "key blocks span whole swizzle periods");
+  int kofs[NC][2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int x = n & SWZK;
+    if constexpr (QF == 0) {
+      kofs[c][0] = n * KRS + 16 * ((4 * c + g) ^ x);
+      kofs[c][1] = n * KRS + 16 * ((4 * c + 2 + g) ^ x);
+      asm("" : "+v"(kofs[c][0]), "+v"(kofs[c][1]));
+    } else if constexpr (qk_bits<QF>() == 6) {
+      kofs[c][0] = n * KRS + 24 * (2 * c + g);
+      kofs[c][1] = 0;
+      asm("" : "+v"(kofs[c][0]));
+    } else {
+      kofs[c][0] = n * KRS + 16 * ((2 * c + g) ^ x);
+      kofs[c][1] = 0;
+      asm("" : "+v"(kofs[c][0]));
+    }
+  }
+
   // ---- Q as the B operand (resident for the whole key loop)
   v8i qa[NC];
   uint32_t qsc = 0;
@@ -288,13 +312,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       uint32_t ksc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int kr = kb * 32 + n;
-        const uint8_t* kp = sKc + kr * KRS;
+        const uint8_t* kt = sKc + kb * 32 * KRS;
         ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
         v16f acc = v16f{};
-        acc = mfma32<0, 0, QF>(qk_operand_lds<QF, SWZK>(kp, kr, 0, g), qa[0], acc, ksc[kb], qsc);
+        acc = mfma32<0, 0, QF>(qk_operand_at<QF>(kt, kofs[0][0], kofs[0][1]), qa[0], acc, ksc[kb], qsc);
         if constexpr (NC > 1)
-          acc = mfma32<2, 2, QF>(qk_operand_lds<QF, SWZK>(kp, kr, 1, g), qa[NC - 1], acc, ksc[kb], qsc);
+          acc = mfma32<2, 2, QF>(qk_operand_at<QF>(kt, kofs[NC - 1][0], kofs[NC - 1][1]), qa[NC - 1], acc, ksc[kb], qsc);
         st[kb] = acc;
       }
       const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
