@@ -238,7 +238,8 @@ mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale,
  * paragraph (P converted to MXFP8, its scales taken from the max the
  * softmax already computed).
  * Computation per (b, h), with c = fl32(softmax_scale * log2(e)):
- *   S = Q^ K^T (Q^, K^ ROW32, exact-ish fp32 MFMA accumulation);
+ *   S = Q^ K^T (Q^, K^ ROW32; the scaled MFMA's fp32 result, within the stated product
+ *   error bound of the exact sum -- see the oracle's reading of the matrix unit);
  *   M_i = ceil(fl32(max_j S_ij * c)) (an integer frame);
  *   p_ij = 2^(S_ij c - M_i) (fp32), l_i = sum_j p_ij;
  *   P^ = MX(p) in blocks of 32 keys per query (aligned at key 0);
@@ -335,12 +336,34 @@ mx_status mx_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const ui
                                   void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
 
 /*
- * mx_attn_bwd_workspace_bytes -- device scratch mx_attn_bwd needs:
- * an fp16 dQ accumulator of tokens x H x D halves (head-major [H, tokens,
- * D], internal) and D_i [B, H, S] fp32 (or [H, T]), each 256-byte aligned.
- * tokens = B*S or T.
+ * mx_attn_bwd_workspace_bytes -- device scratch mx_attn_bwd and
+ * mx_attn_bwd_varlen need ([News], forward/backward paragraph: dQ is reduced
+ * in FP16 under a static scale, which needs an fp16 accumulator beside the
+ * outputs).  Layout (internal): a 256-byte slot holding the fp16 range flag
+ * (see mx_attn_bwd_overflow), the fp16 dQ accumulator of tokens x H x D
+ * halves (head-major [H, tokens, D]) and D_i [B, H, S] fp32 (or [H, T]), each
+ * part 256-byte aligned.  tokens = B*S or T.  Returns 0 for tokens < 0,
+ * H < 1 or D < 1.  No allocation; no error state.
  */
 size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D);
+
+/*
+ * mx_attn_bwd_overflow -- did the last mx_attn_bwd / mx_attn_bwd_varlen on
+ * this workspace leave fp16's range?  The pages keep dQ in FP16 under a
+ * static power-of-two scale because dQ values are consistently small ([News],
+ * forward/backward paragraph); when they are not, a scaled dQ partial beyond
+ * 65504 would saturate and the fp16 accumulator would reach infinity.  The
+ * backward detects both on the GPU and records them in the workspace's flag
+ * slot (cleared at the start of every backward call with at least one
+ * token); the returned dQ is then not valid and the caller should repeat the
+ * call with a smaller dq_scale_log2.
+ *   workspace  the device workspace the backward was given (16-byte aligned)
+ *   overflow   host int: set to 1 if the flag is raised, else 0
+ *   stream     the stream the backward ran on: the call copies the flag on it
+ *              and synchronizes that stream (it blocks the host).
+ * Errors: MX_EINVAL (null or misaligned pointer), MX_EHIP (copy failed).
+ */
+mx_status mx_attn_bwd_overflow(const void* workspace, int* overflow, hipStream_t stream);
 
 /*
  * mx_attn_bwd_bf16_workspace_bytes -- device scratch mx_attn_bwd_bf16 needs:
@@ -402,7 +425,9 @@ mx_status mx_attn_bwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const ui
  *   lse              [B, H, S] fp32 from the forward
  *   dq_scale_log2    in [-15, 15]
  *   dq, dk, dv       [B, S, H, D] in grad_dtype (MX_BF16 or MX_F32)
- *   workspace        >= mx_attn_bwd_workspace_bytes(B*S, H, D) bytes
+ *   workspace        >= mx_attn_bwd_workspace_bytes(B*S, H, D) bytes; a dQ
+ *                    partial or accumulator beyond fp16's range raises its
+ *                    flag (mx_attn_bwd_overflow), never a status here
  */
 mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale,
                       const uint8_t* k_data, const uint8_t* k_scale,

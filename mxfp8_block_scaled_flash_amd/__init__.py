@@ -49,6 +49,7 @@ _SIGS = {
     "mx_attn_fwd_bf16": ([_vp] * 3 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_bf16_varlen": ([_vp] * 4 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_bwd_workspace_bytes": ([_c_int, _c_int, _c_int], _c_size),
+    "mx_attn_bwd_overflow": ([_vp, _vp, _vp], _c_int),
     "mx_attn_bwd_bf16_workspace_bytes": ([_c_int, _c_int], _c_size),
     "mx_attn_bwd_bf16": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int] + [_vp] * 3 + [_c_int, _vp, _c_size, _vp],
                          _c_int),
@@ -235,6 +236,13 @@ def mx_attn_bwd_bf16_varlen(q, k, v, o, dout, lse, cu_seqlens, nseq, total_token
 
 def mx_attn_bwd_workspace_bytes(tokens, H, D) -> int:
     return lib().mx_attn_bwd_workspace_bytes(tokens, H, D)
+
+
+def mx_attn_bwd_overflow(workspace, stream=None) -> bool:
+    """True if the last backward on this workspace left fp16's range (blocks on the stream)."""
+    flag = ctypes.c_int(0)
+    _check(lib().mx_attn_bwd_overflow(_ptr(workspace), ctypes.byref(flag), _stream(stream)), "mx_attn_bwd_overflow")
+    return bool(flag.value)
 
 
 def mx_attn_bwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse, B, S, H, D,
@@ -458,24 +466,29 @@ def attn_fwd_fmt_varlen(q, k, v, cu_seqlens, cu_scale_rows, seqlens, softmax_sca
     return o, lse
 
 
-def attn_bwd(q, k, v, do, o, dout, lse, softmax_scale, causal, dq_scale_log2, grad_dtype=torch.bfloat16):
+def attn_bwd(q, k, v, do, o, dout, lse, softmax_scale, causal, dq_scale_log2, grad_dtype=torch.bfloat16,
+             with_overflow=False):
     """q, k, do: (data, scale) SQ32; v: (data, scale) ROW32; o, dout: [B,S,H,D]; lse [B,H,S].
-    Returns (dQ, dK, dV)."""
+    Returns (dQ, dK, dV), plus the fp16 range flag (mx_attn_bwd_overflow) with with_overflow=True."""
     B, S, H, D = q[0].shape
     dev = q[0].device
     dq, dk, dv = (torch.empty((B, S, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
     ws = torch.empty(mx_attn_bwd_workspace_bytes(B * S, H, D), dtype=torch.uint8, device=dev)
     mx_attn_bwd(q[0], q[1], k[0], k[1], v[0], v[1], do[0], do[1], o, dout, lse, B, S, H, D, softmax_scale, causal,
                 dq_scale_log2, dq, dk, dv, ws)
+    if with_overflow:
+        return dq, dk, dv, mx_attn_bwd_overflow(ws)
     return dq, dk, dv
 
 
 def attn_bwd_varlen(q, k, v, do, o, dout, lse, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal,
-                    dq_scale_log2, grad_dtype=torch.bfloat16):
+                    dq_scale_log2, grad_dtype=torch.bfloat16, with_overflow=False):
     T, H, D = q[0].shape
     dev = q[0].device
     dq, dk, dv = (torch.empty((T, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
     ws = torch.empty(mx_attn_bwd_workspace_bytes(T, H, D), dtype=torch.uint8, device=dev)
     mx_attn_bwd_varlen(q[0], q[1], k[0], k[1], v[0], v[1], do[0], do[1], o, dout, lse, cu_seqlens, cu_scale_rows,
                        len(seqlens), T, max(seqlens), H, D, softmax_scale, causal, dq_scale_log2, dq, dk, dv, ws)
+    if with_overflow:
+        return dq, dk, dv, mx_attn_bwd_overflow(ws)
     return dq, dk, dv

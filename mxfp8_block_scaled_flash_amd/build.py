@@ -69,7 +69,8 @@ def build(verbose: bool = False) -> str:
 
 def _build_test_probe(verbose: bool = False) -> None:
     """tests/hw/libmfmaprobe.so: runs the scaled-MFMA instruction alone, for the
-    GPU test that checks the oracle's accumulation model (test infrastructure)."""
+    GPU tests that measure the instruction against the oracle's stated product bound
+    (test infrastructure)."""
     src = os.path.join(ROOT, "tests", "hw", "mfma_probe.hip")
     if not os.path.exists(src):
         return

@@ -115,8 +115,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
             bf16_lo(x.w) * bf16_lo(y.w) + bf16_hi(x.w) * bf16_hi(y.w);
     }
     // zero this row's fp16 dQ accumulator (D halves; the accumulator is head-major [H, T, D]),
-    // when the caller's path has one
+    // when the caller's path has one, and clear the range flag
     if (a.acc) {
+      if (row == 0 && c == 0) *a.ovf = 0u;
       uint4 z = make_uint4(0, 0, 0, 0);
       uint16_t* accp = (uint16_t*)a.acc + ((row % a.H) * (long)a.T + row / a.H) * D;
       for (int i = c; i < D / 8; i += LPR) *(uint4*)(accp + i * 8) = z;
@@ -344,6 +345,12 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         const uint32_t lofs = (uint32_t)(4 * g + odd) * rh + (uint32_t)(n - odd);
         const int rows_left = L - q0 - 32 * t - 4 * g - odd;   // element rows c_e below this are in range
         const float mult = a.dq_mult;
+        // a scaled partial beyond fp16's largest finite value would saturate in the convert (the
+        // wave's MODE): report it through the range flag instead of passing it on silently
+        float big = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) big = fmaxf(big, fabsf(acc[e]));
+        if (big * mult > 65504.f) *a.ovf = 1u;
         auto add_tile = [&](auto checked) {
 #pragma unroll
           for (int e = 0; e < 16; e += 2) {
@@ -549,6 +556,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n8) {
   const long src = ((row % a.H) * (long)a.T + row / a.H) * (D / 8) + i % (D / 8);
   const uint4 raw = *((const uint4*)a.acc + src);
   const _Float16* hp = (const _Float16*)&raw;
+  // an accumulator at fp16's largest finite magnitude, infinite or NaN has left the range the
+  // static scale was meant to keep it in (read off the bits: the kernel is built without NaN
+  // semantics)
+  const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+  bool out_of_range = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    out_of_range |= (w4[j] & 0x7FFFu) >= 0x7BFFu || ((w4[j] >> 16) & 0x7FFFu) >= 0x7BFFu;
+  if (out_of_range) *a.ovf = 1u;
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = (float)hp[e] * a.dq_unscale;

@@ -377,10 +377,23 @@ mx_status mx_attn_fwd_bf16_varlen(const uint16_t* q, const uint16_t* k, const ui
   return from_hip(mxk::launch_attn_fwd_bf16(D, causal != 0, o_dtype == MX_BF16, a, max_seqlen, stream));
 }
 
+// Backward workspace: the fp16 range flag (one 256-byte slot at offset 0), the fp16 dQ accumulator,
+// D_i; each part 256-byte aligned.
+static constexpr size_t kFlagBytes = 256;
+
 size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D) {
   if (tokens < 0 || H < 1 || D < 1) return 0;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  return up((size_t)tokens * H * D * 2) + up((size_t)tokens * H * 4);
+  return kFlagBytes + up((size_t)tokens * H * D * 2) + up((size_t)tokens * H * 4);
+}
+
+mx_status mx_attn_bwd_overflow(const void* workspace, int* overflow, hipStream_t stream) {
+  if (!workspace || !overflow || !aligned16(workspace)) return MX_EINVAL;
+  uint32_t flag = 0;
+  if (hipMemcpyAsync(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess) return MX_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MX_EHIP;
+  *overflow = flag != 0;
+  return MX_OK;
 }
 
 static mx_status bwd_common(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
@@ -408,8 +421,9 @@ static mx_status bwd_common(const uint8_t* q_data, const uint8_t* q_scale, const
   a.grad_f32 = grad_dtype == MX_F32;
   a.dq = dq; a.dk = dk; a.dv = dv;
   const size_t acc_bytes = ((size_t)tokens * H * D * 2 + 255) / 256 * 256;
-  a.acc = workspace;
-  a.Dbuf = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + acc_bytes);
+  a.ovf = static_cast<uint32_t*>(workspace);
+  a.acc = static_cast<uint8_t*>(workspace) + kFlagBytes;
+  a.Dbuf = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kFlagBytes + acc_bytes);
   return MX_OK;
 }
 

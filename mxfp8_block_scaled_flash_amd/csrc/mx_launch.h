@@ -58,6 +58,8 @@ struct BwdArgs {
   void *dq, *dk, *dv;
   void* acc;            // fp16 dQ accumulator [tokens, H, D] (workspace)
   float* Dbuf;          // D_i (workspace), indexed like lse
+  uint32_t* ovf;        // fp16 dQ range flag (workspace): set to 1 when a scaled partial or the
+                        // accumulator leaves fp16's finite range (MX path only)
 };
 
 hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const QuantArgs& a, hipStream_t st);

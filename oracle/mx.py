@@ -264,3 +264,53 @@ def quantize_varlen(x, cu_seqlens, layouts=("row32", "col32", "sq32")):
             codes[cu[s]:cu[s + 1]] = c
         out[lay] = (codes, sc)
     return out
+
+
+# ------------------------------------------------ admissible MX roundings
+def element_magnitude(codes, k_elem):
+    """2**(binade exponent) of each E4M3 element incl. its block scale (0 for zero codes); k_elem is
+    the element's E8M0 code (already expanded to the codes' shape)."""
+    codes = np.asarray(codes)
+    e = e4m3_exponent(codes) + np.asarray(k_elem).astype(np.int64) - E8M0_BIAS
+    return np.where((codes & 0x7F) != 0, np.exp2(e.astype(np.float64)), 0.0)
+
+
+def block_max_2d(x, bq: int, bk: int):
+    """Maximum of x [n, m] over blocks of bq rows x bk columns aligned at (0, 0) (short tail blocks)."""
+    x = np.asarray(x, np.float64)
+    n, m = x.shape
+    xp = np.full(((n + bq - 1) // bq * bq, (m + bk - 1) // bk * bk), -np.inf)
+    xp[:n, :m] = x
+    return xp.reshape(xp.shape[0] // bq, bq, xp.shape[1] // bk, bk).max(axis=(1, 3))
+
+
+def expand_2d(kb, bq: int, bk: int, shape):
+    return np.repeat(np.repeat(np.asarray(kb), bq, axis=0), bk, axis=1)[:shape[0], :shape[1]]
+
+
+def round_interval(lo, hi, bq: int, bk: int, floor_codes=(0, 1)):
+    """MX rounding of a 2-D array known only up to intervals: each element lies anywhere in
+    [lo, hi], blocks are bq x bk (aligned at (0, 0)), and each block's scale follows from its own
+    (unknown) amax by the rule above.  Encoding is monotone in the value for a fixed scale, so the
+    rounded value of an element lies between the smallest rounding of lo and the largest rounding of
+    hi over the scale codes the block's amax interval allows.  ``floor_codes`` lists the smallest
+    scale codes an implementation may substitute for code 0 (blocks whose amax is below 2^-118,
+    whose contributions are below 2^-118 of the block's binade).  Returns (qlo, qhi, khi) with khi
+    the largest admissible scale code per element."""
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    alo = np.where(lo > 0, lo, np.where(hi < 0, -hi, 0.0))
+    ahi = np.maximum(np.abs(lo), np.abs(hi))
+    klo = expand_2d(scale_code(block_max_2d(alo, bq, bk)).astype(np.int64), bq, bk, lo.shape)
+    khi = expand_2d(scale_code(block_max_2d(ahi, bq, bk)).astype(np.int64), bq, bk, lo.shape)
+    qlo = np.full(lo.shape, np.inf)
+    qhi = np.full(lo.shape, -np.inf)
+    span = int(np.max(khi - klo)) if lo.size else 0
+    for d in range(span + 1):
+        k = np.minimum(klo + d, khi)
+        for f in floor_codes:
+            kk = np.maximum(k, f).astype(np.float64)
+            s = np.exp2(kk - E8M0_BIAS)
+            qlo = np.minimum(qlo, e4m3_decode(e4m3_encode(lo / s)) * s)
+            qhi = np.maximum(qhi, e4m3_decode(e4m3_encode(hi / s)) * s)
+    return qlo, qhi, np.maximum(khi, max(floor_codes))

@@ -127,6 +127,7 @@ class Workload:
     outlier_rate: float = 0.0      # Bernoulli rate of entries multiplied by outlier_mult
     outlier_mult: float = 50.0
     head_scale: bool = False       # per-(tensor, head) scale 10**U(-1, 1)
+    grid: bool = False             # values +-(1 + m/8), m = 0..7, instead of normals
     seqlens: list = field(default_factory=list)  # varlen lengths (empty = fixed)
 
     @property
@@ -169,6 +170,9 @@ def workload(name: str) -> Workload:
         return Workload(name, 2, 8, 8192, 32, 128, causal=True)
     if name == "long":       # B4 H16 S4096 D128 causal, per-head log-uniform scales
         return Workload(name, 3, 4, 4096, 16, 128, causal=True, head_scale=True)
+    if name == "grid":       # B2 H4 S1000 D128 causal, values +-(1 + m/8): every block scale equal and
+        # every product of two elements in two adjacent binades, so a matrix unit adds them exactly
+        return Workload(name, 5, 2, 1000, 4, 128, causal=True, grid=True)
     if name == "varlen":     # 16 sequences, lengths U{256..8192}, H16 D128 causal
         seed = 4
         return Workload(name, seed, 16, 0, 16, 128, causal=True, seqlens=draw_seqlens(seed, 16, 256, 8192))
@@ -198,11 +202,27 @@ def _finish_np(w: Workload, which: str, z: np.ndarray, idx: np.ndarray, head: np
     return x32 if w.dtype == "fp32" else x32.to(torch.bfloat16)
 
 
+def grid_np(seed: int, stream: int, idx: np.ndarray) -> np.ndarray:
+    """+-(1 + m/8): u = uniform draw, j = floor(16 u); sign - for j >= 8, m = j mod 8."""
+    j = np.floor(uniform_np(seed, stream, idx) * 16.0)
+    return np.where(j >= 8, -1.0, 1.0) * (1.0 + np.mod(j, 8.0) / 8.0)
+
+
+def grid_torch(seed: int, stream: int, idx):
+    import torch
+    j = torch.floor(uniform_torch(seed, stream, idx) * 16.0)
+    return torch.where(j >= 8, -1.0, 1.0).to(torch.float64) * (1.0 + torch.remainder(j, 8.0) / 8.0)
+
+
+def _draw_np(w: Workload, which: str, idx: np.ndarray) -> np.ndarray:
+    return (grid_np if w.grid else normal_np)(w.seed, _tensor_id(which), idx)
+
+
 def tensor_np(w: Workload, which: str):
     """The whole input tensor on the CPU (torch, float32 or bfloat16)."""
     n = w.numel()
     idx = np.arange(n, dtype=np.uint64)
-    z = normal_np(w.seed, _tensor_id(which), idx)
+    z = _draw_np(w, which, idx)
     head = (np.arange(n) // w.D) % w.H
     return _finish_np(w, which, z, idx, head).reshape(w.shape())
 
@@ -213,7 +233,17 @@ def head_slice_np(w: Workload, which: str, b: int, h: int):
     s = np.arange(w.S, dtype=np.uint64)[:, None]
     d = np.arange(w.D, dtype=np.uint64)[None, :]
     idx = ((np.uint64(b) * np.uint64(w.S) + s) * np.uint64(w.H) + np.uint64(h)) * np.uint64(w.D) + d
-    z = normal_np(w.seed, _tensor_id(which), idx)
+    z = _draw_np(w, which, idx)
+    return _finish_np(w, which, z, idx, np.full(idx.shape, h))
+
+
+def token_slice_np(w: Workload, which: str, t0: int, t1: int, h: int):
+    """Tokens t0..t1-1 (flat token index: b * S + s, or the packed position) of head h, [t1 - t0, D],
+    on the CPU; the same bits as the whole tensor's slice."""
+    t = np.arange(t0, t1, dtype=np.uint64)[:, None]
+    d = np.arange(w.D, dtype=np.uint64)[None, :]
+    idx = (t * np.uint64(w.H) + np.uint64(h)) * np.uint64(w.D) + d
+    z = _draw_np(w, which, idx)
     return _finish_np(w, which, z, idx, np.full(idx.shape, h))
 
 
@@ -225,7 +255,7 @@ def tensor_torch(w: Workload, which: str, device, chunk: int = 1 << 26):
     hs = torch.tensor(head_scales_np(w, which), dtype=torch.float64, device=device)
     for s0 in range(0, n, chunk):
         idx = torch.arange(s0, min(n, s0 + chunk), dtype=torch.int64, device=device)
-        z = normal_torch(w.seed, _tensor_id(which), idx)
+        z = (grid_torch if w.grid else normal_torch)(w.seed, _tensor_id(which), idx)
         if w.outlier_rate > 0:
             u = uniform_torch(w.seed, STREAM_OUTLIER, idx + _tensor_id(which) * n)
             z = torch.where(u < w.outlier_rate, z * w.outlier_mult, z)

@@ -211,3 +211,55 @@ def test_library_has_no_unresolved_kernel_stubs():
     out = subprocess.run(["nm", "-D", mx._LIB_PATH], capture_output=True, text=True).stdout
     missing = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
     assert not missing, missing
+
+
+def test_workspace_layout_has_the_range_flag_slot():
+    # 256-byte flag slot + fp16 accumulator + D_i, each 256-byte aligned
+    assert mx.lib().mx_attn_bwd_workspace_bytes(64, 1, 128) == 256 + 64 * 128 * 2 + 256
+    assert mx.lib().mx_attn_bwd_workspace_bytes(0, 1, 128) == 256
+
+
+def test_mx_backward_rejects_invalid_arguments():
+    """mx_attn_bwd checks shapes, dtypes, the softmax and dQ scales, pointers and the workspace on
+    the host, before anything touches a device."""
+    L = mx.lib()
+    n = L.mx_attn_bwd_workspace_bytes(64, 1, 128)
+    args = [16] * 8 + [16, 16, mx.BF16, 16, 1, 64, 1, 128, 0.1, 1, 8, 16, 16, 16, mx.BF16, 16, n, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return L.mx_attn_bwd(*a)
+    for bad in (dict(a15=96), dict(a14=0), dict(a12=-1), dict(a13=-5), dict(a16=0.0), dict(a16=float("nan")),
+                dict(a18=16), dict(a18=-16), dict(a10=mx.F16), dict(a22=mx.F16), dict(a0=None), dict(a7=None),
+                dict(a8=None), dict(a11=None), dict(a19=None), dict(a3=24), dict(a9=40), dict(a14=(1 << 16) + 1),
+                dict(a12=2, a13=1 << 30)):
+        assert call(**bad) == EINVAL, bad
+    assert call(a23=None) == EWORKSPACE and call(a23=24) == EWORKSPACE and call(a24=n - 1) == EWORKSPACE
+    assert call(a12=0) == 0 and call(a13=0) == 0
+
+
+def test_mx_backward_varlen_rejects_invalid_arguments():
+    L = mx.lib()
+    n = L.mx_attn_bwd_workspace_bytes(64, 1, 128)
+    args = [16] * 8 + [16, 16, mx.BF16, 16, 16, 16, 2, 64, 40, 1, 128, 0.1, 1, 8, 16, 16, 16, mx.BF16, 16, n, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return L.mx_attn_bwd_varlen(*a)
+    for bad in (dict(a12=None), dict(a13=None), dict(a14=0), dict(a15=-1), dict(a16=-1), dict(a18=80),
+                dict(a19=-1.0), dict(a21=20), dict(a10=mx.F16), dict(a0=None), dict(a22=None)):
+        assert call(**bad) == EINVAL, bad
+    assert call(a26=None) == EWORKSPACE and call(a27=n - 1) == EWORKSPACE
+    assert call(a15=0) == 0 and call(a16=0) == 0
+
+
+def test_overflow_query_rejects_bad_pointers():
+    L = mx.lib()
+    flag = ctypes.c_int(0)
+    assert L.mx_attn_bwd_overflow(None, ctypes.byref(flag), None) == EINVAL
+    assert L.mx_attn_bwd_overflow(16, None, None) == EINVAL
+    assert L.mx_attn_bwd_overflow(24, ctypes.byref(flag), None) == EINVAL

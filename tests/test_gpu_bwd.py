@@ -1,8 +1,13 @@
 """GPU parity: the fused MXFP8 attention backward against the oracle.
 
-Both sides receive the same bytes: Q, K, V, dO from the seeded generator,
-O (rounded to the GPU's bf16) and LSE (fp32) from the oracle's forward.
-dQ, dK, dV must match within 5e-3 relative Frobenius error per tensor."""
+Both sides receive the same bytes: Q, K, V, dO from the seeded generator, O (bf16) and LSE
+(fp32) from the oracle's forward.  The oracle computes the plain definition (every product the
+exact sum, rounded once to fp32).  The matrix unit's S' and dP may differ from it by up to the
+stated bound (oracle/gemm.py), which can move P and dS codes, so the gradients are several-valued:
+per head, the part of each of dQ, dK, dV outside the oracle's admissible interval
+(backward_bounds) must stay within 5e-3 relative Frobenius error of the exact gradient (the plain
+error is logged beside it).  On the grid workload every code-deciding product is exact on the
+matrix unit, and the gradients meet the plain bar against the exact oracle with no widening."""
 import math
 
 import numpy as np
@@ -13,7 +18,7 @@ import mxfp8_block_scaled_flash_amd as mx
 import synth
 from oracle import attention as at
 
-from mxtest import log, rel_fro
+from mxtest import check_grad_bounds, log, oracle_forward_head, rel_fro
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -22,61 +27,42 @@ TOL = 5e-3
 def _fwd_inputs(q, k, v, sigma, causal, cu=None):
     """O (bf16) and LSE (fp32) from the oracle forward, as bytes both sides receive."""
     qn, kn, vn = (t.double().numpy() for t in (q, k, v))
-    if cu is None:
-        O = np.zeros(qn.shape)
-        LSE = np.zeros((qn.shape[0], qn.shape[2], qn.shape[1]))
-        for b in range(qn.shape[0]):
-            for h in range(qn.shape[2]):
-                r = at.forward_head(qn[b, :, h], kn[b, :, h], vn[b, :, h], sigma, causal, gemm="exact")
-                O[b, :, h], LSE[b, h] = r["O"], r["LSE"]
-    else:
-        O, LSE = at.mx_attention_forward(qn, kn, vn, sigma, causal, cu_seqlens=cu)
+    O, LSE = at.mx_attention_forward(qn, kn, vn, sigma, causal, cu_seqlens=cu)
     o = torch.from_numpy(O.astype(np.float32)).to(torch.bfloat16)
     lse = torch.from_numpy(LSE.astype(np.float32))
     return o, lse
 
 
-def _gpu_bwd(q, k, v, do, o, lse, sigma, causal, s, grad_dtype):
-    dev = "cuda"
+def _quantize_bwd(q, k, v, do, dev="cuda"):
     qs = mx.quantize(q.to(dev), mx.SQ32)[mx.SQ32]
     ks = mx.quantize(k.to(dev), mx.SQ32)[mx.SQ32]
     dos = mx.quantize(do.to(dev), mx.SQ32)[mx.SQ32]
     vr = mx.quantize(v.to(dev), mx.ROW32)[mx.ROW32]
-    out = mx.attn_bwd(qs, ks, vr, dos, o.to(dev), do.to(dev), lse.to(dev), sigma, causal, s, grad_dtype)
+    return qs, ks, vr, dos
+
+
+def _gpu_bwd(q, k, v, do, o, lse, sigma, causal, s, grad_dtype, with_overflow=False):
+    dev = "cuda"
+    qs, ks, vr, dos = _quantize_bwd(q, k, v, do, dev)
+    out = mx.attn_bwd(qs, ks, vr, dos, o.to(dev), do.to(dev), lse.to(dev), sigma, causal, s, grad_dtype,
+                      with_overflow=with_overflow)
     torch.cuda.synchronize()
-    return [t.double().cpu().numpy() for t in out]
+    grads = [t.double().cpu().numpy() for t in out[:3]]
+    return (grads, out[3]) if with_overflow else grads
 
 
-def _check(gpu, ref, what):
-    for name, a, b in zip(("dQ", "dK", "dV"), gpu, ref):
-        e = rel_fro(a, b)
-        log(f"  {what} {name}: rel Frobenius {e:.2e}")
-        assert np.all(np.isfinite(a)), f"{what} {name}: non-finite values"
-        assert e <= TOL, f"{what} {name}: rel Frobenius {e:.3e} > {TOL}"
-
-
-def _oracle_bwd_fixed(q, k, v, o, do, lse, sigma, causal, heads=None):
+def _check_heads(gpu, q, k, v, o, do, lse, sigma, causal, heads, what):
+    """Every listed (b, h) against the oracle's exact gradients and admissible intervals."""
     qn, kn, vn, on, don = (t.double().numpy() for t in (q, k, v, o, do))
     ln = lse.double().numpy()
-    B, S, H, D = qn.shape
-    heads = heads or [(b, h) for b in range(B) for h in range(H)]
-    out = {}
+    worst = {n: 0.0 for n in ("dQ", "dK", "dV")}
     for b, h in heads:
-        r = at.backward_head(qn[b, :, h], kn[b, :, h], vn[b, :, h], on[b, :, h], don[b, :, h], ln[b, h], sigma, causal)
-        out[(b, h)] = (r["dQ"], r["dK"], r["dV"])
-    return out
-
-
-def _compare_heads(gpu, ref, what):
-    for i, name in enumerate(("dQ", "dK", "dV")):
-        a = np.concatenate([gpu[i][b, :, h].ravel() for (b, h) in ref])
-        r = np.concatenate([ref[(b, h)][i].ravel() for (b, h) in ref])
-        e = rel_fro(a, r)
-        worst = max(ref, key=lambda bh: rel_fro(gpu[i][bh[0], :, bh[1]], ref[bh][i]))
-        log(f"  {what} {name}: rel Frobenius {e:.2e} (worst head {worst}: "
-            f"{rel_fro(gpu[i][worst[0], :, worst[1]], ref[worst][i]):.2e})")
-        assert np.all(np.isfinite(a)), f"{what} {name}: non-finite values"
-        assert e <= TOL, f"{what} {name}: rel Frobenius {e:.3e} > {TOL}"
+        args = (qn[b, :, h], kn[b, :, h], vn[b, :, h], on[b, :, h], don[b, :, h], ln[b, h], sigma, causal)
+        ex = at.backward_head(*args)
+        bd = at.backward_bounds(*args)
+        for i, n in enumerate(("dQ", "dK", "dV")):
+            worst[n] = max(worst[n], check_grad_bounds(gpu[i][b, :, h], *bd[n], ex[n], f"{what} b{b} h{h} {n}"))
+    log(f"  {what}: worst plain rel Frobenius per head {worst}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -87,10 +73,10 @@ def test_backward_ragged_shapes(B, S, H, D, causal):
     sigma = 1 / math.sqrt(D)
     log(f"bwd ragged {(B, S, H, D)} causal={causal}")
     o, lse = _fwd_inputs(q, k, v, sigma, causal)
-    ref = _oracle_bwd_fixed(q, k, v, o, do, lse, sigma, causal)
+    heads = [(b, h) for b in range(B) for h in range(H)]
     for gd in (torch.float32, torch.bfloat16):
         gpu = _gpu_bwd(q, k, v, do, o, lse, sigma, causal, 8, gd)
-        _compare_heads(gpu, ref, f"ragged {(B, S, H, D)} {gd}")
+        _check_heads(gpu, q, k, v, o, do, lse, sigma, causal, heads, f"ragged {(B, S, H, D)} {gd}")
 
 
 def dq_scale_rule(max_abs_dq):
@@ -99,29 +85,85 @@ def dq_scale_rule(max_abs_dq):
     return int(min(8, math.floor(14 - math.log2(max_abs_dq))))
 
 
+@pytest.mark.timeout(600)
 def test_backward_small_causal_outliers():
-    """The small workload's 0.1% x50 outliers make |dQ| reach ~7e2: at the
-    2^8 static scale the fp16 accumulator overflows (7e2 * 256 > 65504), so
-    the scale comes from the headroom rule (here 2^4)."""
+    """The small workload (B2 H8 S1024 D128, causal, 0.1% of entries x50), all 16 heads.
+
+    The outliers make some logits reach hundreds, and the backward's square-block S' (a different
+    quantization of Q and K than the forward's) then differs from the forward's S by enough that
+    p = 2^(S' c - LSE log2 e) reaches 2^45 on some heads (fp32 infinity on one): there dQ is far
+    beyond what fp16 holds under any static scale 2^s, s in [-15, 15].
+      * At the workload's static scale 2^8 the call must raise the fp16 range flag rather than
+        return saturated dQ as valid.
+      * dQ is checked on the heads whose exact max|dQ| is at most 2^14, at the scale the headroom
+        rule gives for them (the other heads' dQ is out of fp16 range: the flag is raised again).
+      * dK and dV (fp32 accumulation) are checked on every head whose oracle p is finite."""
     w = synth.workload("small")
     sigma = 1 / math.sqrt(w.D)
-    log("bwd small (8 of 16 heads compared)")
+    log("bwd small (all 16 heads)")
     q, k, v, do = (synth.tensor_np(w, t) for t in ("q", "k", "v", "do"))
     o, lse = _fwd_inputs(q, k, v, sigma, True)
-    heads = [(b, h) for b in range(2) for h in (0, 3, 5, 6)]
-    ref = _oracle_bwd_fixed(q, k, v, o, do, lse, sigma, True, heads)
-    mq = max(np.max(np.abs(ref[x][0])) for x in ref)
-    s = dq_scale_rule(mq)
-    log(f"  max|dQ| = {mq:.3e}: max|dQ| * 2^8 = {mq * 256:.3e} (fp16 max 65504); static scale 2^{s}")
-    assert mq * 256 > 65504 and s < 8
-    gpu = _gpu_bwd(q, k, v, do, o, lse, sigma, True, s, torch.bfloat16)
-    _compare_heads(gpu, ref, "small bf16")
+    qn, kn, vn, on, don = (t.double().numpy() for t in (q, k, v, o, do))
+    ln = lse.double().numpy()
+    ex, finite, in_range = {}, [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            args = (qn[b, :, h], kn[b, :, h], vn[b, :, h], on[b, :, h], don[b, :, h], ln[b, h], sigma, True)
+            r = at.backward_head(*args)
+            mq, mp = float(np.max(np.abs(r["dQ"]))), float(np.max(r["p"]))
+            log(f"  head {(b, h)}: max p {mp:.3e}, max|dQ| {mq:.3e}")
+            if np.all(np.isfinite(r["p"])):
+                finite.append((b, h))
+                ex[(b, h)] = (args, r)
+                if mq <= 2.0 ** 14:
+                    in_range.append((b, h))
+    _, ovf8 = _gpu_bwd(q, k, v, do, o, lse, sigma, True, 8, torch.float32, with_overflow=True)
+    mq_in = max(float(np.max(np.abs(ex[bh][1]["dQ"]))) for bh in in_range)
+    s = dq_scale_rule(mq_in)
+    log(f"  flag at 2^8: {ovf8}; heads with finite p: {len(finite)}; dQ in fp16 range: {in_range}, "
+        f"static scale 2^{s}")
+    assert ovf8, "the fp16 dQ range was left at 2^8 without the flag"
+    assert len(in_range) >= 6 and len(finite) >= 14
+    gpu, ovf = _gpu_bwd(q, k, v, do, o, lse, sigma, True, s, torch.float32, with_overflow=True)
+    assert ovf == (len(in_range) < w.B * w.H)
+    worst = {n: 0.0 for n in ("dQ", "dK", "dV")}
+    for b, h in finite:
+        args, r = ex[(b, h)]
+        bd = at.backward_bounds(*args)
+        for i, n in enumerate(("dQ", "dK", "dV")):
+            if n == "dQ" and (b, h) not in in_range:
+                continue
+            worst[n] = max(worst[n], check_grad_bounds(gpu[i][b, :, h], *bd[n], r[n], f"small b{b} h{h} {n}"))
+    log(f"  small: worst plain rel Frobenius per head {worst}")
+
+
+def test_backward_grid_workload_meets_the_plain_bar():
+    """Values +-(1 + m/8) make S' and dP exact on the matrix unit, so P and dS codes are unique:
+    dQ, dK, dV of every head must be within 5e-3 relative Frobenius error of the exact oracle, with
+    no widening, and the range flag stays down at the static scale 2^8."""
+    w = synth.workload("grid")
+    sigma = 1 / math.sqrt(w.D)
+    log(f"bwd grid {w.shape()}")
+    q, k, v, do = (synth.tensor_np(w, t) for t in ("q", "k", "v", "do"))
+    o, lse = _fwd_inputs(q, k, v, sigma, True)
+    for gd in (torch.float32, torch.bfloat16):
+        gpu, ovf = _gpu_bwd(q, k, v, do, o, lse, sigma, True, 8, gd, with_overflow=True)
+        assert not ovf
+        qn, kn, vn, on, don = (t.double().numpy() for t in (q, k, v, o, do))
+        for b in range(w.B):
+            for h in range(w.H):
+                ex = at.backward_head(qn[b, :, h], kn[b, :, h], vn[b, :, h], on[b, :, h], don[b, :, h],
+                                      lse.double().numpy()[b, h], sigma, True)
+                for i, n in enumerate(("dQ", "dK", "dV")):
+                    e = rel_fro(gpu[i][b, :, h], ex[n])
+                    log(f"  grid {gd} b{b} h{h} {n}: rel Frobenius {e:.2e}")
+                    assert np.all(np.isfinite(gpu[i][b, :, h])) and e <= TOL, (gd, b, h, n, e)
 
 
 @pytest.mark.parametrize("seqlens", [[5, 130, 300, 77, 1, 64], [0, 33, 0, 200, 1, 0]])
 def test_backward_varlen(seqlens):
     """Jagged layout; the second batch holds empty sequences (first, middle and last) and a
-    one-token one."""
+    one-token one.  Every (sequence, head) against the oracle."""
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
     H, D = 2, 128
     sigma = 1 / math.sqrt(D)
@@ -139,9 +181,18 @@ def test_backward_varlen(seqlens):
                              lse.to(dev), cu_d, csr, seqlens, sigma, True, 8, torch.float32)
     torch.cuda.synchronize()
     gpu = [t.double().cpu().numpy() for t in gpu]
-    ref = at.mx_attention_backward(*(t.double().numpy() for t in (q, k, v, o, do)), lse.double().numpy(), sigma,
-                                   True, cu_seqlens=cu)
-    _check(gpu, ref, "varlen")
+    qn, kn, vn, on, don = (t.double().numpy() for t in (q, k, v, o, do))
+    ln = lse.double().numpy()
+    for s in range(len(seqlens)):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        for h in range(H):
+            args = (qn[a:b, h], kn[a:b, h], vn[a:b, h], on[a:b, h], don[a:b, h], ln[h, a:b], sigma, True)
+            ex = at.backward_head(*args)
+            bd = at.backward_bounds(*args)
+            for i, n in enumerate(("dQ", "dK", "dV")):
+                check_grad_bounds(gpu[i][a:b, h], *bd[n], ex[n], f"varlen seq{s} h{h} {n}")
 
 
 def test_backward_is_finite_and_repeatable():
@@ -160,92 +211,139 @@ def test_backward_is_finite_and_repeatable():
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
 
 
+def _rows(blocks, L):
+    return np.concatenate([np.arange(32 * i, min(L, 32 * i + 32)) for i in blocks])
+
+
+def _check_blocks(gq, gk, gv, args, qb, kb, what):
+    """Sampled query blocks of dQ and key blocks of dK, dV against the oracle's block-subset exact
+    gradients and admissible intervals."""
+    L = args[0].shape[0]
+    ex = at.backward_head_blocks(*args, q_blocks=qb, k_blocks=kb)
+    bd = at.backward_bounds(*args, q_blocks=qb, k_blocks=kb)
+    for name, g_, bl in (("dQ", gq, qb), ("dK", gk, kb), ("dV", gv, kb)):
+        check_grad_bounds(g_[_rows(bl, L)], *bd[name], np.concatenate([ex[name][i] for i in bl]),
+                          f"{what} {name} blocks {bl}")
+
+
+@pytest.mark.timeout(600)
 def test_backward_llm_shape_sampled_blocks():
-    """The metric shape (B8 H32 S8192 D128, causal) in the call bench.py times.  One sampled
-    (batch, head) carries O and LSE from the oracle forward; every other head holds an inert
-    filler (O = 0, LSE = 30, so its p is ~0), since only the sampled head is compared.  dQ of
-    sampled query blocks and dK, dV of sampled key blocks (first, last and random ones) are
-    checked against the oracle's block-subset backward, within the same 5e-3 bar."""
+    """The metric shape (B8 H32 S8192 D128, causal) in the call bench.py times.  Two sampled
+    (batch, head) pairs carry O and LSE from the oracle forward; every other head holds an inert
+    filler (O = 0, LSE = 30, so its p is ~0), since only the sampled heads are compared.  dQ of
+    sampled query blocks and dK, dV of sampled key blocks (first, last and random ones)."""
     w = synth.workload("llm")
     B, S, H, D = w.B, w.S, w.H, w.D
     sigma = 1 / math.sqrt(D)
-    (b, h), = synth.draw_sample_pairs(w.seed, B, H, 1)
-    log(f"bwd llm {w.shape()} head {(b, h)}")
-    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
-    qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
-    f = at.forward_head(qn, kn, vn, sigma, True, gemm="exact")
-    o_h = torch.from_numpy(f["O"].astype(np.float32)).to(torch.bfloat16)
-    lse_h = torch.from_numpy(f["LSE"].astype(np.float32))
+    pairs = synth.draw_sample_pairs(w.seed, B, H, 2)
+    log(f"bwd llm {w.shape()} heads {pairs}")
     o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, H, S), 30.0, device="cuda")
-    o[b, :, h, :] = o_h.cuda()
-    lse[b, h, :] = lse_h.cuda()
-    qs = mx.quantize(x["q"], mx.SQ32)[mx.SQ32]
-    ks = mx.quantize(x["k"], mx.SQ32)[mx.SQ32]
-    dos = mx.quantize(x["do"], mx.SQ32)[mx.SQ32]
-    vr = mx.quantize(x["v"], mx.ROW32)[mx.ROW32]
+    heads = {}
+    for b, h in pairs:
+        qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+        on, ln = oracle_forward_head(qn, kn, vn, sigma, True)
+        o[b, :, h, :] = torch.from_numpy(on.astype(np.float32)).to(torch.bfloat16).cuda()
+        lse[b, h, :] = torch.from_numpy(ln.astype(np.float32)).cuda()
+        heads[(b, h)] = (qn, kn, vn, on, dn, ln)
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    qs, ks, vr, dos = _quantize_bwd(x["q"], x["k"], x["v"], x["do"])
     dq, dk, dv = mx.attn_bwd(qs, ks, vr, dos, o, x["do"], lse, sigma, True, 8, torch.float32)
     torch.cuda.synchronize()
-    gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
-    del dq, dk, dv, qs, ks, dos, vr, x, o, lse
+    del qs, ks, vr, dos, x
     rng = np.random.default_rng(4)
     nb = S // 32
-    qb = sorted({0, 1, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
-    kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
-    ref = at.backward_head_blocks(qn, kn, vn, o_h.double().numpy(), dn, lse_h.double().numpy(), sigma, True,
-                                  q_blocks=qb, k_blocks=kb)
-    rows = lambda bl: np.concatenate([np.arange(32 * i, 32 * i + 32) for i in bl])  # noqa: E731
-    for name, g_, bl, key in (("dQ", gq, qb, "dQ"), ("dK", gk, kb, "dK"), ("dV", gv, kb, "dV")):
-        e = rel_fro(g_[rows(bl)], np.concatenate([ref[key][i] for i in bl]))
-        log(f"  llm {name} blocks {bl}: rel Frobenius {e:.2e}")
-        assert e <= TOL, f"llm {name}: rel Frobenius {e:.3e} > {TOL}"
+    for (b, h), (qn, kn, vn, on, dn, ln) in heads.items():
+        gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
+        qb = sorted({0, 1, nb - 1, *rng.choice(nb, 3, replace=False).tolist()})
+        kb = sorted({0, nb - 1, *rng.choice(nb, 3, replace=False).tolist()})
+        _check_blocks(gq, gk, gv, (qn, kn, vn, on, dn, ln, sigma, True), qb, kb, f"llm b{b} h{h}")
 
 
+@pytest.mark.timeout(600)
 def test_backward_long_context_sampled_blocks():
     """The long-context backward (B4 H16 S4096 D128, causal; every (tensor, head) scaled by
     10^U(-1, 1), which stresses the E8M0 range).  Two sampled heads carry O and LSE from the oracle
     forward, the other heads an inert filler (O = 0, LSE = 1e4: with logits up to a few hundred here,
-    their p underflows to 0 instead of overflowing).  The static dQ scale follows the
-    headroom rule from the float64 textbook dQ of the sampled heads.  dQ of sampled query blocks
-    and dK, dV of sampled key blocks are checked against the oracle's block-subset backward."""
+    their p underflows to 0 instead of overflowing).  The static dQ scale follows the headroom rule
+    from the float64 textbook dQ of the sampled heads."""
     w = synth.workload("long")
     B, S, H, D = w.B, w.S, w.H, w.D
     sigma = 1 / math.sqrt(D)
     pairs = synth.draw_sample_pairs(w.seed, B, H, 2)
     log(f"bwd long {w.shape()} heads {pairs}")
-    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
     o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, H, S), 1e4, device="cuda")
     heads, mq = {}, 0.0
     for b, h in pairs:
         qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
-        f = at.forward_head(qn, kn, vn, sigma, True, gemm="exact")
-        o_h = torch.from_numpy(f["O"].astype(np.float32)).to(torch.bfloat16)
-        lse_h = torch.from_numpy(f["LSE"].astype(np.float32))
-        o[b, :, h, :] = o_h.cuda()
-        lse[b, h, :] = lse_h.cuda()
-        on, ln = o_h.double().numpy(), lse_h.double().numpy()
+        on, ln = oracle_forward_head(qn, kn, vn, sigma, True)
+        o[b, :, h, :] = torch.from_numpy(on.astype(np.float32)).to(torch.bfloat16).cuda()
+        lse[b, h, :] = torch.from_numpy(ln.astype(np.float32)).cuda()
         ideal = at.backward_head(qn, kn, vn, on, dn, ln, sigma, True, quantize=False, exact=True)
         mq = max(mq, float(np.max(np.abs(ideal["dQ"]))))
-        heads[(b, h)] = (qn, kn, vn, dn, on, ln)
+        heads[(b, h)] = (qn, kn, vn, on, dn, ln)
     s = dq_scale_rule(mq)
     log(f"  max|dQ| = {mq:.3e}; static scale 2^{s}")
-    qs = mx.quantize(x["q"], mx.SQ32)[mx.SQ32]
-    ks = mx.quantize(x["k"], mx.SQ32)[mx.SQ32]
-    dos = mx.quantize(x["do"], mx.SQ32)[mx.SQ32]
-    vr = mx.quantize(x["v"], mx.ROW32)[mx.ROW32]
-    dq, dk, dv = mx.attn_bwd(qs, ks, vr, dos, o, x["do"], lse, sigma, True, s, torch.float32)
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    qs, ks, vr, dos = _quantize_bwd(x["q"], x["k"], x["v"], x["do"])
+    dq, dk, dv, ovf = mx.attn_bwd(qs, ks, vr, dos, o, x["do"], lse, sigma, True, s, torch.float32, with_overflow=True)
     torch.cuda.synchronize()
+    assert not ovf
     rng = np.random.default_rng(6)
     nb = S // 32
-    rows = lambda bl: np.concatenate([np.arange(32 * i, 32 * i + 32) for i in bl])  # noqa: E731
-    for (b, h), (qn, kn, vn, dn, on, ln) in heads.items():
+    for (b, h), (qn, kn, vn, on, dn, ln) in heads.items():
         gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
         qb = sorted({0, 1, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
         kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
-        ref = at.backward_head_blocks(qn, kn, vn, on, dn, ln, sigma, True, q_blocks=qb, k_blocks=kb)
-        for name, g_, bl in (("dQ", gq, qb), ("dK", gk, kb), ("dV", gv, kb)):
-            e = rel_fro(g_[rows(bl)], np.concatenate([ref[name][i] for i in bl]))
-            log(f"  long b{b} h{h} {name} blocks {bl}: rel Frobenius {e:.2e}")
-            assert np.all(np.isfinite(g_[rows(bl)])), f"long {name}: non-finite values"
-            assert e <= TOL, f"long b{b} h{h} {name}: rel Frobenius {e:.3e} > {TOL}"
+        _check_blocks(gq, gk, gv, (qn, kn, vn, on, dn, ln, sigma, True), qb, kb, f"long b{b} h{h}")
+
+
+@pytest.mark.timeout(900)
+def test_backward_varlen_workload_every_sequence():
+    """The jagged workload as configured: 16 packed sequences, lengths U{256..8192} (seeded), H16
+    D128, causal, scale rows at the 128-aligned offsets.  Every sequence carries O and LSE from the
+    oracle forward on one seeded head (the other heads an inert filler: O = 0, LSE = 30), and on
+    that head dQ of sampled query blocks and dK, dV of sampled key blocks (first, last, random) are
+    checked against the oracle."""
+    w = synth.workload("varlen")
+    sigma = 1 / math.sqrt(w.D)
+    cu = w.cu_seqlens()
+    T, H, D = int(cu[-1]), w.H, w.D
+    rng = np.random.default_rng(11)
+    head_of = [int(rng.integers(H)) for _ in w.seqlens]
+    log(f"bwd varlen workload T={T} heads {head_of}")
+    o = torch.zeros(T, H, D, dtype=torch.bfloat16)
+    lse = torch.full((H, T), 30.0)
+    per_seq = []
+    for s, h in enumerate(head_of):
+        a, b = int(cu[s]), int(cu[s + 1])
+        qn, kn, vn, dn = (synth.token_slice_np(w, t, a, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+        on, ln = oracle_forward_head(qn, kn, vn, sigma, True)
+        o[a:b, h] = torch.from_numpy(on.astype(np.float32)).to(torch.bfloat16)
+        lse[h, a:b] = torch.from_numpy(ln.astype(np.float32))
+        per_seq.append((qn, kn, vn, on, dn, ln))
+        log(f"  oracle forward seq{s} (L={b - a}) h{h} done")
+    dev = "cuda"
+    x = {t: synth.tensor_torch(w, t, dev) for t in ("q", "k", "v", "do")}
+    cu_d = torch.from_numpy(cu).to(dev)
+    qs, csr = mx.quantize_varlen(x["q"].to(dev), cu_d, w.seqlens, mx.SQ32)
+    ks, _ = mx.quantize_varlen(x["k"].to(dev), cu_d, w.seqlens, mx.SQ32)
+    dos, _ = mx.quantize_varlen(x["do"].to(dev), cu_d, w.seqlens, mx.SQ32)
+    vr, _ = mx.quantize_varlen(x["v"].to(dev), cu_d, w.seqlens, mx.ROW32)
+    dq, dk, dv, ovf = mx.attn_bwd_varlen(qs[mx.SQ32], ks[mx.SQ32], vr[mx.ROW32], dos[mx.SQ32], o.to(dev),
+                                         x["do"], lse.to(dev), cu_d, csr, w.seqlens, sigma, True, 8,
+                                         torch.float32, with_overflow=True)
+    torch.cuda.synchronize()
+    assert not ovf
+    del qs, ks, dos, vr, x
+    gq, gk, gv = (t.double().cpu().numpy() for t in (dq, dk, dv))
+    for s, h in enumerate(head_of):
+        a, b = cu[s], cu[s + 1]
+        L = b - a
+        nb = (L + 31) // 32
+        qb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        qn, kn, vn, on, dn, ln = per_seq[s]
+        _check_blocks(gq[a:b, h], gk[a:b, h], gv[a:b, h], (qn, kn, vn, on, dn, ln, sigma, True), qb, kb,
+                      f"varlen seq{s} (L={L}) h{h}")

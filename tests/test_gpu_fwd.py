@@ -1,7 +1,12 @@
 """GPU parity: the fused MXFP8 attention forward against the oracle.
 
-O (fp32 output) within 1e-3 * max|O|; bf16 O within that plus half a bf16
-ulp of the oracle value; LSE within 1e-4 + 1e-6 |LSE|."""
+The oracle computes the plain definition (every product the exact sum, rounded once to fp32).
+The matrix unit's products may differ from it by up to the stated bound (oracle/gemm.py), which
+can move P codes, so O is several-valued: O (fp32 output) must lie within 1e-3 * max|O| of the
+oracle's admissible interval, bf16 O within that plus half a bf16 ulp, LSE within 1e-4 +
+1e-6 |LSE| of its interval.  Where the interval is one value this is the plain check; each test
+logs how many rows needed the widening.  The grid workload makes every S product exact on the
+matrix unit, so there O meets the plain bar against the exact oracle with no widening."""
 import math
 
 import numpy as np
@@ -12,7 +17,7 @@ import mxfp8_block_scaled_flash_amd as mx
 import synth
 from oracle import attention as at
 
-from mxtest import check_lse, check_out, log
+from mxtest import check_lse, check_lse_bounds, check_out, check_out_bounds, log
 
 pytestmark = pytest.mark.gpu
 ALL = mx.ROW32 | mx.COL32 | mx.SQ32
@@ -33,9 +38,10 @@ def _compare_full(q, k, v, sigma, causal, what):
     o16, _ = _gpu_fwd(q.cuda(), k.cuda(), v.cuda(), sigma, causal, torch.bfloat16)
     qn, kn, vn = (t.double().numpy() for t in (q, k, v))
     O, LSE = at.mx_attention_forward(qn, kn, vn, sigma, causal)
-    check_out(o32.double().cpu().numpy(), O, f"{what} fp32-out")
-    check_out(o16.double().cpu().numpy(), O, f"{what} bf16-out", bf16=True)
-    check_lse(lse.cpu().numpy(), LSE, what)
+    lo, hi, llo, lhi = at.mx_attention_forward_bounds(qn, kn, vn, sigma, causal)
+    check_out_bounds(o32.double().cpu().numpy(), lo, hi, O, f"{what} fp32-out")
+    check_out_bounds(o16.double().cpu().numpy(), lo, hi, O, f"{what} bf16-out", bf16=True)
+    check_lse_bounds(lse.cpu().numpy(), llo, lhi, what)
 
 
 def test_forward_tiny_noncausal_fp32():
@@ -74,9 +80,12 @@ def test_forward_one_hot_rows_follow_the_integer_frame():
 
 
 def test_forward_llm_shape_sampled():
+    """The metric shape (B8 H32 S8192 D128, causal, bf16 O) in the launch bench.py times; the
+    seeded sample of 4 (batch, head) pairs, each on its first 40 rows, 300 random rows and the last
+    row, against the oracle's admissible interval."""
     w = synth.workload("llm")
     sigma = 1 / math.sqrt(w.D)
-    pairs = synth.draw_sample_pairs(w.seed, w.B, w.H, 2)
+    pairs = synth.draw_sample_pairs(w.seed, w.B, w.H, 4)
     log(f"fwd llm {w.shape()} pairs {pairs}")
     q, k, v = (synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v"))
     o, lse = _gpu_fwd(q, k, v, sigma, True, torch.bfloat16)
@@ -86,8 +95,10 @@ def test_forward_llm_shape_sampled():
         rows = np.sort(np.concatenate([np.arange(0, 40), rng.choice(w.S, 300, replace=False), [w.S - 1]]))
         rows = np.unique(rows)
         r = at.forward_head(qs, ks, vs, sigma, True, q_rows=rows)
-        check_out(o[b, rows, h, :].double().cpu().numpy(), r["O"], f"llm b{b} h{h}", bf16=True)
-        check_lse(lse[b, h, rows].cpu().numpy(), r["LSE"], f"llm b{b} h{h}")
+        bd = at.forward_head_bounds(qs, ks, vs, sigma, True, q_rows=rows)
+        check_out_bounds(o[b, rows, h, :].double().cpu().numpy(), bd["O_lo"], bd["O_hi"], r["O"], f"llm b{b} h{h}",
+                         bf16=True)
+        check_lse_bounds(lse[b, h, rows].cpu().numpy(), bd["LSE_lo"], bd["LSE_hi"], f"llm b{b} h{h}")
 
 
 def test_forward_varlen_sampled():
@@ -109,9 +120,11 @@ def test_forward_varlen_sampled():
         h = int(rng.integers(w.H))
         a, b = cu[s], cu[s + 1]
         rows = np.unique(np.concatenate([np.arange(min(40, b - a)), rng.choice(b - a, 64, replace=False)]))
-        r = at.forward_head(xn["q"][a:b, h], xn["k"][a:b, h], xn["v"][a:b, h], sigma, True, q_rows=rows)
-        check_out(o[a:b, h][rows].double().cpu().numpy(), r["O"], f"varlen seq{s} h{h}")
-        check_lse(lse[h, a:b][rows].cpu().numpy(), r["LSE"], f"varlen seq{s} h{h}")
+        args = (xn["q"][a:b, h], xn["k"][a:b, h], xn["v"][a:b, h], sigma, True)
+        r = at.forward_head(*args, q_rows=rows)
+        bd = at.forward_head_bounds(*args, q_rows=rows)
+        check_out_bounds(o[a:b, h][rows].double().cpu().numpy(), bd["O_lo"], bd["O_hi"], r["O"], f"varlen seq{s} h{h}")
+        check_lse_bounds(lse[h, a:b][rows].cpu().numpy(), bd["LSE_lo"], bd["LSE_hi"], f"varlen seq{s} h{h}")
 
 
 def test_forward_is_deterministic():
@@ -139,6 +152,26 @@ def test_forward_varlen_short_and_empty_sequences(seqlens):
     o, lse = mx.attn_fwd_varlen(qq[mx.ROW32], kq[mx.ROW32], vq[mx.COL32], cu_d, csr, seqlens, sigma, True,
                                 torch.float32)
     torch.cuda.synchronize()
-    O, LSE = at.mx_attention_forward(*(t.double().numpy() for t in (q, k, v)), sigma, True, cu_seqlens=cu)
-    check_out(o.double().cpu().numpy(), O, f"varlen {seqlens}")
-    check_lse(lse.cpu().numpy(), LSE, f"varlen {seqlens}")
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    O, LSE = at.mx_attention_forward(qn, kn, vn, sigma, True, cu_seqlens=cu)
+    lo, hi, llo, lhi = at.mx_attention_forward_bounds(qn, kn, vn, sigma, True, cu_seqlens=cu)
+    check_out_bounds(o.double().cpu().numpy(), lo, hi, O, f"varlen {seqlens}")
+    check_lse_bounds(lse.cpu().numpy(), llo, lhi, f"varlen {seqlens}")
+
+
+def test_forward_grid_workload_meets_the_plain_bar():
+    """Values +-(1 + m/8): every block scale is equal and every product of two elements lies in two
+    adjacent binades, so S = Q^K^T is exact on the matrix unit and P's codes are unique.  O must
+    then match the exact oracle within 1e-3 max|O| (bf16 O: plus half a bf16 ulp) and LSE within
+    1e-4 + 1e-6 |LSE|, with no widening.  B2 H4 S1000 D128 causal: several query and key tiles and
+    a ragged tail (1000 = 7 x 128 + 104)."""
+    w = synth.workload("grid")
+    sigma = 1 / math.sqrt(w.D)
+    log(f"fwd grid {w.shape()}")
+    q, k, v = (synth.tensor_np(w, t) for t in ("q", "k", "v"))
+    o32, lse = _gpu_fwd(q.cuda(), k.cuda(), v.cuda(), sigma, True, torch.float32)
+    o16, _ = _gpu_fwd(q.cuda(), k.cuda(), v.cuda(), sigma, True, torch.bfloat16)
+    O, LSE = at.mx_attention_forward(*(t.double().numpy() for t in (q, k, v)), sigma, True)
+    check_out(o32.double().cpu().numpy(), O, "grid fp32-out")
+    check_out(o16.double().cpu().numpy(), O, "grid bf16-out", bf16=True)
+    check_lse(lse.cpu().numpy(), LSE, "grid")

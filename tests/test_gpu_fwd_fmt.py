@@ -1,8 +1,9 @@
 """GPU parity: the fused attention forward with Q and K in MXFP6 (E2M3, E3M2) or MXFP4 (E2M1)
 (mx_attn_fwd_fmt; P and V stay MXFP8) against the oracle's forward with the same Q/K element
 format.  Q and K are quantized by mx_quantize_rows (bit-exact with the oracle's codec, tested in
-test_gpu_mxsmall.py).  Bounds as for the MXFP8 forward: O within 1e-3 * max|O| (bf16 O plus half a
-bf16 ulp), LSE within 1e-4 + 1e-6 |LSE|."""
+test_gpu_mxsmall.py).  As for the MXFP8 forward, the oracle computes the plain definition and O
+must lie within 1e-3 * max|O| of its admissible interval (bf16 O plus half a bf16 ulp), LSE
+within 1e-4 + 1e-6 |LSE| of its interval."""
 import math
 
 import numpy as np
@@ -13,7 +14,7 @@ import mxfp8_block_scaled_flash_amd as mx
 import synth
 from oracle import attention as at
 
-from mxtest import check_lse, check_out, log
+from mxtest import check_lse_bounds, check_out_bounds, log
 
 pytestmark = pytest.mark.gpu
 FMTS = {mx.E2M3: "e2m3", mx.E3M2: "e3m2", mx.E2M1: "e2m1"}
@@ -34,9 +35,10 @@ def _compare_full(q, k, v, sigma, causal, fmt, what):
     o16, _ = _gpu_fwd(q.cuda(), k.cuda(), v.cuda(), sigma, causal, fmt, torch.bfloat16)
     qn, kn, vn = (t.double().numpy() for t in (q, k, v))
     O, LSE = at.mx_attention_forward(qn, kn, vn, sigma, causal, qk_fmt=FMTS[fmt])
-    check_out(o32.double().cpu().numpy(), O, f"{what} fp32-out")
-    check_out(o16.double().cpu().numpy(), O, f"{what} bf16-out", bf16=True)
-    check_lse(lse.cpu().numpy(), LSE, what)
+    lo, hi, llo, lhi = at.mx_attention_forward_bounds(qn, kn, vn, sigma, causal, qk_fmt=FMTS[fmt])
+    check_out_bounds(o32.double().cpu().numpy(), lo, hi, O, f"{what} fp32-out")
+    check_out_bounds(o16.double().cpu().numpy(), lo, hi, O, f"{what} bf16-out", bf16=True)
+    check_lse_bounds(lse.cpu().numpy(), llo, lhi, what)
 
 
 @pytest.mark.parametrize("fmt", list(FMTS))
@@ -69,8 +71,10 @@ def test_forward_e2m1_llm_shape_sampled():
         qs, ks, vs = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v"))
         rows = np.unique(np.concatenate([np.arange(0, 40), rng.choice(w.S, 200, replace=False), [w.S - 1]]))
         r = at.forward_head(qs, ks, vs, sigma, True, q_rows=rows, qk_fmt="e2m1")
-        check_out(o[b, rows, h, :].double().cpu().numpy(), r["O"], f"e2m1 llm b{b} h{h}", bf16=True)
-        check_lse(lse[b, h, rows].cpu().numpy(), r["LSE"], f"e2m1 llm b{b} h{h}")
+        bd = at.forward_head_bounds(qs, ks, vs, sigma, True, q_rows=rows, qk_fmt="e2m1")
+        check_out_bounds(o[b, rows, h, :].double().cpu().numpy(), bd["O_lo"], bd["O_hi"], r["O"], f"e2m1 llm b{b} h{h}",
+                         bf16=True)
+        check_lse_bounds(lse[b, h, rows].cpu().numpy(), bd["LSE_lo"], bd["LSE_hi"], f"e2m1 llm b{b} h{h}")
 
 
 def test_forward_fmt_with_e4m3_is_the_mxfp8_forward():
@@ -107,7 +111,9 @@ def test_forward_qk_format_varlen_sampled(fmt):
         h = int(rng.integers(w.H))
         a, b = cu[s], cu[s + 1]
         rows = np.unique(np.concatenate([np.arange(min(40, b - a)), rng.choice(b - a, 48, replace=False)]))
-        r = at.forward_head(xn["q"][a:b, h], xn["k"][a:b, h], xn["v"][a:b, h], sigma, True, q_rows=rows,
-                            qk_fmt=FMTS[fmt])
-        check_out(o[a:b, h][rows].double().cpu().numpy(), r["O"], f"{FMTS[fmt]} varlen seq{s} h{h}")
-        check_lse(lse[h, a:b][rows].cpu().numpy(), r["LSE"], f"{FMTS[fmt]} varlen seq{s} h{h}")
+        args = (xn["q"][a:b, h], xn["k"][a:b, h], xn["v"][a:b, h], sigma, True)
+        r = at.forward_head(*args, q_rows=rows, qk_fmt=FMTS[fmt])
+        bd = at.forward_head_bounds(*args, q_rows=rows, qk_fmt=FMTS[fmt])
+        check_out_bounds(o[a:b, h][rows].double().cpu().numpy(), bd["O_lo"], bd["O_hi"], r["O"],
+                         f"{FMTS[fmt]} varlen seq{s} h{h}")
+        check_lse_bounds(lse[h, a:b][rows].cpu().numpy(), bd["LSE_lo"], bd["LSE_hi"], f"{FMTS[fmt]} varlen seq{s} h{h}")

@@ -88,7 +88,7 @@ def test_causal_first_row_closed_form():
     L, D = 40, 128
     q, k, v = (_rand((L, D), s) for s in (14, 15, 16))
     sigma = 1 / math.sqrt(D)
-    r = at.forward_head(q, k, v, sigma, True, gemm="exact")
+    r = at.forward_head(q, k, v, sigma, True)
     qh = mx.dequantize_row32(*mx.quantize_row32(q))
     kh = mx.dequantize_row32(*mx.quantize_row32(k))
     s00 = float(np.float32(qh[0] @ kh[0]))
@@ -202,7 +202,7 @@ def test_forward_operand_layouts_are_pinned():
         x[..., ::32] = 320.0 * np.sign(rng.standard_normal(x[..., ::32].shape))  # a top-binade element per block
         return x * np.exp2(rng.integers(-12, 6, size=shape[:-1] + (1,)))
     q, k = row_exact((L, D)), row_exact((L, D))
-    r = at.forward_head(q, k, _rand((L, D), 31), 0.1, False, gemm="exact")
+    r = at.forward_head(q, k, _rand((L, D), 31), 0.1, False)
     assert np.array_equal(r["S"], at.fl32(q @ k.T))
     # V: each 32-key block of each column has its own power-of-two scale
     v = mx.e4m3_decode(rng.integers(0x30, 0x7F, size=(L, D)))
@@ -228,7 +228,7 @@ def test_backward_operand_layouts_are_pinned():
     v[:, ::32] = 320.0
     v = v * np.exp2(rng.integers(-8, 8, size=(L, 1)))
     O, lse = at.attention_fp64(q, k, v, 0.05, True)
-    g = at.backward_head(q, k, v, O, do, lse, 0.05, True, gemm="exact")
+    g = at.backward_head(q, k, v, O, do, lse, 0.05, True)
     assert np.array_equal(g["S"], at.fl32(q @ k.T))
     assert np.array_equal(g["dP"], at.fl32(do @ v.T))
     assert np.array_equal(g["D"], at.fl32(np.sum(do * O, axis=1)))
@@ -274,7 +274,7 @@ def test_backward_blocks_equal_the_full_backward(causal):
     rng = np.random.default_rng(21)
     L, D, sigma = 150, 64, 0.125
     q, k, v, do = (rng.standard_normal((L, D)).astype(np.float32).astype(np.float64) for _ in range(4))
-    f = at.forward_head(q, k, v, sigma, causal, gemm="exact")
+    f = at.forward_head(q, k, v, sigma, causal)
     o, lse = f["O"].astype(np.float32).astype(np.float64), f["LSE"].astype(np.float32).astype(np.float64)
     full = at.backward_head(q, k, v, o, do, lse, sigma, causal)
     blocks = [0, 2, 4]   # block 4 holds rows 128..149

@@ -14,7 +14,7 @@ def test_splitmix64_published_sequence():
 
 
 def test_numpy_and_torch_generators_agree():
-    for name in ("tiny", "small", "long"):
+    for name in ("tiny", "small", "long", "grid"):
         w = synth.workload(name)
         if w.numel() > 1 << 24:
             w = synth.Workload(w.name, w.seed, 1, 256, w.H, w.D, w.causal, w.dtype, w.outlier_rate,
@@ -40,3 +40,17 @@ def test_normal_moments_and_recipes():
     assert np.all((hs >= 0.1) & (hs <= 10))
     pairs = synth.draw_sample_pairs(2, 8, 32, 4)
     assert len(set(pairs)) == 4
+
+
+def test_grid_recipe_values():
+    """The grid workload draws +-(1 + m/8) with every sign and m equally likely."""
+    x = synth.grid_np(5, 0, np.arange(160000))
+    assert set(np.unique(np.abs(x))) == {1 + m / 8 for m in range(8)}
+    counts = np.unique(x, return_counts=True)[1]
+    assert len(counts) == 16 and counts.min() > 0.9 * 10000 and counts.max() < 1.1 * 10000
+
+
+def test_token_slice_matches_whole_tensor():
+    w = synth.workload("small")
+    full = synth.tensor_np(w, "v")
+    assert torch.equal(synth.token_slice_np(w, "v", 1024 + 100, 1024 + 333, 6), full[1, 100:333, 6, :])
