@@ -22,7 +22,8 @@ largest binade and truncated no further than 13 bits below it lose less than
 2**(E - 10) per group of 8, which is at most 2**-10 times the group's share of
 the sum above; the partial sums of 16 products are then added in fp32, each
 addition off by at most 2**-24 of a partial sum, which is below 4 times the sum
-above.  The attention parity checks
+above.  Products and sums below fp32's normal range may flush to zero, which adds
+(K + 1) 2**-126 to the bound.  The attention parity checks
 propagate this bound through the method's steps (oracle/attention.py,
 ``forward_head_bounds`` and ``backward_bounds``); whether the matrix
 instruction itself stays inside it is measured on the GPU by the tests.
@@ -59,4 +60,5 @@ def bound_rel(K: int) -> float:
 def product_error_bound(amag, bmag):
     """eps [M, N] for a [M, K] @ b[N, K]^T from the operands' element magnitudes."""
     amag, bmag = np.asarray(amag, np.float64), np.asarray(bmag, np.float64)
-    return bound_rel(amag.shape[-1]) * (amag @ bmag.T)
+    K = amag.shape[-1]
+    return bound_rel(K) * (amag @ bmag.T) + (K + 1) * 2.0 ** -126
