@@ -358,6 +358,7 @@ size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D);
  * token); the returned dQ is then not valid and the caller should repeat the
  * call with a smaller dq_scale_log2.
  *   workspace  the device workspace the backward was given (16-byte aligned)
+ *              (NULL: the calling device's scratch of mx_attn_bwd_noalloc)
  *   overflow   host int: set to 1 if the flag is raised, else 0
  *   stream     the stream the backward ran on: the call copies the flag on it
  *              and synchronizes that stream (it blocks the host).
@@ -452,6 +453,32 @@ mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              float softmax_scale, int causal, int dq_scale_log2,
                              void* dq, void* dk, void* dv, mx_dtype grad_dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_attn_bwd_noalloc -- mx_attn_bwd for callers that cannot allocate device
+ * memory or hand in a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, computation and
+ * errors as mx_attn_bwd, without the workspace: the range flag, fp16 dQ
+ * accumulator and D_i live in a static device array of the library, one per
+ * GPU, 128 MiB each (MX_NOALLOC_MAX_BYTES), held until the process ends.
+ * Calls whose mx_attn_bwd_workspace_bytes(B*S, H, D) exceeds it return
+ * MX_EWORKSPACE before anything is launched (D = 128: up to 516 000 token-head
+ * rows, e.g. B4 S4096 H16 or B2 S8192 H16 fit, B4 S8192 H16 does not).  The call allocates nothing and clears what must
+ * start at zero with kernels on the stream.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, threads)
+ * race and must be serialized by the caller.  The range flag is read with
+ * mx_attn_bwd_overflow(NULL, ...) on the same device.
+ */
+#define MX_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+mx_status mx_attn_bwd_noalloc(const uint8_t* q_data, const uint8_t* q_scale,
+                              const uint8_t* k_data, const uint8_t* k_scale,
+                              const uint8_t* v_data, const uint8_t* v_scale,
+                              const uint8_t* do_data, const uint8_t* do_scale,
+                              const void* o, const void* dout, mx_dtype io_dtype, const float* lse,
+                              int B, int S, int H, int D, float softmax_scale, int causal,
+                              int dq_scale_log2,
+                              void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

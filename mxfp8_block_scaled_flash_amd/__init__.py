@@ -57,6 +57,8 @@ _SIGS = {
                                 + [_c_int, _vp, _c_size, _vp], _c_int),
     "mx_attn_bwd": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
                     + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
+    "mx_attn_bwd_noalloc": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
+                            + [_vp] * 3 + [_c_int, _vp], _c_int),
     "mx_attn_bwd_varlen": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_vp, _vp] + [_c_int] * 5
                            + [_c_float, _c_int, _c_int] + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
 }
@@ -239,7 +241,8 @@ def mx_attn_bwd_workspace_bytes(tokens, H, D) -> int:
 
 
 def mx_attn_bwd_overflow(workspace, stream=None) -> bool:
-    """True if the last backward on this workspace left fp16's range (blocks on the stream)."""
+    """True if the last backward on this workspace (None: this device's no-allocation scratch) left
+    fp16's range (blocks on the stream)."""
     flag = ctypes.c_int(0)
     _check(lib().mx_attn_bwd_overflow(_ptr(workspace), ctypes.byref(flag), _stream(stream)), "mx_attn_bwd_overflow")
     return bool(flag.value)
@@ -252,6 +255,15 @@ def mx_attn_bwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_s
                              B, S, H, D, float(softmax_scale), int(bool(causal)), int(dq_scale_log2), _ptr(dq),
                              _ptr(dk), _ptr(dv), _dtype_code(dq.dtype), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream)), "mx_attn_bwd")
+
+
+def mx_attn_bwd_noalloc(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse, B, S, H,
+                        D, softmax_scale, causal, dq_scale_log2, dq, dk, dv, stream=None):
+    _check(lib().mx_attn_bwd_noalloc(_ptr(q_data), _ptr(q_scale), _ptr(k_data), _ptr(k_scale), _ptr(v_data),
+                                     _ptr(v_scale), _ptr(do_data), _ptr(do_scale), _ptr(o), _ptr(dout),
+                                     _dtype_code(o.dtype), _ptr(lse), B, S, H, D, float(softmax_scale),
+                                     int(bool(causal)), int(dq_scale_log2), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _dtype_code(dq.dtype), _stream(stream)), "mx_attn_bwd_noalloc")
 
 
 def mx_attn_bwd_varlen(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse,

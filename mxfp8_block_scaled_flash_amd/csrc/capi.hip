@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mxfa.h"
 #include "mx_launch.h"
@@ -387,8 +388,15 @@ size_t mx_attn_bwd_workspace_bytes(int tokens, int H, int D) {
   return kFlagBytes + up((size_t)tokens * H * D * 2) + up((size_t)tokens * H * 4);
 }
 
+static mx_status scratch_ptr(void** out);
+
 mx_status mx_attn_bwd_overflow(const void* workspace, int* overflow, hipStream_t stream) {
-  if (!workspace || !overflow || !aligned16(workspace)) return MX_EINVAL;
+  if (!overflow || (workspace && !aligned16(workspace))) return MX_EINVAL;
+  if (!workspace) {   // the calling device's scratch (mx_attn_bwd_noalloc)
+    void* p = nullptr;
+    if (mx_status st = scratch_ptr(&p)) return st;
+    workspace = p;
+  }
   uint32_t flag = 0;
   if (hipMemcpyAsync(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess) return MX_EHIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return MX_EHIP;
@@ -539,6 +547,56 @@ mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, cons
   a.nseq = nseq;
   a.T = total_tokens;
   return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, max_seqlen, stream));
+}
+
+// ---------------------------------------------------------------- no-allocation backward
+// The backward's scratch (range flag, fp16 dQ accumulator, D_i) for callers that cannot allocate:
+// one file-scope device array, so each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel or a copy.
+static constexpr size_t kScratchBytes = MX_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[64];   // device address of `scratch`, per device ordinal
+
+static mx_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MX_EHIP;
+  if (dev < 0 || dev >= 64) return MX_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MX_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MX_OK;
+}
+
+mx_status mx_attn_bwd_noalloc(const uint8_t* q_data, const uint8_t* q_scale, const uint8_t* k_data,
+                              const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                              const uint8_t* do_data, const uint8_t* do_scale, const void* o, const void* dout,
+                              mx_dtype io_dtype, const float* lse, int B, int S, int H, int D,
+                              float softmax_scale, int causal, int dq_scale_log2, void* dq, void* dk, void* dv,
+                              mx_dtype grad_dtype, hipStream_t stream) {
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  const size_t need = mx_attn_bwd_workspace_bytes(B * S, H, D);
+  // the arguments are checked (against an aligned stand-in workspace) before the device is touched
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_common(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                                io_dtype, lse, H, D, softmax_scale, dq_scale_log2, dq, dk, dv, grad_dtype,
+                                reinterpret_cast<void*>(static_cast<uintptr_t>(256)), need, B * S, a))
+    return st;
+  if (need > kScratchBytes) return MX_EWORKSPACE;
+  if (mx_status st = check_device()) return st;
+  void* ws = nullptr;
+  if (mx_status st = scratch_ptr(&ws)) return st;
+  return mx_attn_bwd(q_data, q_scale, k_data, k_scale, v_data, v_scale, do_data, do_scale, o, dout, io_dtype, lse,
+                     B, S, H, D, softmax_scale, causal, dq_scale_log2, dq, dk, dv, grad_dtype, ws, need, stream);
 }
 
 }  // extern "C"

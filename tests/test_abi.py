@@ -260,6 +260,28 @@ def test_mx_backward_varlen_rejects_invalid_arguments():
 def test_overflow_query_rejects_bad_pointers():
     L = mx.lib()
     flag = ctypes.c_int(0)
-    assert L.mx_attn_bwd_overflow(None, ctypes.byref(flag), None) == EINVAL
     assert L.mx_attn_bwd_overflow(16, None, None) == EINVAL
     assert L.mx_attn_bwd_overflow(24, ctypes.byref(flag), None) == EINVAL
+    assert L.mx_attn_bwd_overflow(None, None, None) == EINVAL
+
+
+def test_noalloc_backward_rejects_invalid_and_oversized_calls_before_the_device():
+    """mx_attn_bwd_noalloc validates like mx_attn_bwd (no workspace arguments) and rejects calls
+    whose scratch would exceed MX_NOALLOC_MAX_BYTES (128 MiB) with MX_EWORKSPACE, all on the host."""
+    L = mx.lib()
+    args = [16] * 8 + [16, 16, mx.BF16, 16, 1, 64, 1, 128, 0.1, 1, 8, 16, 16, 16, mx.BF16, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return L.mx_attn_bwd_noalloc(*a)
+    for bad in (dict(a15=96), dict(a14=0), dict(a12=-1), dict(a16=0.0), dict(a18=16), dict(a10=mx.F16),
+                dict(a0=None), dict(a11=None), dict(a3=24)):
+        assert call(**bad) == EINVAL, bad
+    assert call(a12=0) == 0
+    # the long-context workload (B4 S4096 H16 D128) and B2 S8192 H16 fit; B4 S8192 H16 does not
+    assert L.mx_attn_bwd_workspace_bytes(4 * 4096, 16, 128) <= 128 << 20
+    assert L.mx_attn_bwd_workspace_bytes(2 * 8192, 16, 128) <= 128 << 20
+    assert call(a12=4, a13=8192, a14=16) == EWORKSPACE
+    assert call(a12=8, a13=8192, a14=32) == EWORKSPACE
