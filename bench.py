@@ -70,28 +70,81 @@ def measured_traffic():
     return float(kv["bytes_per_call"])
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, sigma):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    the forward for 1024 query rows at the end of one (batch, head) (rows with
-    the most visible keys)."""
+    """The oracle, as it stands, on a bounded sample of the same workload, on the host's cores.
+
+    Sample: the workload's seeded 4 (batch, head) pairs; per pair the forward of the last 2048
+    query rows (the rows with the most visible keys, two chunks of 1024) and the backward of the
+    last 4 query blocks (dQ) and the first 4 key blocks (dK, dV).  The work items run on a pool of
+    threads (numpy releases the interpreter lock inside its array operations; BLAS is held to one
+    thread per item), one per core of this machine's CPU share (at most 16).  FLOPs are counted like
+    the GPU's over the visible pairs each item covers: 4 D per pair for the forward, 6 D for a
+    query block's backward (S, dP, dQ) and 8 D for a key block's (S, dP, dV, dK)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import synth
     from oracle import attention as at
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
     except Exception:
-        threads = 1
-    b, h = synth.draw_sample_pairs(w.seed, w.B, w.H, 1)[0]
-    q, k, v = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v"))
-    rows = np.arange(w.S - 1024, w.S)
-    t0 = time.perf_counter()
-    at.forward_head(q, k, v, sigma, True, q_rows=rows)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * float(np.sum(rows + 1))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"forward of 1024 query rows (S-1024..S-1) of (b={b}, h={h}) of the B8 H32 S8192 D128 causal "
-                      f"workload, {dt:.1f} s; numpy, elementwise work on 1 thread, BLAS on {threads}"}
+        threadpool_limits = None
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:
+        avail = os.cpu_count() or 1
+    nthreads = max(1, min(16, avail))
+    S, D = w.S, w.D
+    pairs = synth.draw_sample_pairs(w.seed, w.B, w.H, 4)
+    heads = {}
+    for b, h in pairs:
+        q, k, v, do = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+        heads[(b, h)] = (q, k, v, do)
+    # the backward needs O and LSE of every query: the sample's own forward provides them only for
+    # the rows it covers, so the backward items take O = 0 and LSE = log(visible keys) (the uniform
+    # softmax's), inputs of the right scale for the oracle's arithmetic
+    lse = np.log(np.arange(1, S + 1, dtype=np.float64))
+    zero_o = np.zeros((S, D))
+
+    def fwd_item(bh, r0, r1):
+        q, k, v, _ = heads[bh]
+        at.forward_head(q[:r1], k[:r1], v[:r1], sigma, True, q_rows=np.arange(r0, r1))
+        return 4.0 * D * float(np.sum(np.arange(r0, r1) + 1))
+
+    def bwd_item(bh, qb, kb):
+        q, k, v, do = heads[bh]
+        at.backward_head_blocks(q, k, v, zero_o, do, lse, sigma, True, q_blocks=qb, k_blocks=kb)
+        fl = sum(6.0 * D * float(np.sum(np.arange(32 * i, 32 * i + 32) + 1)) for i in qb)
+        return fl + sum(8.0 * D * float(np.sum(S - np.arange(32 * j, 32 * j + 32))) for j in kb)
+
+    nb = S // 32
+    items = [(fwd_item, (bh, S - 1024 * (i + 1), S - 1024 * i)) for bh in pairs for i in range(2)]
+    items += [(bwd_item, (bh, [nb - 1 - i], [])) for bh in pairs for i in range(4)]
+    items += [(bwd_item, (bh, [], [i])) for bh in pairs for i in range(4)]
+    limit = threadpool_limits(1) if threadpool_limits else None
+    try:
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(nthreads) as ex:
+            flops = sum(ex.map(lambda it: it[0](*it[1]), items))
+        dt = time.perf_counter() - t0
+    finally:
+        if limit is not None:
+            limit.unregister()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"oracle (numpy, float64) on the B8 H32 S8192 D128 causal workload's 4 sampled (batch, head) "
+                      f"pairs {pairs}: forward of the last 2048 query rows and backward of the last 4 query blocks "
+                      f"and the first 4 key blocks of each; {len(items)} work items on {nthreads} threads, "
+                      f"{dt:.1f} s wall, {flops / 1e12:.3f} TFLOP; CPU: {_cpu_model()}, {avail} cores visible"}
 
 
 def _bwd_available(mx) -> bool:

@@ -131,11 +131,20 @@ mx_status mx_varlen_scale_offsets(const int32_t* cu_seqlens, int nseq, int32_t* 
 
 /*
  * mx_quantize_varlen -- mx_quantize for a packed [T, H, D] tensor.
- *   cu_seqlens, cu_scale_rows   device int32 [nseq+1]
- *   total_tokens                T = cu_seqlens[nseq]
+ * Defines: the jagged layout of [News], contributions paragraph (FP8 payload
+ * at its unpadded packed position, scales at padded 128-aligned per-sequence
+ * offsets), with mx_quantize's blocks ([Blog], "Understanding OCP MXFP8
+ * Microscaling on Blackwell"; square blocks: [News], forward/backward
+ * paragraph).
+ *   x                           [T, H, D] in x_dtype (MX_BF16 or MX_F32)
+ *   cu_seqlens, cu_scale_rows   device int32 [nseq+1] (mx_varlen_scale_offsets)
+ *   total_tokens                T = cu_seqlens[nseq] (host int)
  *   total_scale_rows            Tpad = cu_scale_rows[nseq] (a multiple of 128)
- * Blocks along tokens start at each sequence's first token; pad scale
- * slots are written as 0.
+ *   outputs                     payload [T, H, D]; ROW32 scales [Tpad, H, D/32],
+ *                               COL32 [Tpad/32, H, D], SQ32 [Tpad/32, H, D/32]
+ * Blocks along tokens start at each sequence's first token (short tail
+ * blocks); pad scale slots are written as 0.  Errors: as mx_quantize, and
+ * MX_EINVAL for nseq < 1, null offset arrays or negative totals; T = 0: MX_OK.
  */
 mx_status mx_quantize_varlen(const void* x, mx_dtype x_dtype,
                              const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
@@ -198,6 +207,25 @@ mx_status mx_quantize_rows(const void* x, mx_dtype x_dtype, int rows, int K, mx_
                            uint8_t* data, uint8_t* scale, hipStream_t stream);
 
 /*
+ * mx_quantize_rows_varlen -- mx_quantize_rows for a packed [T, H, K] tensor
+ * in the jagged layout: payload rows [T, H, K*w/8] at their packed token
+ * positions, scale rows [Tpad, H, K/32] at the 128-aligned per-sequence
+ * offsets ([News], contributions paragraph), pad rows written as 0.
+ * Defines: as mx_quantize_rows (the MXFP6 / MXFP4 operands of [News],
+ * paragraph on the block-scaled MMA's formats), with the placement above.
+ *   x              [T, H, K] in x_dtype (MX_BF16 or MX_F32), 16-byte aligned
+ *   cu_seqlens, cu_scale_rows   device int32 [nseq+1] (mx_varlen_scale_offsets)
+ *   total_tokens, total_scale_rows   T and Tpad (host ints)
+ *   data, scale    outputs as above
+ * Errors: as mx_quantize_rows, and MX_EINVAL for nseq < 1, null offset arrays
+ * or negative totals; T = 0: MX_OK.  Ownership: caller's buffers.
+ */
+mx_status mx_quantize_rows_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens,
+                                  const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                                  int total_scale_rows, int H, int K, mx_elem format,
+                                  uint8_t* data, uint8_t* scale, hipStream_t stream);
+
+/*
  * mx_gemm_quantize -- MX GEMM with a quantizing epilogue: C = A B^T.
  * Defines: [News], contributions paragraph (fused GEMM + Quantize producers
  * emitting FP8 with several scale layouts in one pass); the block-scaled
@@ -257,9 +285,18 @@ mx_status mx_attn_fwd(const uint8_t* q_data, const uint8_t* q_scale,
                       void* o, mx_dtype o_dtype, float* lse, hipStream_t stream);
 
 /*
- * mx_attn_fwd_varlen -- mx_attn_fwd over packed sequences ([T, H, D]
- * payloads, varlen scale layouts).  Causality is within each sequence.
- * lse is [H, T].  max_seqlen bounds every L_s (host int).
+ * mx_attn_fwd_varlen -- mx_attn_fwd over packed sequences.
+ * Defines: [News], contributions paragraph (a jagged attention whose FP8
+ * payload stays unpadded while its scales sit at 128-aligned per-sequence
+ * offsets), applied to mx_attn_fwd's computation per sequence.
+ *   q_*, k_*   [T, H, D] payloads, ROW32 scales [Tpad, H, D/32]
+ *   v_*        [T, H, D] payload, COL32 scales [Tpad/32, H, D]
+ *   cu_seqlens, cu_scale_rows   device int32 [nseq+1] (as mx_quantize_varlen)
+ *   total_tokens T; max_seqlen bounds every L_s (host ints)
+ *   o          [T, H, D]; lse [H, T] fp32 (may be null)
+ * Causality is within each sequence; empty sequences are allowed.  Errors:
+ * as mx_attn_fwd, and MX_EINVAL for nseq < 1 or null offset arrays; T = 0 or
+ * max_seqlen = 0: MX_OK.  Ownership: caller's buffers.
  */
 mx_status mx_attn_fwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              const uint8_t* k_data, const uint8_t* k_scale,
@@ -441,7 +478,18 @@ mx_status mx_attn_bwd(const uint8_t* q_data, const uint8_t* q_scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * mx_attn_bwd_varlen -- mx_attn_bwd over packed sequences (lse [H, T]).
+ * mx_attn_bwd_varlen -- mx_attn_bwd over packed sequences.
+ * Defines: [News], contributions paragraph (jagged layout: unpadded FP8
+ * payload, scales at 128-aligned per-sequence offsets) applied to
+ * mx_attn_bwd's computation per sequence.
+ *   q_*, k_*, do_*   [T, H, D] payloads, SQ32 scales [Tpad/32, H, D/32]
+ *   v_*              [T, H, D] payload, ROW32 scales [Tpad, H, D/32]
+ *   o, dout          [T, H, D] in io_dtype; lse [H, T] fp32
+ *   cu_seqlens, cu_scale_rows   device int32 [nseq+1]
+ *   dq, dk, dv       [T, H, D] in grad_dtype
+ *   workspace        >= mx_attn_bwd_workspace_bytes(T, H, D) bytes
+ * Causality within each sequence.  Errors: as mx_attn_bwd, and MX_EINVAL for
+ * nseq < 1 or null offset arrays; T = 0 or max_seqlen = 0: MX_OK.
  */
 mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              const uint8_t* k_data, const uint8_t* k_scale,

@@ -39,6 +39,7 @@ _SIGS = {
     "mx_rmsnorm_quantize_varlen": ([_vp, _c_int, _vp, _c_float, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
     "mx_quantize_rows": ([_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "mx_quantize_rows_varlen": ([_vp, _c_int, _vp, _vp] + [_c_int] * 6 + [_vp, _vp, _vp], _c_int),
     "mx_gemm_quantize": ([_vp] * 4 + [_c_int] * 4 + [ctypes.c_uint] + [_vp] * 7 + [_vp], _c_int),
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
@@ -163,6 +164,13 @@ def mx_rmsnorm_quantize_varlen(x, gamma, eps, cu_seqlens, cu_scale_rows, nseq, t
 def mx_quantize_rows(x, rows, K, fmt, data, scale, stream=None):
     _check(lib().mx_quantize_rows(_ptr(x), _dtype_code(x.dtype), rows, K, fmt, _ptr(data), _ptr(scale),
                                   _stream(stream)), "mx_quantize_rows")
+
+
+def mx_quantize_rows_varlen(x, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows, H, K, fmt, data,
+                            scale, stream=None):
+    _check(lib().mx_quantize_rows_varlen(_ptr(x), _dtype_code(x.dtype), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq,
+                                         total_tokens, total_scale_rows, H, K, fmt, _ptr(data), _ptr(scale),
+                                         _stream(stream)), "mx_quantize_rows_varlen")
 
 
 def mx_gemm_quantize(a_data, a_scale, b_data, b_scale, fmt, M, N, K, layouts, c_row32_data, c_row32_scale,
@@ -367,19 +375,15 @@ def quantize_varlen(x, cu_seqlens, seqlens, layouts=ROW32 | COL32 | SQ32):
     return out, csr
 
 
-def quantize_rows_varlen(x, seqlens, fmt=E4M3):
-    """Row quantization (element format fmt) of a packed [T, H, D] tensor with its scale rows at
-    the 128-aligned per-sequence offsets of the jagged layout (one mx_quantize_rows call per
-    sequence; pad rows zero).  Returns (packed data [T, H, D w/8], scales [Tp, H, D/32])."""
+def quantize_rows_varlen(x, cu_seqlens, cu_scale_rows, seqlens, fmt=E4M3):
+    """Row quantization (element format fmt) of a packed [T, H, D] tensor in the jagged layout
+    (mx_quantize_rows_varlen: scale rows at the 128-aligned per-sequence offsets, pad rows zero).
+    Returns (packed data [T, H, D w/8], scales [Tp, H, D/32])."""
     T, H, D = x.shape
+    Tp = padded_scale_rows(seqlens)
     data = torch.empty((T, H, D * ELEM_BITS[fmt] // 8), dtype=torch.uint8, device=x.device)
-    scale = torch.zeros((padded_scale_rows(seqlens), H, D // 32), dtype=torch.uint8, device=x.device)
-    tok = srow = 0
-    for L in (int(v) for v in seqlens):
-        if L:
-            mx_quantize_rows(x[tok:tok + L], L * H, D, fmt, data[tok:tok + L], scale[srow:srow + L])
-        tok += L
-        srow += (L + 127) // 128 * 128
+    scale = torch.empty((Tp, H, D // 32), dtype=torch.uint8, device=x.device)
+    mx_quantize_rows_varlen(x, cu_seqlens, cu_scale_rows, len(seqlens), T, Tp, H, D, fmt, data, scale)
     return data, scale
 
 

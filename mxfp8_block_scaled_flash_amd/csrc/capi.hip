@@ -206,6 +206,21 @@ mx_status mx_quantize_rows(const void* x, mx_dtype x_dtype, int rows, int K, mx_
   return from_hip(mxk::launch_quantize_rows(x, x_dtype == MX_F32, rows, K, (int)format, data, scale, stream));
 }
 
+mx_status mx_quantize_rows_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens,
+                                  const int32_t* cu_scale_rows, int nseq, int total_tokens, int total_scale_rows,
+                                  int H, int K, mx_elem format, uint8_t* data, uint8_t* scale, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || total_scale_rows < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || K < 32 || K % 32 != 0 || !valid_elem(format)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  if ((long)total_scale_rows * H * K > kMaxElems || (long)total_tokens * H * K > kMaxElems) return MX_EINVAL;
+  if (total_scale_rows < total_tokens || total_scale_rows % 128 != 0) return MX_EINVAL;
+  if (total_tokens == 0) return MX_OK;
+  if (!all_aligned({x, data}) || !scale) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_quantize_rows_varlen(x, x_dtype == MX_F32, cu_seqlens, cu_scale_rows, nseq,
+                                                   total_scale_rows, H, K, (int)format, data, scale, stream));
+}
+
 mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const uint8_t* b_data,
                            const uint8_t* b_scale, mx_elem ab_format, int M, int N, int K, unsigned layouts,
                            uint8_t* c_row32_data,

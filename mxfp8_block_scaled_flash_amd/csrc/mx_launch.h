@@ -71,6 +71,9 @@ hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st);
 hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int fmt, uint8_t* data, uint8_t* scale,
                                 hipStream_t st);
+hipError_t launch_quantize_rows_varlen(const void* x, bool fp32, const int32_t* cu, const int32_t* csr, int nseq,
+                                       long total_scale_rows, int H, int K, int fmt, uint8_t* data, uint8_t* scale,
+                                       hipStream_t st);
 hipError_t launch_gemm_quantize(GemmArgs a, hipStream_t st);
 
 }  // namespace mxk

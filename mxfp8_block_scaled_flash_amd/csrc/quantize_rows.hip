@@ -54,15 +54,13 @@ MX_DEV uint32_t encode(float y) {
   return code | sign;
 }
 
+// One 32-element block: src (32 elements) -> W dwords of packed codes at dst, E8M0 scale at *sc.
 template <typename T, int FMT>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, long nblk, uint8_t* __restrict__ data,
-                                                            uint8_t* __restrict__ scale) {
+MX_DEV void quantize_block(const T* __restrict__ src, uint8_t* __restrict__ dst_bytes, uint8_t* __restrict__ sc) {
   using F = Fmt<FMT>;
-  const long b = (long)blockIdx.x * 256 + threadIdx.x;   // block index = row * (K/32) + block in row
-  if (b >= nblk) return;
   float v[32];
   if constexpr (sizeof(T) == 2) {
-    const uint4* p = (const uint4*)(x + b * 32);
+    const uint4* p = (const uint4*)src;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 u = p[c];
@@ -74,7 +72,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
       }
     }
   } else {
-    const float4* p = (const float4*)(x + b * 32);
+    const float4* p = (const float4*)src;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float4 f = p[c];
@@ -96,7 +94,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
     out[wd] |= c << bit;
     if (bit + F::W > 32) out[wd + 1] |= c >> (32 - bit);
   }
-  uint32_t* dst = (uint32_t*)(data + b * (4 * F::W));
+  uint32_t* dst = (uint32_t*)dst_bytes;
   if constexpr (F::W == 8) {
     ((uint4*)dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
     ((uint4*)dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -107,7 +105,45 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
   } else {
     ((uint4*)dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
   }
-  scale[b] = (uint8_t)k;
+  *sc = (uint8_t)k;
+}
+
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, long nblk, uint8_t* __restrict__ data,
+                                                            uint8_t* __restrict__ scale) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;   // block index = row * (K/32) + block in row
+  if (b >= nblk) return;
+  quantize_block<T, FMT>(x + b * 32, data + b * (4 * Fmt<FMT>::W), scale + b);
+}
+
+// Jagged rows: one thread per (scale row, head, 32-element block) of the padded scale tensor
+// [Tp, H, K/32].  Scale row r belongs to the sequence s with cu_scale_rows[s] <= r <
+// cu_scale_rows[s+1] (binary search; empty sequences own no row); a row past the sequence's length
+// is padding and gets scale 0, a row inside it quantizes token cu_seqlens[s] + (r - cu_scale_rows[s]),
+// whose payload stays at its packed position.
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void quantize_rows_varlen_kernel(const T* __restrict__ x, const int32_t* __restrict__ cu,
+                                                                   const int32_t* __restrict__ csr, int nseq, int H,
+                                                                   int kb, long nblk, uint8_t* __restrict__ data,
+                                                                   uint8_t* __restrict__ scale) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;   // ((r * H) + h) * kb + j
+  if (b >= nblk) return;
+  const long rh = b / kb;
+  const int j = (int)(b - rh * kb);
+  const int r = (int)(rh / H), h = (int)(rh - (long)r * H);
+  int lo = 0, hi = nseq - 1;   // largest s in [0, nseq) with csr[s] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (csr[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int t_in = r - csr[lo];
+  if (t_in >= cu[lo + 1] - cu[lo]) {
+    scale[b] = 0;
+    return;
+  }
+  const long src = ((long)(cu[lo] + t_in) * H + h) * kb + j;   // block index in the packed payload
+  quantize_block<T, FMT>(x + src * 32, data + src * (4 * Fmt<FMT>::W), scale + b);
 }
 
 }  // namespace
@@ -125,6 +161,27 @@ hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int 
   }
   MX_QR_CASE(0) MX_QR_CASE(2) MX_QR_CASE(3) MX_QR_CASE(4)
 #undef MX_QR_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_rows_varlen(const void* x, bool fp32, const int32_t* cu, const int32_t* csr, int nseq,
+                                       long total_scale_rows, int H, int K, int fmt, uint8_t* data, uint8_t* scale,
+                                       hipStream_t st) {
+  const int kb = K / 32;
+  const long nblk = total_scale_rows * H * kb;
+  if (nblk == 0) return hipSuccess;
+  dim3 g((unsigned)((nblk + 255) / 256)), b(256);
+#define MX_QRV_CASE(F)                                                                                        \
+  if (fmt == F) {                                                                                             \
+    if (fp32)                                                                                                 \
+      quantize_rows_varlen_kernel<float, F><<<g, b, 0, st>>>((const float*)x, cu, csr, nseq, H, kb, nblk, data, scale); \
+    else                                                                                                      \
+      quantize_rows_varlen_kernel<uint16_t, F><<<g, b, 0, st>>>((const uint16_t*)x, cu, csr, nseq, H, kb, nblk, data, \
+                                                                  scale);                                     \
+    return hipGetLastError();                                                                                 \
+  }
+  MX_QRV_CASE(0) MX_QRV_CASE(2) MX_QRV_CASE(3) MX_QRV_CASE(4)
+#undef MX_QRV_CASE
   return hipErrorInvalidValue;
 }
 

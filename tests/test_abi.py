@@ -285,3 +285,18 @@ def test_noalloc_backward_rejects_invalid_and_oversized_calls_before_the_device(
     assert L.mx_attn_bwd_workspace_bytes(2 * 8192, 16, 128) <= 128 << 20
     assert call(a12=4, a13=8192, a14=16) == EWORKSPACE
     assert call(a12=8, a13=8192, a14=32) == EWORKSPACE
+
+
+def test_quantize_rows_varlen_validation():
+    L = mx.lib()
+    ok = dict(x=16, dt=mx.BF16, cu=16, csr=16, nseq=2, T=100, Tp=256, H=2, K=64, fmt=mx.E2M1, d=16, s=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mx_quantize_rows_varlen(a["x"], a["dt"], a["cu"], a["csr"], a["nseq"], a["T"], a["Tp"], a["H"],
+                                         a["K"], a["fmt"], a["d"], a["s"], None)
+    for bad in (dict(cu=None), dict(csr=None), dict(nseq=0), dict(T=-1), dict(Tp=100), dict(Tp=64), dict(K=48),
+                dict(fmt=1), dict(dt=mx.F16), dict(H=0), dict(x=None), dict(d=24), dict(s=None)):
+        assert call(**bad) == EINVAL, bad
+    assert call(T=0) == 0

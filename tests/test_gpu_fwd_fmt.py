@@ -100,9 +100,9 @@ def test_forward_qk_format_varlen_sampled(fmt):
     log(f"fwd {FMTS[fmt]} varlen T={cu[-1]}")
     x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v")}
     cu_d = torch.from_numpy(cu).cuda()
-    qf = mx.quantize_rows_varlen(x["q"], w.seqlens, fmt)
-    kf = mx.quantize_rows_varlen(x["k"], w.seqlens, fmt)
     vq, csr = mx.quantize_varlen(x["v"], cu_d, w.seqlens, mx.COL32)
+    qf = mx.quantize_rows_varlen(x["q"], cu_d, csr, w.seqlens, fmt)
+    kf = mx.quantize_rows_varlen(x["k"], cu_d, csr, w.seqlens, fmt)
     o, lse = mx.attn_fwd_fmt_varlen(qf, kf, vq[mx.COL32], cu_d, csr, w.seqlens, sigma, True, fmt, torch.float32)
     torch.cuda.synchronize()
     xn = {t: x[t].double().cpu().numpy() for t in x}

@@ -113,3 +113,34 @@ def test_gemm_from_the_gpu_quantizer_end_to_end():
         rel = float(np.linalg.norm(c.double().cpu().numpy() - full) / np.linalg.norm(full))
         log(f"end to end {FMTS[fmt]}: rel Frobenius error vs the unquantized product {rel:.3e}")
         assert rel < {mx.E4M3: 0.05, mx.E2M3: 0.1, mx.E3M2: 0.2, mx.E2M1: 0.4}[fmt]
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
+@pytest.mark.parametrize("seqlens", [[5, 128, 33, 200, 0, 64], [0, 1, 0, 300, 0]])
+def test_quantize_rows_varlen_places_scale_rows_at_the_padded_offsets(fmt, seqlens):
+    """mx_quantize_rows_varlen: payload rows at the packed token positions, scale rows at the
+    oracle's 128-aligned per-sequence offsets (empty sequences own none), pad rows 0, every byte
+    equal to the oracle's per-sequence row quantization."""
+    H, D = 3, 64
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    T = int(cu[-1])
+    x = _data(T * H, D, 40 + fmt).reshape(T, H, D)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    x = xt.double().numpy()
+    cu_d = torch.from_numpy(cu).cuda()
+    csr = torch.empty(len(seqlens) + 1, dtype=torch.int32, device="cuda")
+    mx.mx_varlen_scale_offsets(cu_d, len(seqlens), csr)
+    d, s = mx.quantize_rows_varlen(xt.cuda(), cu_d, csr, seqlens, fmt)
+    torch.cuda.synchronize()
+    po = omx.padded_offsets(seqlens)
+    assert to_np(csr).tolist() == po.tolist()
+    gd, gs = to_np(d), to_np(s)
+    ref_s = np.zeros_like(gs)
+    for i in range(len(seqlens)):
+        a, b = cu[i], cu[i + 1]
+        if a == b:
+            continue
+        rd, rs, _, _ = _oracle_rows(x[a:b].reshape(-1, D), fmt)
+        assert np.array_equal(gd[a:b].reshape(rd.shape), rd), (FMTS[fmt], i)
+        ref_s[po[i]:po[i] + (b - a)] = rs.reshape(b - a, H, D // 32)
+    assert np.array_equal(gs, ref_s), FMTS[fmt]
