@@ -13,14 +13,14 @@
 //  1. bwd_pre_kernel: D_i = sum_d dO_id O_id in fp32 from the unquantized
 //     tensors, and zero the fp16 dQ accumulator (head-major [H, T, D], so a
 //     head's rows are contiguous for the atomics).
-//  2. attn_bwd_kernel: one workgroup per (sequence, head, 128-key tile),
-//     four waves of 32 keys, walking 64-query tiles.  Per tile each wave
+//  2. attn_bwd_kernel: one workgroup per (sequence, head, 256-key tile),
+//     eight waves of 32 keys, walking 64-query tiles.  Per tile each wave
 //     computes S = Q^ K^T and dP = dO^ V^T (scaled MFMA, keys as the output
 //     columns so a lane owns one key), p = exp2(S c - LSE log2 e),
 //     dS = p (dP - D), then MX codes of P (32 queries per key) and of dS
 //     (square 32 x 32 blocks, wave-wide amax), and accumulates dV^T and
 //     dK^T in registers.  The dS codes go to LDS, and the workgroup's waves
-//     then form dQ = dS K for the tile (128 keys of contraction) and add it,
+//     then form dQ = dS K for the tile (256 keys of contraction) and add it,
 //     scaled by softmax_scale * 2^s, into the fp16 accumulator with packed
 //     fp16 atomics laid along contiguous features (neighbouring lanes pair
 //     up), so each atomic instruction touches four 64-byte row segments.  Q^ and dO^ are read from LDS in both
@@ -320,15 +320,19 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       if (q0 + 32 * t < L) {
         v16f acc = v16f{};
         int kscale[BN / 64], sscale[BN / 64];
+        // all operands first, then the four products: one LDS round trip instead of four.  Key
+        // blocks after every query of the block carry zero dS codes (masked or cleared in A), so
+        // they are multiplied in rather than branched around.
+        v8i sbv[BN / 64], kav[BN / 64];
 #pragma unroll
         for (int kk = 0; kk < BN / 64; ++kk) {
           sscale[kk] = sDSs[bufc][t][2 * kk + g];
           kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-          if (CAUSAL && kbase + 64 * kk > q0 + 32 * t + 31) continue;   // every key after every query
-          const v8i sb = tr_operand(sDS[bufc] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-          const v8i ka = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);   // columns: features
-          acc = mfma32b<0, 0>(sb, ka, acc, sscale[kk], kscale[kk]);
+          sbv[kk] = tr_operand(sDS[bufc] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+          kav[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);         // columns: features
         }
+#pragma unroll
+        for (int kk = 0; kk < BN / 64; ++kk) acc = mfma32b<0, 0>(sbv[kk], kav[kk], acc, sscale[kk], kscale[kk]);
         keep(acc[0]);
 #pragma unroll
         for (int kk = 0; kk < BN / 64; ++kk) {
