@@ -11,7 +11,9 @@ are pinned here against things outside themselves:
     the extremes +-eps) lands inside them -- the bounds hold what they claim to hold;
   * the instruction model (tests/hw/mfma_model.py, a measured characterisation of gfx950's
     block-scaled instruction) lands inside them on a workload with 50x outliers;
-  * round_interval against brute-force quantization of sampled values.
+  * round_interval against brute-force quantization of sampled values;
+  * tightness: plausible mistakes planted in the oracle (a 1% softmax-scale error, LSE in the
+    wrong log base, D_i dropped from dS, a flipped sign, the causal diagonal hidden) fall outside.
 Besides: the backward's online quantizations are pinned to their blockings ([News],
 forward/backward and contributions paragraphs: dS in square [32 x 32] blocks, P for dV in
 blocks of 32 queries per key) by a hand-derived closed form that every other blocking
@@ -243,3 +245,34 @@ def test_padded_offsets_literal_values():
     assert mx.padded_offsets([129]).tolist() == [0, 256]
     assert mx.padded_offsets([]).tolist() == [0]
     assert mx.padded_offsets([0, 0, 1]).tolist() == [0, 0, 0, 128]
+
+
+def _outside_share(x, lo, hi):
+    return float(np.mean((x < lo) | (x > hi)))
+
+
+def test_bounds_catch_planted_mistakes():
+    """Tightness: the admissible intervals are narrow enough that plausible kernel mistakes, planted
+    here in the oracle on the CPU, land outside them -- a softmax scale off by 1% (a wrong c), the
+    LSE left in log2 units, the D_i term dropped from dS (dS = p dP), dO's sign flipped in dP, and a
+    causal mask that also hides the diagonal (rows shifted by one key)."""
+    q, k, v, do = _case(7, L=128)
+    sig = 0.125
+    b = at.forward_head_bounds(q, k, v, sig, True)
+    f = at.forward_head(q, k, v, sig, True)
+    assert _inside(f["O"], b["O_lo"], b["O_hi"])
+    wrong_c = at.forward_head(q, k, v, sig * 1.01, True)
+    assert _outside_share(wrong_c["O"], b["O_lo"], b["O_hi"]) > 0.05
+    assert _outside_share(f["LSE"] / math.log(2), b["LSE_lo"], b["LSE_hi"]) > 0.9
+    # diagonal hidden too: row i sees keys < i, i.e. the causal result of keys shifted down by one
+    k_shift, v_shift = np.roll(k, 1, axis=0), np.roll(v, 1, axis=0)
+    no_diag = at.forward_head(q, k_shift, v_shift, sig, True)
+    assert _outside_share(no_diag["O"][1:], b["O_lo"][1:], b["O_hi"][1:]) > 0.5
+    o, lse = at.bf16(f["O"]), at.fl32(f["LSE"])
+    bb = at.backward_bounds(q, k, v, o, do, lse, sig, True)
+    no_d = at.backward_head(q, k, v, np.zeros_like(o), do, lse, sig, True)   # D_i = 0: dS = p dP
+    for n in ("dQ", "dK"):
+        assert _outside_share(no_d[n], *bb[n]) > 0.05, n
+    flipped = at.backward_head(q, k, v, o, -do, lse, sig, True)              # every gradient negated
+    for n in ("dQ", "dK", "dV"):
+        assert _outside_share(flipped[n], *bb[n]) > 0.5, n
