@@ -94,11 +94,16 @@ def _quantize_keys(x):
     return vals, gm.magnitudes(vals, mx.element_exponent_col32(c, k, axis=0))
 
 
-def _quantize_sq(x):
-    """Square [32 tokens x 32 features] blocks (Q, K, dO in the backward); (values, magnitudes)."""
-    c, k = mx.quantize_sq32(x, 0)
-    vals = mx.dequantize_sq32(c, k, 0)
-    return vals, gm.magnitudes(vals, mx.element_exponent_sq32(c, k, 0))
+def _quantize_sq(x, fmt="e4m3"):
+    """Square [32 tokens x 32 features] blocks (Q, K, dO in the backward); (values, magnitudes).
+    fmt: MXFP8 E4M3, or for Q and K the MXFP6 / MXFP4 elements (oracle/mxsmall.py)."""
+    if fmt == "e4m3":
+        c, k = mx.quantize_sq32(x, 0)
+        vals = mx.dequantize_sq32(c, k, 0)
+        return vals, gm.magnitudes(vals, mx.element_exponent_sq32(c, k, 0))
+    c, k = ms.quantize_sq32(x, fmt)
+    vals = ms.dequantize_sq32(c, k, fmt)
+    return vals, gm.magnitudes(vals, ms.element_exponent_sq32(c, k, fmt))
 
 
 def _quantize_row(x):
@@ -218,13 +223,15 @@ def forward_head_bounds(q, k, v, sigma, causal, q_rows=None, qk_fmt="e4m3", mma=
 
 # ---------------------------------------------------------------- backward
 def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False, p_round=None,
-                  s_delta=None, dp_delta=None):
+                  s_delta=None, dp_delta=None, qk_fmt="e4m3"):
     """One (batch, head) backward.  o, do: [L, D] (the forward output as the
     caller holds it, and the incoming gradient); lse: [L] (fp32 values).
     ``p_round="bf16"`` (with ``quantize=False``): the BF16 baseline, in which P
     (for dV) and dS (for dK and dQ) enter their products rounded to bfloat16.
     ``s_delta``, ``dp_delta`` (tests only): added to the exact sums of S' and dP before their
     fp32 rounding (see forward_head).
+    ``qk_fmt``: element format of Q and K in their square blocks ("e4m3", or MXFP6 "e2m3" /
+    "e3m2", MXFP4 "e2m1"); dO, V, P and dS stay MXFP8.
 
     Returns float64 dQ, dK, dV [L, D] and the internals (p, dS, D).
     """
@@ -232,7 +239,7 @@ def backward_head(q, k, v, o, do, lse, sigma, causal, quantize=True, exact=False
     lse = np.asarray(lse, np.float64)
     r = (lambda a: np.asarray(a, np.float64)) if exact else fl32
     if quantize:
-        (qs, _), (ks, _), (dos, _) = _quantize_sq(q), _quantize_sq(k), _quantize_sq(do)
+        (qs, _), (ks, _), (dos, _) = _quantize_sq(q, qk_fmt), _quantize_sq(k, qk_fmt), _quantize_sq(do)
         vr, _ = _quantize_row(v)
     else:
         qs, ks, dos, vr = q, k, do, v
@@ -265,7 +272,7 @@ def _rows_of(blocks, L):
         np.zeros(0, np.int64)
 
 
-def backward_head_blocks(q, k, v, o, do, lse, sigma, causal, q_blocks=(), k_blocks=()):
+def backward_head_blocks(q, k, v, o, do, lse, sigma, causal, q_blocks=(), k_blocks=(), qk_fmt="e4m3"):
     """backward_head for selected 32-row blocks only: dQ of the query blocks in q_blocks and dK, dV
     of the key blocks in k_blocks.  Every step is local to such a block: the square [32 x 32] dS
     blocks of one query block need only that block's rows against all keys, and P's 32-query blocks
@@ -276,7 +283,7 @@ def backward_head_blocks(q, k, v, o, do, lse, sigma, causal, q_blocks=(), k_bloc
     q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
     lse = np.asarray(lse, np.float64)
     L = q.shape[0]
-    (qs, _), (ks, _), (dos, _) = _quantize_sq(q), _quantize_sq(k), _quantize_sq(do)
+    (qs, _), (ks, _), (dos, _) = _quantize_sq(q, qk_fmt), _quantize_sq(k, qk_fmt), _quantize_sq(do)
     vr, _ = _quantize_row(v)
     c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
     Dv = fl32(np.sum(do * o, axis=1))
@@ -326,7 +333,7 @@ def _interval_matmul(a_lo, a_hi, b):
 
 
 def backward_bounds(q, k, v, o, do, lse, sigma, causal, q_blocks=None, k_blocks=None, mma=True, fp32=True,
-                    chunk=8):
+                    chunk=8, qk_fmt="e4m3"):
     """The admissible dQ (rows of q_blocks), dK and dV (rows of k_blocks) of one (batch, head):
     backward_head's steps on intervals, as forward_head_bounds does for the forward.
       * S' and dP within eps of their exact sums -> p = 2^(S' c - LSE log2 e) in [p_lo, p_hi];
@@ -344,7 +351,7 @@ def backward_bounds(q, k, v, o, do, lse, sigma, causal, q_blocks=None, k_blocks=
     nb = (L + 31) // 32
     q_blocks = list(range(nb)) if q_blocks is None else list(q_blocks)
     k_blocks = list(range(nb)) if k_blocks is None else list(k_blocks)
-    (qs, qm), (ks, km), (dos, dm) = _quantize_sq(q), _quantize_sq(k), _quantize_sq(do)
+    (qs, qm), (ks, km), (dos, dm) = _quantize_sq(q, qk_fmt), _quantize_sq(k, qk_fmt), _quantize_sq(do)
     vr, vm = _quantize_row(v)
     c, L2 = log2_scale(sigma), fl32(lse * LOG2E32)
     Dv = fl32(np.sum(do * o, axis=1))
@@ -486,9 +493,10 @@ def mx_attention_forward(q, k, v, sigma, causal, cu_seqlens=None, bf16_baseline=
     return O, LSE
 
 
-def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None, bf16_baseline=False):
+def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None, bf16_baseline=False, qk_fmt="e4m3"):
     """Backward over whole tensors; lse is [B, H, S] (or [H, T]).  Returns float64 dQ, dK, dV.
-    ``bf16_baseline``: no MX step, P and dS rounded to bfloat16 before their products."""
+    ``bf16_baseline``: no MX step, P and dS rounded to bfloat16 before their products.
+    ``qk_fmt``: element format of Q and K (backward_head)."""
     q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
     lse = np.asarray(lse, np.float64)
     dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -505,7 +513,7 @@ def mx_attention_backward(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None, b
             sl = (slice(cu_seqlens[a], cu_seqlens[a + 1]), h, slice(None))
         res = (backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal, quantize=False,
                              p_round="bf16") if bf16_baseline
-               else backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal))
+               else backward_head(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal, qk_fmt=qk_fmt))
         dQ[sl], dK[sl], dV[sl] = res["dQ"], res["dK"], res["dV"]
     return dQ, dK, dV
 
@@ -533,9 +541,9 @@ def mx_attention_forward_bounds(q, k, v, sigma, causal, cu_seqlens=None, qk_fmt=
     return O_lo, O_hi, L_lo, L_hi
 
 
-def mx_attention_backward_bounds(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None):
+def mx_attention_backward_bounds(q, k, v, o, do, lse, sigma, causal, cu_seqlens=None, qk_fmt="e4m3"):
     """backward_bounds over whole tensors; returns {"dQ": (lo, hi), "dK": ..., "dV": ...} in the
-    inputs' layout."""
+    inputs' layout.  ``qk_fmt``: element format of Q and K."""
     q, k, v, o, do = (np.asarray(a, np.float64) for a in (q, k, v, o, do))
     lse = np.asarray(lse, np.float64)
     out = {n: (np.zeros_like(q), np.zeros_like(q)) for n in ("dQ", "dK", "dV")}
@@ -550,7 +558,7 @@ def mx_attention_backward_bounds(q, k, v, o, do, lse, sigma, causal, cu_seqlens=
         else:
             lh = lse[h, cu_seqlens[a]:cu_seqlens[a + 1]]
             sl = (slice(cu_seqlens[a], cu_seqlens[a + 1]), h, slice(None))
-        b = backward_bounds(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal)
+        b = backward_bounds(qh, K[key], V[key], Oh[key], DOh[key], lh, sigma, causal, qk_fmt=qk_fmt)
         for n in out:
             out[n][0][sl], out[n][1][sl] = b[n]
     return out

@@ -140,3 +140,55 @@ def unpack(data, n: int, fmt: str) -> np.ndarray:
     bits = ((d[..., :, None] >> np.arange(8, dtype=np.uint64)) & 1).reshape(*d.shape[:-1], -1)[..., :n * w]
     f = bits.reshape(*d.shape[:-1], n, w)
     return (f << np.arange(w, dtype=np.uint64)).sum(axis=-1).astype(np.uint8)
+
+
+# ------------------------------------------------------------------ square blocks
+def quantize_sq32(x, fmt: str):
+    """Square [32 tokens x 32 features] blocks of a [L, D] head (Q, K in the backward with MXFP6 /
+    MXFP4 operands: the backward's square blocks, [News] forward/backward paragraph, in the small
+    element formats of the same paragraph family), blocked from (0, 0); a short tail block along the
+    tokens holds the remaining rows.  Scale per block by this format's rule (scale_code).
+    Returns (codes [L, D], one per element, unpacked) and scale codes [ceil(L/32), D/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    L, D = x.shape
+    assert D % BLOCK == 0
+    nb = (L + BLOCK - 1) // BLOCK
+    xp = np.zeros((nb * BLOCK, D))
+    xp[:L] = x
+    blk = xp.reshape(nb, BLOCK, D // BLOCK, BLOCK).swapaxes(1, 2)      # [nb, D/32, 32 tok, 32 feat]
+    k = scale_code(np.max(np.abs(blk), axis=(2, 3)), fmt)
+    y = blk * np.exp2(E8M0_BIAS - k.astype(np.float64))[:, :, None, None]
+    codes = encode(y, fmt).swapaxes(1, 2).reshape(nb * BLOCK, D)[:L]
+    return codes, k
+
+
+def dequantize_sq32(codes, k, fmt: str) -> np.ndarray:
+    codes = np.asarray(codes)
+    L, D = codes.shape
+    s = np.repeat(np.repeat(np.exp2(np.asarray(k).astype(np.float64) - E8M0_BIAS), BLOCK, axis=0), BLOCK, axis=1)
+    return decode(codes, fmt) * s[:L, :D]
+
+
+def element_exponent_sq32(codes, k, fmt: str) -> np.ndarray:
+    """As element_exponent_rows, for square blocks."""
+    eb, mb, bias, _ = FORMATS[fmt]
+    codes = np.asarray(codes).astype(np.int64)
+    L, D = codes.shape
+    E = (codes >> mb) & ((1 << eb) - 1)
+    e = np.where(E == 0, 1 - bias, E - bias)
+    ks = np.repeat(np.repeat(np.asarray(k).astype(np.int64) - E8M0_BIAS, BLOCK, axis=0), BLOCK, axis=1)
+    return e + ks[:L, :D]
+
+
+def pack_sq32_columns(codes, fmt: str) -> np.ndarray:
+    """The column-packed copy of square-block codes: for block row b and feature f, the 32 tokens
+    32 b .. 32 b + 31 of column f as one packed block (tokens past L as code 0).  The instruction
+    reads a transposed operand (contraction over tokens) as such blocks.  Returns bytes
+    [ceil(L/32), D, 32 w / 8]."""
+    codes = np.asarray(codes)
+    L, D = codes.shape
+    nb = (L + BLOCK - 1) // BLOCK
+    cp = np.zeros((nb * BLOCK, D), dtype=np.uint8)
+    cp[:L] = codes
+    cols = cp.reshape(nb, BLOCK, D).swapaxes(1, 2)                      # [nb, D, 32 tokens]
+    return pack(cols, fmt)

@@ -228,14 +228,14 @@ def _check_blocks(gq, gk, gv, args, qb, kb, what):
 
 @pytest.mark.timeout(600)
 def test_backward_llm_shape_sampled_blocks():
-    """The metric shape (B8 H32 S8192 D128, causal) in the call bench.py times.  Two sampled
-    (batch, head) pairs carry O and LSE from the oracle forward; every other head holds an inert
-    filler (O = 0, LSE = 30, so its p is ~0), since only the sampled heads are compared.  dQ of
-    sampled query blocks and dK, dV of sampled key blocks (first, last and random ones)."""
+    """The metric shape (B8 H32 S8192 D128, causal) in the call bench.py times.  The workload's four
+    seeded (batch, head) pairs carry O and LSE from the oracle forward; every other head holds an
+    inert filler (O = 0, LSE = 30, so its p is ~0), since only the sampled heads are compared.  dQ
+    of sampled query blocks and dK, dV of sampled key blocks (first, last and random ones)."""
     w = synth.workload("llm")
     B, S, H, D = w.B, w.S, w.H, w.D
     sigma = 1 / math.sqrt(D)
-    pairs = synth.draw_sample_pairs(w.seed, B, H, 2)
+    pairs = synth.draw_sample_pairs(w.seed, B, H, 4)
     log(f"bwd llm {w.shape()} heads {pairs}")
     o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, H, S), 30.0, device="cuda")

@@ -141,3 +141,113 @@ def test_attention_qk_formats_stay_close_to_float64_attention(fmt, floor):
     ref = at.forward_head(q, k, v, 0.125, True, quantize=False, exact=True)["O"]
     o = at.forward_head(q, k, v, 0.125, True, qk_fmt=fmt)["O"]
     assert np.sum(o * ref) / np.linalg.norm(o) / np.linalg.norm(ref) >= floor
+
+
+# ---------------------------------------------------------------- square blocks (backward)
+def _e2m1_brute_sq(x):
+    """E2M1 square [32 x 32] blocks by search: per block scale 2^(floor(log2 amax) - 2) over all
+    1024 entries, each element the nearest magnitude (ties to the even code)."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    out = np.zeros_like(x)
+    for r0 in range(0, x.shape[0], 32):
+        for c0 in range(0, x.shape[1], 32):
+            blk = x[r0:r0 + 32, c0:c0 + 32]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                continue
+            s = 2.0 ** (math.floor(math.log2(amax)) - 2)
+            for (i, j), y in np.ndenumerate(blk):
+                d = np.abs(np.abs(y) / s - mags)
+                best = np.flatnonzero(d == d.min())
+                code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+                out[r0 + i, c0 + j] = math.copysign(mags[code] * s, y)
+    return out
+
+
+def test_square_blocks_e2m1_match_a_brute_force_quantizer():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((70, 64)) * np.exp2(rng.integers(-4, 5, size=(70, 1)))   # a ragged tail
+    c, k = ms.quantize_sq32(x, "e2m1")
+    assert np.array_equal(ms.dequantize_sq32(c, k, "e2m1"), _e2m1_brute_sq(x))
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2", "e2m1"])
+def test_square_blocks_transpose_invariant_and_exact_on_representable_blocks(fmt):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 64))
+    c, k = ms.quantize_sq32(x, fmt)
+    ct, kt = ms.quantize_sq32(x.T, fmt)
+    assert np.array_equal(ct, c.T) and np.array_equal(kt, k.T)
+    # values already on the grid of one block scale come back unchanged
+    y = ms.dequantize_sq32(c, k, fmt)
+    c2, k2 = ms.quantize_sq32(y, fmt)
+    assert np.array_equal(ms.dequantize_sq32(c2, k2, fmt), y)
+    # the block max sets the scale: floor(log2 amax) - emax + 127
+    blk = np.abs(x[:32, :32]).max()
+    assert int(k[0, 0]) == math.floor(math.log2(blk)) - ms.FORMATS[fmt][3] + 127
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e2m1"])
+def test_column_packed_copy_holds_each_token_block_of_each_feature(fmt):
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((45, 64))              # second block row: 13 tokens, the rest zero codes
+    c, _ = ms.quantize_sq32(x, fmt)
+    cols = ms.pack_sq32_columns(c, fmt)
+    assert cols.shape == (2, 64, 32 * ms.BITS[fmt] // 8)
+    back = ms.unpack(cols, 32, fmt)                 # [2, 64, 32 tokens]
+    for b in range(2):
+        for f in (0, 17, 63):
+            want = np.zeros(32, dtype=np.uint8)
+            n = min(32, 45 - 32 * b)
+            want[:n] = c[32 * b:32 * b + n, f]
+            assert np.array_equal(back[b, f], want)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2", "e2m1"])
+def test_backward_qk_formats_agree_on_representable_operands(fmt):
+    """Q and K on a grid every square block represents exactly in the small format (and in E4M3):
+    the backward in that format equals the MXFP8 backward bit for bit."""
+    from oracle import attention as at
+    L, D = 80, 64
+    rng = np.random.default_rng(9)
+    mags = np.array([1.0, 1.5, 2.0, 3.0])        # in every format's grid under a common block scale
+    q = rng.choice(mags, (L, D)) * rng.choice([-1.0, 1.0], (L, D)) * 0.5
+    k = rng.choice(mags, (L, D)) * rng.choice([-1.0, 1.0], (L, D)) * 0.25
+    v, do = (rng.standard_normal((L, D)) for _ in range(2))
+    f = at.forward_head(q, k, v, 0.125, True)
+    o, lse = at.bf16(f["O"]), at.fl32(f["LSE"])
+    a = at.backward_head(q, k, v, o, do, lse, 0.125, True, qk_fmt=fmt)
+    b = at.backward_head(q, k, v, o, do, lse, 0.125, True)
+    for n in ("dQ", "dK", "dV", "S"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e2m1"])
+def test_backward_qk_format_bounds_collapse_and_contain_the_oracle(fmt):
+    from oracle import attention as at
+    rng = np.random.default_rng(10)
+    L, D = 96, 64
+    q, k, v, do = (rng.standard_normal((L, D)) for _ in range(4))
+    f = at.forward_head(q, k, v, 0.125, True)
+    o, lse = at.bf16(f["O"]), at.fl32(f["LSE"])
+    g = at.backward_head(q, k, v, o, do, lse, 0.125, True, qk_fmt=fmt)
+    tight = at.backward_bounds(q, k, v, o, do, lse, 0.125, True, mma=False, fp32=False, qk_fmt=fmt)
+    wide = at.backward_bounds(q, k, v, o, do, lse, 0.125, True, qk_fmt=fmt)
+    for n in ("dQ", "dK", "dV"):
+        scale = np.max(np.abs(g[n]))
+        assert np.max(np.abs(tight[n][0] - g[n])) <= 1e-12 * scale, n
+        assert np.all((wide[n][0] <= g[n]) & (g[n] <= wide[n][1])), n
+
+
+@pytest.mark.parametrize("fmt,floor", [("e2m3", 0.98), ("e2m1", 0.9)])
+def test_backward_qk_formats_stay_close_to_float64_gradients(fmt, floor):
+    from oracle import attention as at
+    rng = np.random.default_rng(11)
+    L, D = 96, 64
+    q, k, v, do = (rng.standard_normal((L, D)) for _ in range(4))
+    ref = at.attention_fp64_backward(q, k, v, do, 0.125, True)
+    f = at.forward_head(q, k, v, 0.125, True)
+    g = at.backward_head(q, k, v, at.bf16(f["O"]), do, at.fl32(f["LSE"]), 0.125, True, qk_fmt=fmt)
+    for i, n in enumerate(("dQ", "dK", "dV")):
+        x, y = g[n], ref[i]
+        assert np.sum(x * y) / np.linalg.norm(x) / np.linalg.norm(y) >= floor, n
