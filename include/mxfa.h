@@ -226,6 +226,43 @@ mx_status mx_quantize_rows_varlen(const void* x, mx_dtype x_dtype, const int32_t
                                   uint8_t* data, uint8_t* scale, hipStream_t stream);
 
 /*
+ * mx_quantize_sq_fmt -- square [32 tokens x 32 features] blocks of a [B, S, H, D]
+ * tensor in a small element format, for the backward's Q and K with MXFP6 /
+ * MXFP4 payloads (mx_attn_bwd_fmt).
+ * Defines: [News], forward/backward paragraph (Q, K in square [32, 32] blocks
+ * so one set of codes serves both orientations) with the element formats of
+ * [News]' paragraph on the block-scaled MMA (OCP MX E2M3, E3M2, E2M1); the E8M0
+ * scale of a block is clamp(floor(log2 amax) - emax + 127, 0, 254), emax 2, 4, 2.
+ * Blocks start at token 0 and feature 0; a short tail block holds the rest.
+ *   x          [B, S, H, D] in x_dtype (MX_BF16 or MX_F32), 16-byte aligned; D = 64 or 128
+ *   format     MX_E2M3, MX_E3M2 or MX_E2M1
+ *   row_data   [B, S, H, D*w/8] bytes: each token row along D, packed as the
+ *              matrix instruction reads it (element j at bits [w j, w j + w))
+ *   col_data   [B, ceil(S/32), H, D, 32*w/8] bytes: for each block row and
+ *              feature, that feature's 32 tokens packed the same way (tokens
+ *              past S as code 0) -- the same codes read across the rows
+ *   scale      [B, ceil(S/32), H, D/32] E8M0 bytes (the SQ32 scale layout)
+ * Errors: MX_EINVAL for a bad shape, format, dtype, alignment or null
+ * output; B*S = 0: MX_OK.  Ownership: caller's buffers.
+ */
+mx_status mx_quantize_sq_fmt(const void* x, mx_dtype x_dtype, int B, int S, int H, int D, mx_elem format,
+                             uint8_t* row_data, uint8_t* col_data, uint8_t* scale, hipStream_t stream);
+
+/*
+ * mx_quantize_sq_fmt_varlen -- mx_quantize_sq_fmt for a packed [T, H, D] tensor
+ * in the jagged layout ([News], contributions paragraph): row_data [T, H, D*w/8]
+ * at the packed token positions; col_data [Tpad/32, H, D, 32*w/8] and scale
+ * [Tpad/32, H, D/32] at the 128-aligned per-sequence block rows, pad rows
+ * written as 0.  Sequence arguments as mx_quantize_rows_varlen.
+ * Errors: as mx_quantize_sq_fmt, and as mx_quantize_rows_varlen for the
+ * sequence arguments; T = 0: MX_OK.  Ownership: caller's buffers.
+ */
+mx_status mx_quantize_sq_fmt_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens,
+                                    const int32_t* cu_scale_rows, int nseq, int total_tokens,
+                                    int total_scale_rows, int H, int D, mx_elem format,
+                                    uint8_t* row_data, uint8_t* col_data, uint8_t* scale, hipStream_t stream);
+
+/*
  * mx_gemm_quantize -- MX GEMM with a quantizing epilogue: C = A B^T.
  * Defines: [News], contributions paragraph (fused GEMM + Quantize producers
  * emitting FP8 with several scale layouts in one pass); the block-scaled

@@ -40,6 +40,8 @@ _SIGS = {
                                     ctypes.c_uint] + [_vp] * 6 + [_vp], _c_int),
     "mx_quantize_rows": ([_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "mx_quantize_rows_varlen": ([_vp, _c_int, _vp, _vp] + [_c_int] * 6 + [_vp, _vp, _vp], _c_int),
+    "mx_quantize_sq_fmt": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp], _c_int),
+    "mx_quantize_sq_fmt_varlen": ([_vp, _c_int, _vp, _vp] + [_c_int] * 6 + [_vp, _vp, _vp, _vp], _c_int),
     "mx_gemm_quantize": ([_vp] * 4 + [_c_int] * 4 + [ctypes.c_uint] + [_vp] * 7 + [_vp], _c_int),
     "mx_attn_fwd": ([_vp] * 6 + [_c_int] * 4 + [_c_float, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "mx_attn_fwd_varlen": ([_vp] * 6 + [_vp, _vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp, _vp],
@@ -345,6 +347,44 @@ def gemm_quantize(a, b, layouts=ROW32 | COL32 | SQ32, with_f32=False, fmt=E4M3):
     mx_gemm_quantize(a[0], a[1], b[0], b[1], fmt, M, N, K, layouts, g(ROW32, 0), g(ROW32, 1), g(COL32, 0),
                      g(COL32, 1), g(SQ32, 0), g(SQ32, 1), c32)
     return out, c32
+
+
+def mx_quantize_sq_fmt(x, B, S, H, D, fmt, row_data, col_data, scale, stream=None):
+    _check(lib().mx_quantize_sq_fmt(_ptr(x), _dtype_code(x.dtype), B, S, H, D, fmt, _ptr(row_data), _ptr(col_data),
+                                    _ptr(scale), _stream(stream)), "mx_quantize_sq_fmt")
+
+
+def mx_quantize_sq_fmt_varlen(x, cu_seqlens, cu_scale_rows, nseq, total_tokens, total_scale_rows, H, D, fmt,
+                              row_data, col_data, scale, stream=None):
+    _check(lib().mx_quantize_sq_fmt_varlen(_ptr(x), _dtype_code(x.dtype), _ptr(cu_seqlens), _ptr(cu_scale_rows), nseq,
+                                           total_tokens, total_scale_rows, H, D, fmt, _ptr(row_data), _ptr(col_data),
+                                           _ptr(scale), _stream(stream)), "mx_quantize_sq_fmt_varlen")
+
+
+def quantize_sq_fmt(x, fmt):
+    """Square-block quantization of a [B, S, H, D] tensor in a small element format (E2M3, E3M2,
+    E2M1).  Returns (row-packed data [B, S, H, D w/8], column-packed data [B, ceil(S/32), H, D, 32 w/8],
+    scales [B, ceil(S/32), H, D/32])."""
+    B, S, H, D = x.shape
+    w, nb = ELEM_BITS[fmt], (S + 31) // 32
+    row = torch.empty((B, S, H, D * w // 8), dtype=torch.uint8, device=x.device)
+    col = torch.empty((B, nb, H, D, 32 * w // 8), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((B, nb, H, D // 32), dtype=torch.uint8, device=x.device)
+    mx_quantize_sq_fmt(x, B, S, H, D, fmt, row, col, scale)
+    return row, col, scale
+
+
+def quantize_sq_fmt_varlen(x, cu_seqlens, cu_scale_rows, seqlens, fmt):
+    """quantize_sq_fmt for a packed [T, H, D] tensor (jagged layout).  Returns (row-packed data
+    [T, H, D w/8], column-packed data [Tp/32, H, D, 32 w/8], scales [Tp/32, H, D/32])."""
+    T, H, D = x.shape
+    Tp = padded_scale_rows(seqlens)
+    w = ELEM_BITS[fmt]
+    row = torch.empty((T, H, D * w // 8), dtype=torch.uint8, device=x.device)
+    col = torch.empty((Tp // 32, H, D, 32 * w // 8), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((Tp // 32, H, D // 32), dtype=torch.uint8, device=x.device)
+    mx_quantize_sq_fmt_varlen(x, cu_seqlens, cu_scale_rows, len(seqlens), T, Tp, H, D, fmt, row, col, scale)
+    return row, col, scale
 
 
 def quantize_rows(x, fmt=E4M3):

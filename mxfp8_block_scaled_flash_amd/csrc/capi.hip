@@ -221,6 +221,39 @@ mx_status mx_quantize_rows_varlen(const void* x, mx_dtype x_dtype, const int32_t
                                                    total_scale_rows, H, K, (int)format, data, scale, stream));
 }
 
+static bool small_elem(int f) { return f == MX_E2M3 || f == MX_E3M2 || f == MX_E2M1; }
+
+mx_status mx_quantize_sq_fmt(const void* x, mx_dtype x_dtype, int B, int S, int H, int D, mx_elem format,
+                             uint8_t* row_data, uint8_t* col_data, uint8_t* scale, hipStream_t stream) {
+  if (B < 0 || S < 0 || H < 1 || H > kMaxHeads || (D != 64 && D != 128) || !small_elem(format)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  const long nrows = (long)B * ((S + 31) / 32);
+  if ((long)B * S * H * D > kMaxElems || nrows * 32 * H * D > kMaxElems || nrows * H > 2147483647L) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  if (!all_aligned({x, row_data, col_data}) || !scale) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_quantize_sq_fmt(x, x_dtype == MX_F32, nullptr, nullptr, B, S, nrows, H, D, (int)format,
+                                              row_data, col_data, scale, stream));
+}
+
+mx_status mx_quantize_sq_fmt_varlen(const void* x, mx_dtype x_dtype, const int32_t* cu_seqlens,
+                                    const int32_t* cu_scale_rows, int nseq, int total_tokens, int total_scale_rows,
+                                    int H, int D, mx_elem format, uint8_t* row_data, uint8_t* col_data,
+                                    uint8_t* scale, hipStream_t stream) {
+  if (nseq < 1 || total_tokens < 0 || total_scale_rows < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if (H < 1 || H > kMaxHeads || (D != 64 && D != 128) || !small_elem(format)) return MX_EINVAL;
+  if (x_dtype != MX_BF16 && x_dtype != MX_F32) return MX_EINVAL;
+  if ((long)total_scale_rows * H * D > kMaxElems || (long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_scale_rows < total_tokens || total_scale_rows % 128 != 0) return MX_EINVAL;
+  if ((long)(total_scale_rows / 32) * H > 2147483647L) return MX_EINVAL;
+  if (total_tokens == 0) return MX_OK;
+  if (!all_aligned({x, row_data, col_data}) || !scale) return MX_EINVAL;
+  if (mx_status st = check_device()) return st;
+  return from_hip(mxk::launch_quantize_sq_fmt(x, x_dtype == MX_F32, cu_seqlens, cu_scale_rows, nseq, 0,
+                                              (long)total_scale_rows / 32, H, D, (int)format, row_data, col_data,
+                                              scale, stream));
+}
+
 mx_status mx_gemm_quantize(const uint8_t* a_data, const uint8_t* a_scale, const uint8_t* b_data,
                            const uint8_t* b_scale, mx_elem ab_format, int M, int N, int K, unsigned layouts,
                            uint8_t* c_row32_data,

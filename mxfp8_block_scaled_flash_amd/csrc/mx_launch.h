@@ -75,5 +75,8 @@ hipError_t launch_quantize_rows_varlen(const void* x, bool fp32, const int32_t* 
                                        long total_scale_rows, int H, int K, int fmt, uint8_t* data, uint8_t* scale,
                                        hipStream_t st);
 hipError_t launch_gemm_quantize(GemmArgs a, hipStream_t st);
+hipError_t launch_quantize_sq_fmt(const void* x, bool fp32, const int32_t* cu, const int32_t* csr, int nseq, int S,
+                                  long nrows, int H, int D, int fmt, uint8_t* row_data, uint8_t* col_data,
+                                  uint8_t* scale, hipStream_t st);
 
 }  // namespace mxk

@@ -146,6 +146,117 @@ __global__ __launch_bounds__(256) void quantize_rows_varlen_kernel(const T* __re
   quantize_block<T, FMT>(x + src * 32, data + src * (4 * Fmt<FMT>::W), scale + b);
 }
 
+
+// Square [32 tokens x 32 features] blocks in a small element format (E2M3, E3M2, E2M1): the backward's
+// Q and K operands with MXFP6 / MXFP4 payloads (its square blocks: "Low Precision Flash Attention 4",
+// forward/backward paragraph; the formats: the same page's paragraph on the block-scaled MMA).  A
+// packed payload cannot be read across its rows the way a byte payload can, so each block is written
+// twice: row-packed (token rows along D, as mx_quantize_rows) and column-packed (for each feature, the
+// block's 32 tokens as one packed 32-element block), both from the same codes and one E8M0 scale.
+// One wave per block: lane l holds token row l / 2, features 16 (l % 2) .. +15; the column copy goes
+// through a 1 KB LDS transpose per wave.
+struct SqFmtArgs {
+  SeqMap seq;
+  int H, nseq;
+  long nrows;                     // padded 32-token block rows (fixed: B ceil(S/32); jagged: Tpad / 32)
+  uint8_t *row_data, *col_data, *scale;
+};
+
+template <int W>
+MX_DEV void pack16(const uint32_t (&c)[16], uint32_t (&o)[W / 2]) {
+#pragma unroll
+  for (int j = 0; j < W / 2; ++j) o[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int pos = W * i, wd = pos >> 5, bit = pos & 31;
+    o[wd] |= c[i] << bit;
+    if (bit + W > 32) o[wd + 1] |= c[i] >> (32 - bit);
+  }
+}
+
+template <typename T, int FMT, int D>
+__global__ __launch_bounds__(64 * D / 32) void quantize_sq_fmt_kernel(const T* __restrict__ x, SqFmtArgs a) {
+  using F = Fmt<FMT>;
+  constexpr int W = F::W, BB = 32 * W / 8, HB = BB / 2, KRB = D * W / 8;
+  __shared__ __attribute__((aligned(16))) uint8_t tc[D / 32][32][32];   // per wave: codes [feature][token]
+  const int lane = threadIdx.x & 63, fb = threadIdx.x >> 6;
+  const int h = (int)(blockIdx.x % a.H);
+  const long g = blockIdx.x / a.H;         // padded block row
+  int s, blk;
+  if (a.seq.cu) {  // padded block row -> sequence: the last s with csr[s] <= 32 g
+    const long row = g * 32;
+    int lo = 0, hi = a.nseq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long)a.seq.csr[mid] <= row) lo = mid; else hi = mid;
+    }
+    s = lo;
+    blk = (int)(g - (a.seq.csr[s] >> 5));
+  } else {
+    s = (int)(g / a.seq.nblk);
+    blk = (int)(g % a.seq.nblk);
+  }
+  int tok0, L, srow0, sblk0;
+  a.seq.get(s, tok0, L, srow0, sblk0);
+  const int r = lane >> 1, hf = lane & 1;
+  const int t = blk * 32 + r;
+  float v[16];
+  if (t < L) {
+    const T* src = x + ((long)(tok0 + t) * a.H + h) * D + fb * 32 + hf * 16;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 u = ((const uint4*)src)[c];
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * c + 2 * i] = bf16_lo(w4[i]);
+          v[8 * c + 2 * i + 1] = bf16_hi(w4[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 f = ((const float4*)src)[c];
+        v[4 * c] = f.x; v[4 * c + 1] = f.y; v[4 * c + 2] = f.z; v[4 * c + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max_nonneg(amax);
+  // E8M0 = clamp(floor(log2 amax) - EMAX + 127, 0, 254); zero and fp32-subnormal amax give 0
+  const int ea = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  const int k = ea == 0 ? 0 : min(max(ea - F::EMAX, 0), 254);
+  uint32_t c[16], o[W / 2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = encode<FMT>(ldexpf(v[i], 127 - k));
+  pack16<W>(c, o);
+  if (t < L) {
+    uint32_t* dst = (uint32_t*)(a.row_data + ((long)(tok0 + t) * a.H + h) * KRB + fb * BB + hf * HB);
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) dst[j] = o[j];
+  }
+  // column copy: token-major codes of each feature through LDS
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tc[fb][hf * 16 + i][r] = (uint8_t)c[i];
+  __syncthreads();
+  const int col = lane >> 1;
+  const uint4 u = *(const uint4*)&tc[fb][col][hf * 16];
+  const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = (w4[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+  pack16<W>(c, o);
+  uint32_t* cdst = (uint32_t*)(a.col_data + (((long)(sblk0 + blk) * a.H + h) * D + fb * 32 + col) * BB + hf * HB);
+#pragma unroll
+  for (int j = 0; j < W / 2; ++j) cdst[j] = o[j];
+  if (lane == 0) a.scale[((long)(sblk0 + blk) * a.H + h) * (D / 32) + fb] = (uint8_t)k;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int fmt, uint8_t* data, uint8_t* scale,
@@ -182,6 +293,35 @@ hipError_t launch_quantize_rows_varlen(const void* x, bool fp32, const int32_t* 
   }
   MX_QRV_CASE(0) MX_QRV_CASE(2) MX_QRV_CASE(3) MX_QRV_CASE(4)
 #undef MX_QRV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_sq_fmt(const void* x, bool fp32, const int32_t* cu, const int32_t* csr, int nseq, int S,
+                                  long nrows, int H, int D, int fmt, uint8_t* row_data, uint8_t* col_data,
+                                  uint8_t* scale, hipStream_t st) {
+  SqFmtArgs a{};
+  a.seq.cu = cu;
+  a.seq.csr = csr;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.H = H;
+  a.nseq = nseq;
+  a.nrows = nrows;
+  a.row_data = row_data;
+  a.col_data = col_data;
+  a.scale = scale;
+  const long nwg = nrows * H;
+  if (nwg == 0) return hipSuccess;
+  dim3 g((unsigned)nwg), b((unsigned)(64 * D / 32));
+#define MX_QSQ_CASE(F, DD)                                                                              \
+  if (fmt == F && D == DD) {                                                                            \
+    if (fp32) quantize_sq_fmt_kernel<float, F, DD><<<g, b, 0, st>>>((const float*)x, a);                \
+    else quantize_sq_fmt_kernel<uint16_t, F, DD><<<g, b, 0, st>>>((const uint16_t*)x, a);               \
+    return hipGetLastError();                                                                           \
+  }
+  MX_QSQ_CASE(2, 128) MX_QSQ_CASE(3, 128) MX_QSQ_CASE(4, 128) MX_QSQ_CASE(2, 64) MX_QSQ_CASE(3, 64)
+  MX_QSQ_CASE(4, 64)
+#undef MX_QSQ_CASE
   return hipErrorInvalidValue;
 }
 

@@ -300,3 +300,33 @@ def test_quantize_rows_varlen_validation():
                 dict(fmt=1), dict(dt=mx.F16), dict(H=0), dict(x=None), dict(d=24), dict(s=None)):
         assert call(**bad) == EINVAL, bad
     assert call(T=0) == 0
+
+
+def test_quantize_sq_fmt_validation():
+    L = mx.lib()
+    ok = dict(x=16, dt=mx.BF16, B=2, S=40, H=2, D=128, fmt=mx.E2M3, r=16, c=16, s=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mx_quantize_sq_fmt(a["x"], a["dt"], a["B"], a["S"], a["H"], a["D"], a["fmt"], a["r"], a["c"],
+                                    a["s"], None)
+    for bad in (dict(D=96), dict(D=32), dict(B=-1), dict(S=-1), dict(H=0), dict(fmt=mx.E4M3), dict(fmt=1),
+                dict(dt=mx.F16), dict(x=None), dict(r=None), dict(c=24), dict(s=None)):
+        assert call(**bad) == EINVAL, bad
+    assert call(B=0) == 0 and call(S=0) == 0
+
+
+def test_quantize_sq_fmt_varlen_validation():
+    L = mx.lib()
+    ok = dict(x=16, dt=mx.BF16, cu=16, csr=16, nseq=2, T=100, Tp=256, H=2, D=64, fmt=mx.E2M1, r=16, c=16, s=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mx_quantize_sq_fmt_varlen(a["x"], a["dt"], a["cu"], a["csr"], a["nseq"], a["T"], a["Tp"], a["H"],
+                                           a["D"], a["fmt"], a["r"], a["c"], a["s"], None)
+    for bad in (dict(cu=None), dict(csr=None), dict(nseq=0), dict(T=-1), dict(Tp=100), dict(Tp=64), dict(D=48),
+                dict(fmt=mx.E4M3), dict(dt=mx.F16), dict(H=0), dict(x=None), dict(r=24), dict(c=None), dict(s=None)):
+        assert call(**bad) == EINVAL, bad
+    assert call(T=0) == 0

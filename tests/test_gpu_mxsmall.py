@@ -144,3 +144,67 @@ def test_quantize_rows_varlen_places_scale_rows_at_the_padded_offsets(fmt, seqle
         assert np.array_equal(gd[a:b].reshape(rd.shape), rd), (FMTS[fmt], i)
         ref_s[po[i]:po[i] + (b - a)] = rs.reshape(b - a, H, D // 32)
     assert np.array_equal(gs, ref_s), FMTS[fmt]
+
+
+SMALL = [mx.E2M3, mx.E3M2, mx.E2M1]
+
+
+def _oracle_sq(xh, fmt):
+    """Row-packed bytes [L, D w/8], column-packed bytes [ceil(L/32), D, 32 w/8], scales of one head."""
+    name = FMTS[fmt]
+    c, k = ms.quantize_sq32(xh, name)
+    return ms.pack(c, name), ms.pack_sq32_columns(c, name), k
+
+
+@pytest.mark.parametrize("fmt", SMALL)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(2, 70, 3, 128), (1, 33, 2, 64)])
+def test_quantize_sq_fmt_matches_the_oracle_bit_for_bit(fmt, dtype, shape):
+    """mx_quantize_sq_fmt: square blocks in a small format, row-packed and column-packed payloads and
+    the scales equal to the oracle's, byte for byte (ragged tails, mixed magnitudes, zero blocks)."""
+    B, S, H, D = shape
+    x = _data(B * S * H, D, 60 + fmt).reshape(B, S, H, D)
+    x[0, 32:64, 0, :32] = 0.0                       # one all-zero square block
+    xt = torch.from_numpy(x).to(dtype)
+    x = xt.double().numpy()
+    row, col, sc = mx.quantize_sq_fmt(xt.cuda(), fmt)
+    torch.cuda.synchronize()
+    gr, gc, gs = to_np(row), to_np(col), to_np(sc)
+    for b in range(B):
+        for h in range(H):
+            rr, rc, rk = _oracle_sq(x[b, :, h, :], fmt)
+            assert np.array_equal(gr[b, :, h], rr), (FMTS[fmt], b, h, "row")
+            assert np.array_equal(gc[b, :, h], rc), (FMTS[fmt], b, h, "col")
+            assert np.array_equal(gs[b, :, h], rk), (FMTS[fmt], b, h, "scale")
+
+
+@pytest.mark.parametrize("fmt", SMALL)
+def test_quantize_sq_fmt_varlen_places_block_rows_at_the_padded_offsets(fmt):
+    """mx_quantize_sq_fmt_varlen: row-packed payload at the packed token positions; column-packed
+    blocks and scales at the 128-aligned per-sequence block rows; pad block rows all zero."""
+    seqlens = [5, 128, 0, 70, 200]
+    H, D = 2, 128
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    T = int(cu[-1])
+    x = _data(T * H, D, 80 + fmt).reshape(T, H, D)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    x = xt.double().numpy()
+    cu_d = torch.from_numpy(cu).cuda()
+    csr = torch.empty(len(seqlens) + 1, dtype=torch.int32, device="cuda")
+    mx.mx_varlen_scale_offsets(cu_d, len(seqlens), csr)
+    row, col, sc = mx.quantize_sq_fmt_varlen(xt.cuda(), cu_d, csr, seqlens, fmt)
+    torch.cuda.synchronize()
+    po = omx.padded_offsets(seqlens)
+    gr, gc, gs = to_np(row), to_np(col), to_np(sc)
+    ref_c, ref_s = np.zeros_like(gc), np.zeros_like(gs)
+    for i in range(len(seqlens)):
+        a, b = cu[i], cu[i + 1]
+        if a == b:
+            continue
+        nb = (b - a + 31) // 32
+        for h in range(H):
+            rr, rc, rk = _oracle_sq(x[a:b, h, :], fmt)
+            assert np.array_equal(gr[a:b, h], rr), (FMTS[fmt], i, h)
+            ref_c[po[i] // 32:po[i] // 32 + nb, h] = rc
+            ref_s[po[i] // 32:po[i] // 32 + nb, h] = rk
+    assert np.array_equal(gc, ref_c) and np.array_equal(gs, ref_s), FMTS[fmt]
