@@ -540,6 +540,54 @@ mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mx_attn_bwd_fmt -- mx_attn_bwd with Q and K in MXFP6 or MXFP4.
+ * Defines: mx_attn_bwd's computation ([News], forward/backward and contributions
+ * paragraphs) with the block-scaled MMA's other element formats ([News],
+ * paragraph on the block-scaled MMA: MXFP8, MXFP6, MXFP4), read as the OCP MX
+ * elements for Q and K only: their square [32, 32] blocks carry E2M3, E3M2 or
+ * E2M1 codes (mx_quantize_sq_fmt); dO and V stay MXFP8, and P and dS are
+ * quantized online in MXFP8 as in mx_attn_bwd.  Every product takes its
+ * operands through the matrix instruction's format fields.
+ *   q_row, k_row     [B, S, H, D*w/8] row-packed payloads (mx_quantize_sq_fmt)
+ *   q_col, k_col     [B, ceil(S/32), H, D, 32*w/8] column-packed payloads
+ *   q_scale, k_scale [B, ceil(S/32), H, D/32] square-block E8M0 scales
+ *   qk_format        MX_E2M3, MX_E3M2 or MX_E2M1 (D = 128), or MX_E4M3: then
+ *                    exactly mx_attn_bwd with q_row/k_row as the SQ32
+ *                    payloads (q_col, k_col unused, may be NULL)
+ *   everything else  as mx_attn_bwd
+ * Errors: as mx_attn_bwd, and MX_EINVAL for another format, D != 128 with a
+ * small format, or a null or misaligned column-packed payload.
+ */
+mx_status mx_attn_bwd_fmt(const uint8_t* q_row, const uint8_t* q_col, const uint8_t* q_scale,
+                          const uint8_t* k_row, const uint8_t* k_col, const uint8_t* k_scale,
+                          const uint8_t* v_data, const uint8_t* v_scale,
+                          const uint8_t* do_data, const uint8_t* do_scale,
+                          const void* o, const void* dout, mx_dtype io_dtype, const float* lse,
+                          int B, int S, int H, int D, float softmax_scale, int causal,
+                          int dq_scale_log2, mx_elem qk_format,
+                          void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_attn_bwd_fmt_varlen -- mx_attn_bwd_fmt over packed sequences ([News],
+ * contributions paragraph, jagged layout): q_row, k_row [T, H, D*w/8];
+ * q_col, k_col [Tpad/32, H, D, 32*w/8] and the scales [Tpad/32, H, D/32] at
+ * the 128-aligned per-sequence block rows (mx_quantize_sq_fmt_varlen); the
+ * rest as mx_attn_bwd_varlen.  Errors: as mx_attn_bwd_fmt and
+ * mx_attn_bwd_varlen.
+ */
+mx_status mx_attn_bwd_fmt_varlen(const uint8_t* q_row, const uint8_t* q_col, const uint8_t* q_scale,
+                                 const uint8_t* k_row, const uint8_t* k_col, const uint8_t* k_scale,
+                                 const uint8_t* v_data, const uint8_t* v_scale,
+                                 const uint8_t* do_data, const uint8_t* do_scale,
+                                 const void* o, const void* dout, mx_dtype io_dtype, const float* lse,
+                                 const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                                 int total_tokens, int max_seqlen, int H, int D,
+                                 float softmax_scale, int causal, int dq_scale_log2, mx_elem qk_format,
+                                 void* dq, void* dk, void* dv, mx_dtype grad_dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mx_attn_bwd_noalloc -- mx_attn_bwd for callers that cannot allocate device
  * memory or hand in a workspace: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation.  Same arguments, computation and

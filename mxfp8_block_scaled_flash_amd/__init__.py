@@ -60,6 +60,10 @@ _SIGS = {
                                 + [_c_int, _vp, _c_size, _vp], _c_int),
     "mx_attn_bwd": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
                     + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
+    "mx_attn_bwd_fmt": ([_vp] * 10 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int, _c_int]
+                        + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
+    "mx_attn_bwd_fmt_varlen": ([_vp] * 10 + [_vp, _vp, _c_int, _vp] + [_vp, _vp] + [_c_int] * 5
+                               + [_c_float, _c_int, _c_int, _c_int] + [_vp] * 3 + [_c_int, _vp, _c_size, _vp], _c_int),
     "mx_attn_bwd_noalloc": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_c_int] * 4 + [_c_float, _c_int, _c_int]
                             + [_vp] * 3 + [_c_int, _vp], _c_int),
     "mx_attn_bwd_varlen": ([_vp] * 8 + [_vp, _vp, _c_int, _vp] + [_vp, _vp] + [_c_int] * 5
@@ -532,6 +536,60 @@ def attn_bwd(q, k, v, do, o, dout, lse, softmax_scale, causal, dq_scale_log2, gr
     ws = torch.empty(mx_attn_bwd_workspace_bytes(B * S, H, D), dtype=torch.uint8, device=dev)
     mx_attn_bwd(q[0], q[1], k[0], k[1], v[0], v[1], do[0], do[1], o, dout, lse, B, S, H, D, softmax_scale, causal,
                 dq_scale_log2, dq, dk, dv, ws)
+    if with_overflow:
+        return dq, dk, dv, mx_attn_bwd_overflow(ws)
+    return dq, dk, dv
+
+
+def mx_attn_bwd_fmt(q_row, q_col, q_scale, k_row, k_col, k_scale, v_data, v_scale, do_data, do_scale, o, dout, lse,
+                    B, S, H, D, softmax_scale, causal, dq_scale_log2, qk_format, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd_fmt(_ptr(q_row), _ptr(q_col), _ptr(q_scale), _ptr(k_row), _ptr(k_col), _ptr(k_scale),
+                                 _ptr(v_data), _ptr(v_scale), _ptr(do_data), _ptr(do_scale), _ptr(o), _ptr(dout),
+                                 _dtype_code(o.dtype), _ptr(lse), B, S, H, D, float(softmax_scale), int(bool(causal)),
+                                 int(dq_scale_log2), int(qk_format), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq.dtype),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mx_attn_bwd_fmt")
+
+
+def mx_attn_bwd_fmt_varlen(q_row, q_col, q_scale, k_row, k_col, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                           lse, cu_seqlens, cu_scale_rows, nseq, total_tokens, max_seqlen, H, D, softmax_scale, causal,
+                           dq_scale_log2, qk_format, dq, dk, dv, workspace, stream=None):
+    _check(lib().mx_attn_bwd_fmt_varlen(_ptr(q_row), _ptr(q_col), _ptr(q_scale), _ptr(k_row), _ptr(k_col),
+                                        _ptr(k_scale), _ptr(v_data), _ptr(v_scale), _ptr(do_data), _ptr(do_scale),
+                                        _ptr(o), _ptr(dout), _dtype_code(o.dtype), _ptr(lse), _ptr(cu_seqlens),
+                                        _ptr(cu_scale_rows), nseq, total_tokens, max_seqlen, H, D,
+                                        float(softmax_scale), int(bool(causal)), int(dq_scale_log2), int(qk_format),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq.dtype), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mx_attn_bwd_fmt_varlen")
+
+
+def attn_bwd_fmt(q, k, v, do, o, dout, lse, softmax_scale, causal, dq_scale_log2, qk_format,
+                 grad_dtype=torch.bfloat16, with_overflow=False):
+    """q, k: (row-packed, column-packed, scales) from quantize_sq_fmt in element format qk_format;
+    v: (data, scale) ROW32; do: (data, scale) SQ32; o, dout: [B,S,H,D]; lse [B,H,S].
+    Returns (dQ, dK, dV), plus the fp16 range flag with with_overflow=True."""
+    B, S, H, D = o.shape
+    dev = o.device
+    dq, dk, dv = (torch.empty((B, S, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_workspace_bytes(B * S, H, D), dtype=torch.uint8, device=dev)
+    mx_attn_bwd_fmt(q[0], q[1], q[2], k[0], k[1], k[2], v[0], v[1], do[0], do[1], o, dout, lse, B, S, H, D,
+                    softmax_scale, causal, dq_scale_log2, qk_format, dq, dk, dv, ws)
+    if with_overflow:
+        return dq, dk, dv, mx_attn_bwd_overflow(ws)
+    return dq, dk, dv
+
+
+def attn_bwd_fmt_varlen(q, k, v, do, o, dout, lse, cu_seqlens, cu_scale_rows, seqlens, softmax_scale, causal,
+                        dq_scale_log2, qk_format, grad_dtype=torch.bfloat16, with_overflow=False):
+    """attn_bwd_fmt over packed sequences (q, k from quantize_sq_fmt_varlen)."""
+    T, H, D = o.shape
+    dev = o.device
+    dq, dk, dv = (torch.empty((T, H, D), dtype=grad_dtype, device=dev) for _ in range(3))
+    ws = torch.empty(mx_attn_bwd_workspace_bytes(T, H, D), dtype=torch.uint8, device=dev)
+    mx_attn_bwd_fmt_varlen(q[0], q[1], q[2], k[0], k[1], k[2], v[0], v[1], do[0], do[1], o, dout, lse, cu_seqlens,
+                           cu_scale_rows, len(seqlens), T, max(seqlens), H, D, softmax_scale, causal, dq_scale_log2,
+                           qk_format, dq, dk, dv, ws)
     if with_overflow:
         return dq, dk, dv, mx_attn_bwd_overflow(ws)
     return dq, dk, dv

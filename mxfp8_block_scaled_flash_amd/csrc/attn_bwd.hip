@@ -48,6 +48,25 @@ MX_DEV v8i pack8b(uint4 lo, uint4 hi) {
   return r;
 }
 
+// The same with element formats fa, fb for the two operands (0 E4M3, 2 E2M3, 3 E3M2, 4 E2M1).
+template <int FA, int FB, int OA, int OB>
+MX_DEV v16f mfma32f(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OA, sa, OB, sb);
+}
+
+// One 32-element block of a small-format operand: 24 (6-bit) or 16 (4-bit) packed bytes, as the
+// instruction reads them from the first dwords of the operand.
+template <int W>
+MX_DEV v8i small_operand(const uint8_t* p) {
+  if constexpr (W == 6) {
+    const uint2 x = ((const uint2*)p)[0], y = ((const uint2*)p)[1], z = ((const uint2*)p)[2];
+    return v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
+  } else {
+    const uint4 x = *(const uint4*)p;
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  }
+}
+
 MX_DEV v2i tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
@@ -59,6 +78,16 @@ MX_DEV v8i tr_operand(const uint8_t* base, int stride, int lane) {
   const int G = lane >> 4, i16 = lane & 15;
   const uint8_t* p = base + (16 * (G >> 1) + (i16 >> 1)) * stride + 16 * (G & 1) + 8 * (i16 & 1);
   v2i r0 = tr8(p), r1 = tr8(p + 8 * stride), r2 = tr8(p + 32 * stride), r3 = tr8(p + 40 * stride);
+  return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// tr_operand over an unpadded 64-byte-row tile whose 16-byte chunks sit XOR-swizzled by (row & 3);
+// chunk0 = the operand's first chunk (2 t for query block t).  Rows r, r+8, r+32, r+40 share r & 3.
+MX_DEV v8i tr_operand_swz64(const uint8_t* rows, int chunk0, int lane) {
+  const int G = lane >> 4, i16 = lane & 15;
+  const int r = 16 * (G >> 1) + (i16 >> 1);
+  const uint8_t* p = rows + r * 64 + 16 * ((chunk0 + (G & 1)) ^ (r & 3)) + 8 * (i16 & 1);
+  v2i r0 = tr8(p), r1 = tr8(p + 8 * 64), r2 = tr8(p + 32 * 64), r3 = tr8(p + 40 * 64);
   return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
@@ -163,8 +192,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // issue the next step's loads: a wave's waits on its own loads also wait on
 // the atomics it issued after them, so waves 4-7, whose atomics come last,
 // load nothing and reach the barrier without waiting on memory.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int QF>
 __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
+  // QF: element format of Q and K (0: MXFP8 E4M3; 2, 3: MXFP6 E2M3, E3M2; 4: MXFP4 E2M1).  In the small
+  // formats (D = 128 only) Q and K arrive row-packed (S = Q^ K^T) and column-packed (dK = dS^T Q^ and
+  // dQ = dS^ K^ contract over tokens), and the V and dS tiles drop their padding for XOR-swizzled
+  // chunks so the larger tiles fit in LDS.
+  constexpr bool SMALL = QF != 0;
+  constexpr int W = QF == 0 ? 8 : QF == 4 ? 4 : 6;   // bits per Q / K element
+  constexpr int BB = 32 * W / 8;                     // bytes of one packed 32-element block
+  constexpr int KRB = D * W / 8;                     // bytes of one packed Q / K row
+  static_assert(!SMALL || D == 128, "small-format Q, K for D = 128 only");
   constexpr int NW = 8;
   constexpr int BN = 32 * NW;   // keys per workgroup
   constexpr int BQ = 64;        // queries per step
@@ -177,13 +215,22 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int SLQ = KST / 16;                 // 16-byte slots per padded Q / dO row
   constexpr int NBQ = BQ * KST / 1024;          // 1 KB DMA blocks per tile (one wave instruction each)
   static_assert(BQ * KST % 1024 == 0, "tiles must be whole DMA blocks");
-  __shared__ __attribute__((aligned(16))) uint8_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * KST];
+  constexpr int VST = SMALL ? D : KST;          // V row stride (small formats: chunk j of row r in slot j ^ (r & 7))
+  constexpr int DST = SMALL ? BQ : SST;         // dS row stride (small formats: chunk j in slot j ^ (r & 3))
+  constexpr int KROW = SMALL ? BN * KRB : BN * KST;   // row-major K tile bytes
+  constexpr int KCOL = SMALL ? (BN / 32) * D * BB : 0;   // column-packed K: [key block][feature][BB]
+  constexpr int QROW = SMALL ? BQ * KRB : BQ * KST;   // row-major Q step tile bytes
+  constexpr int QCOL = SMALL ? 2 * D * BB : 0;        // column-packed Q: [query block][feature][BB]
+  constexpr int NBQR = QROW / 1024, NBQC = QCOL / 1024;   // DMA blocks of the Q tiles
+  constexpr int NBT = NBQR + NBQC + NBQ;                  // DMA blocks per step (Q, then dO)
+  static_assert(QROW % 1024 == 0 && QCOL % 1024 == 0 && (D * BB) % 1024 == 0, "tiles must be whole DMA blocks");
+  __shared__ __attribute__((aligned(16))) uint8_t sK[KROW + KCOL];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * VST];
   // Q^ and dO^ step tiles arrive by 16-byte DMA (buffer loads straight into LDS): a padded row
   // is KST / 16 slots, the last one a copy of the row's last chunk (never read)
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][BQ * KST];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][QROW + QCOL];
   __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * SST];   // [step parity]
+  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * DST];   // [step parity]
   __shared__ uint32_t sKs[NW];                 // K SQ32 scale word (bytes = feature blocks) per key block
   __shared__ uint32_t sVs[BN];                 // V ROW32 scale word per key
   __shared__ uint32_t sQs[2][2], sDOs[2][2];   // [buffer][query block]
@@ -212,16 +259,39 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int kj = kw0 + n;             // this lane's key
 
   // ---- K and V tiles (zero past the end) and their scales
-  for (int ch = tid; ch < BN * D / 16; ch += NT) {
-    const int r = ch / (D / 16), cx = ch % (D / 16);
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (kbase + r < L) {
-      const long off = (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16;
-      kv = *(const uint4*)(a.k + off);
-      vv = *(const uint4*)(a.v + off);
+  if constexpr (!SMALL) {
+    for (int ch = tid; ch < BN * D / 16; ch += NT) {
+      const int r = ch / (D / 16), cx = ch % (D / 16);
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (kbase + r < L) {
+        const long off = (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16;
+        kv = *(const uint4*)(a.k + off);
+        vv = *(const uint4*)(a.v + off);
+      }
+      *(uint4*)(sK + r * KST + cx * 16) = kv;
+      *(uint4*)(sV + r * KST + cx * 16) = vv;
     }
-    *(uint4*)(sK + r * KST + cx * 16) = kv;
-    *(uint4*)(sV + r * KST + cx * 16) = vv;
+  } else {
+    for (int ch = tid; ch < BN * D / 16; ch += NT) {   // V: swizzled, unpadded
+      const int r = ch / (D / 16), cx = ch % (D / 16);
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (kbase + r < L) vv = *(const uint4*)(a.v + (long)(tok0 + kbase + r) * rowH + (long)h * D + cx * 16);
+      *(uint4*)(sV + r * VST + 16 * (cx ^ (r & 7))) = vv;
+    }
+    const long rowHk = (long)a.H * KRB;
+    for (int ch = tid; ch < KROW / 16; ch += NT) {     // K rows, packed
+      const int r = ch / (KRB / 16), cx = ch % (KRB / 16);
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (kbase + r < L) kv = *(const uint4*)(a.k + (long)(tok0 + kbase + r) * rowHk + (long)h * KRB + cx * 16);
+      *(uint4*)(sK + r * KRB + cx * 16) = kv;
+    }
+    for (int ch = tid; ch < KCOL / 16; ch += NT) {     // K columns, packed per key block
+      const int kb = ch / (D * BB / 16), cx = ch % (D * BB / 16);
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (kbase + 32 * kb < L)
+        kv = *(const uint4*)(a.kc + ((long)(sblk0 + kbase / 32 + kb) * a.H + h) * (D * BB) + cx * 16);
+      *(uint4*)(sK + KROW + kb * (D * BB) + cx * 16) = kv;
+    }
   }
   if (tid < NW) {
     uint32_t wk = 0;
@@ -248,18 +318,56 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
     const int rows = min(BQ, L - q0);   // >= 1
     const long tb = (long)(tok0 + q0) * rowH + (long)h * D;
     const int nrec = (rows - 1) * (int)rowH + D;
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + tb, nrec), rdo = buffer_rsrc(a.dob + tb, nrec);
+    const __amdgpu_buffer_rsrc_t rdo = buffer_rsrc(a.dob + tb, nrec);
+    if constexpr (!SMALL) {
+      const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + tb, nrec);
 #pragma unroll
-    for (int j = 0; j < (2 * NBQ + DW - 1) / DW; ++j) {
-      const int blk = w + DW * j;               // Q blocks first, then dO
-      if (w < DW && (2 * NBQ % DW == 0 || blk < 2 * NBQ)) {
-        const bool isq = blk < NBQ;
-        const int b = isq ? blk : blk - NBQ;
-        const int ch = b * 64 + lane, r = ch / SLQ;
-        const int off = r * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
-        uint8_t* dst = (isq ? sQ[buf] : sDO[buf]) + 1024 * b;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isq ? rq : rdo, (__attribute__((address_space(3))) void*)dst, 16,
-                                                 off, 0, 0, 0);
+      for (int j = 0; j < (2 * NBQ + DW - 1) / DW; ++j) {
+        const int blk = w + DW * j;               // Q blocks first, then dO
+        if (w < DW && (2 * NBQ % DW == 0 || blk < 2 * NBQ)) {
+          const bool isq = blk < NBQ;
+          const int b = isq ? blk : blk - NBQ;
+          const int ch = b * 64 + lane, r = ch / SLQ;
+          const int off = r * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+          uint8_t* dst = (isq ? sQ[buf] : sDO[buf]) + 1024 * b;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isq ? rq : rdo, (__attribute__((address_space(3))) void*)dst, 16,
+                                                   off, 0, 0, 0);
+        }
+      }
+    } else {
+      // packed Q rows (rows contiguous in LDS), then the column-packed blocks of the step's two query
+      // blocks (each D BB contiguous bytes), then dO as above
+      const long rowHq = (long)a.H * KRB;
+      const __amdgpu_buffer_rsrc_t rq =
+          buffer_rsrc(a.q + (long)(tok0 + q0) * rowHq + (long)h * KRB, (rows - 1) * (int)rowHq + KRB);
+      const int nqb = (rows + 31) / 32;
+      const __amdgpu_buffer_rsrc_t rqc = buffer_rsrc(a.qc + ((long)(sblk0 + q0 / 32) * a.H + h) * (D * BB),
+                                                     (nqb - 1) * a.H * (D * BB) + D * BB);
+#pragma unroll
+      for (int j = 0; j < (NBT + DW - 1) / DW; ++j) {
+        const int blk = w + DW * j;
+        if (w < DW && (NBT % DW == 0 || blk < NBT)) {
+          __amdgpu_buffer_rsrc_t r = rdo;
+          int off;
+          uint8_t* dst;
+          if (blk < NBQR) {
+            const int p = 16 * (blk * 64 + lane);
+            r = rq;
+            off = (p / KRB) * (int)rowHq + p % KRB;
+            dst = sQ[buf] + 1024 * blk;
+          } else if (blk < NBQR + NBQC) {
+            const int bb = blk - NBQR, t = bb / (D * BB / 1024);
+            r = rqc;
+            off = t * a.H * (D * BB) + (bb % (D * BB / 1024)) * 1024 + 16 * lane;
+            dst = sQ[buf] + QROW + 1024 * bb;
+          } else {
+            const int b = blk - NBQR - NBQC;
+            const int ch = b * 64 + lane, rr = ch / SLQ;
+            off = rr * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+            dst = sDO[buf] + 1024 * b;
+          }
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+        }
       }
     }
     // LSE and D by wave 0, the scales by wave 1: the waves that store them
@@ -328,11 +436,17 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         for (int kk = 0; kk < BN / 64; ++kk) {
           sscale[kk] = sDSs[bufc][t][2 * kk + g];
           kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-          sbv[kk] = tr_operand(sDS[bufc] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-          kav[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);         // columns: features
+          if constexpr (!SMALL) {
+            sbv[kk] = tr_operand(sDS[bufc] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
+            kav[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);         // columns: features
+          } else {
+            sbv[kk] = tr_operand_swz64(sDS[bufc] + (64 * kk) * DST, 2 * t, lane);
+            // column-packed K: key block 2 kk + g of feature 32 dc + n
+            kav[kk] = small_operand<W>(sK + KROW + ((2 * kk + g) * D + 32 * dc + n) * BB);
+          }
         }
 #pragma unroll
-        for (int kk = 0; kk < BN / 64; ++kk) acc = mfma32b<0, 0>(sbv[kk], kav[kk], acc, sscale[kk], kscale[kk]);
+        for (int kk = 0; kk < BN / 64; ++kk) acc = mfma32f<0, QF, 0, 0>(sbv[kk], kav[kk], acc, sscale[kk], kscale[kk]);
         keep(acc[0]);
 #pragma unroll
         for (int kk = 0; kk < BN / 64; ++kk) {
@@ -392,6 +506,10 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       if (live) {
         const uint8_t* kr = sK + (32 * w + n) * KST + 16 * g;
         const uint8_t* vr = sV + (32 * w + n) * KST + 16 * g;
+        // small formats: packed K row of this lane's key (block 2 c + g at (2 c + g) BB); swizzled V row
+        const uint8_t* krs = sK + (32 * w + n) * KRB + g * BB;
+        const uint8_t* vrs = sV + (32 * w + n) * VST;
+        auto vchunk = [&](int j) __attribute__((always_inline)) { return *(const uint4*)(vrs + 16 * (j ^ (n & 7))); };
         const uint32_t ksc = sKs[w] >> (8 * g), vsc = sVs[32 * w + n] >> (8 * g);
   #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -406,15 +524,27 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           // finite); the mask zeroes p and dS where nothing is visible
           const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
           const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
-          v16f st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
-                                  pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), v16f{}, qsa, ksc);
-          v16f dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
-                                   pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), v16f{}, dsa, vsc);
-          if constexpr (NC > 1) {
-            st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
-                               pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
+          v16f st, dpt;
+          if constexpr (!SMALL) {
+            st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
+                               pack8b(*(const uint4*)kr, *(const uint4*)(kr + 32)), v16f{}, qsa, ksc);
+            dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)),
+                                pack8b(*(const uint4*)vr, *(const uint4*)(vr + 32)), v16f{}, dsa, vsc);
+            if constexpr (NC > 1) {
+              st = mfma32b<2, 2>(pack8b(*(const uint4*)(qp + 64), *(const uint4*)(qp + 96)),
+                                 pack8b(*(const uint4*)(kr + 64), *(const uint4*)(kr + 96)), st, qsa, ksc);
+              dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
+                                  pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
+            }
+          } else {
+            // S from the packed rows (lane half g: 32-element block 2 c + g); dP as above with V swizzled
+            const uint8_t* qps = sQb + (32 * t + n) * KRB + g * BB;
+            st = mfma32f<QF, QF, 0, 0>(small_operand<W>(qps), small_operand<W>(krs), v16f{}, qsa, ksc);
+            dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), pack8b(vchunk(g), vchunk(2 + g)),
+                                v16f{}, dsa, vsc);
+            st = mfma32f<QF, QF, 2, 2>(small_operand<W>(qps + 2 * BB), small_operand<W>(krs + 2 * BB), st, qsa, ksc);
             dpt = mfma32b<2, 2>(pack8b(*(const uint4*)(op + 64), *(const uint4*)(op + 96)),
-                                pack8b(*(const uint4*)(vr + 64), *(const uint4*)(vr + 96)), dpt, dsa, vsc);
+                                pack8b(vchunk(4 + g), vchunk(6 + g)), dpt, dsa, vsc);
           }
           // ---- p = 2^(S c - LSE log2 e) (0 where masked), dS = p (dP - D); two copies of the
           // pass: with the mask (diagonal, edge or empty blocks) and without.  LSE and D are read
@@ -475,7 +605,11 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
           pB[4 * t + 0] = a02[0]; pB[4 * t + 1] = a02[1]; pB[4 * t + 2] = a13[0]; pB[4 * t + 3] = a13[1];
           sB[4 * t + 0] = b02[0]; sB[4 * t + 1] = b02[1]; sB[4 * t + 2] = b13[0]; sB[4 * t + 3] = b13[1];
-          *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+          if constexpr (!SMALL)
+            *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+          else
+            *(uint4*)(sDS[buf] + (32 * w + n) * DST + 16 * ((2 * t + g) ^ (n & 3))) =
+                make_uint4(b02[0], b02[1], b13[0], b13[1]);
           if (lane == 0) sDSs[buf][t][w] = ks2;
           kpc[t] = kp;
           ksc2[t] = ks2;
@@ -488,21 +622,31 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
           const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
-          const v8i qa = tr_operand(sQb + 32 * dc, KST, lane);
-          if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32b<0, 0>(qa, sB, dkt[0], qw, sscale); }
-          if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32b<1, 0>(qa, sB, dkt[1], qw, sscale); }
+          // Q^T: the 64 queries of feature 32 dc + n; small formats from the column-packed blocks
+          // (lane half g: query block g)
+          const v8i qa = SMALL ? small_operand<W>(sQb + QROW + (g * D + 32 * dc + n) * BB)
+                               : tr_operand(sQb + 32 * dc, KST, lane);
+          if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32f<QF, 0, 0, 0>(qa, sB, dkt[0], qw, sscale); }
+          if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32f<QF, 0, 1, 0>(qa, sB, dkt[1], qw, sscale); }
           if constexpr (ND > 2) {
-            if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pB, dvt[2], dow, pscale); dkt[2] = mfma32b<2, 0>(qa, sB, dkt[2], qw, sscale); }
-            if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pB, dvt[3], dow, pscale); dkt[3] = mfma32b<3, 0>(qa, sB, dkt[3], qw, sscale); }
+            if (dc == 2) { dvt[2] = mfma32b<2, 0>(oa, pB, dvt[2], dow, pscale); dkt[2] = mfma32f<QF, 0, 2, 0>(qa, sB, dkt[2], qw, sscale); }
+            if (dc == 3) { dvt[3] = mfma32b<3, 0>(oa, pB, dvt[3], dow, pscale); dkt[3] = mfma32f<QF, 0, 3, 0>(qa, sB, dkt[3], qw, sscale); }
           }
         }
         dow_prev = dow; qw_prev = qw; psc_prev = pscale; ssc_prev = sscale;
       } else {
         // every key of the block comes after every query of the step: dS is zero
         const uint4 z = make_uint4(0, 0, 0, 0);
-        uint8_t* rowp = sDS[buf] + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
-        *(uint4*)rowp = z;
-        *(uint4*)(rowp + 16) = z;
+        if constexpr (!SMALL) {
+          uint8_t* rowp = sDS[buf] + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
+          *(uint4*)rowp = z;
+          *(uint4*)(rowp + 16) = z;
+        } else {
+          const int rr = 32 * w + (lane >> 1);
+          uint8_t* rowp = sDS[buf] + rr * DST;
+          *(uint4*)(rowp + 16 * ((2 * (lane & 1)) ^ (rr & 3))) = z;
+          *(uint4*)(rowp + 16 * ((2 * (lane & 1) + 1) ^ (rr & 3))) = z;
+        }
         if (lane == 0) {
           sDSs[buf][0][w] = 1;
           sDSs[buf][1][w] = 1;
@@ -586,10 +730,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n8) {
   }
 }
 
-template __global__ void attn_bwd_kernel<64, true>(BwdArgs);
-template __global__ void attn_bwd_kernel<64, false>(BwdArgs);
-template __global__ void attn_bwd_kernel<128, true>(BwdArgs);
-template __global__ void attn_bwd_kernel<128, false>(BwdArgs);
+template __global__ void attn_bwd_kernel<64, true, 0>(BwdArgs);
+template __global__ void attn_bwd_kernel<64, false, 0>(BwdArgs);
+template __global__ void attn_bwd_kernel<128, true, 0>(BwdArgs);
+template __global__ void attn_bwd_kernel<128, false, 0>(BwdArgs);
 
 hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st) {
   const long rows = (long)a.T * a.H;
@@ -605,7 +749,8 @@ hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st) {
+hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st, int qk_fmt) {
+  if (qk_fmt != 0 && D != 128) return hipErrorInvalidValue;
   const long rows = (long)a.T * a.H;
   if (rows == 0) return hipSuccess;
   // 1. D_i and zeroed accumulator
@@ -620,10 +765,20 @@ hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_l
     const long units = (long)a.nseq * a.H;
     const long grid = ((units + 7) / 8) * 8 * a.nkt;
     dim3 g((unsigned)grid), b(512);
-    if (D == 64 && causal) attn_bwd_kernel<64, true><<<g, b, 0, st>>>(a);
-    else if (D == 64) attn_bwd_kernel<64, false><<<g, b, 0, st>>>(a);
-    else if (causal) attn_bwd_kernel<128, true><<<g, b, 0, st>>>(a);
-    else attn_bwd_kernel<128, false><<<g, b, 0, st>>>(a);
+    if (qk_fmt == 0) {
+      if (D == 64 && causal) attn_bwd_kernel<64, true, 0><<<g, b, 0, st>>>(a);
+      else if (D == 64) attn_bwd_kernel<64, false, 0><<<g, b, 0, st>>>(a);
+      else if (causal) attn_bwd_kernel<128, true, 0><<<g, b, 0, st>>>(a);
+      else attn_bwd_kernel<128, false, 0><<<g, b, 0, st>>>(a);
+    } else {
+#define MX_BWDF_CASE(F)                                                   \
+  if (qk_fmt == F) {                                                      \
+    if (causal) attn_bwd_kernel<128, true, F><<<g, b, 0, st>>>(a);        \
+    else attn_bwd_kernel<128, false, F><<<g, b, 0, st>>>(a);              \
+  } else
+      MX_BWDF_CASE(2) MX_BWDF_CASE(3) MX_BWDF_CASE(4) return hipErrorInvalidValue;
+#undef MX_BWDF_CASE
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -597,6 +597,72 @@ mx_status mx_attn_bwd_varlen(const uint8_t* q_data, const uint8_t* q_scale, cons
   return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, max_seqlen, stream));
 }
 
+mx_status mx_attn_bwd_fmt(const uint8_t* q_row, const uint8_t* q_col, const uint8_t* q_scale, const uint8_t* k_row,
+                          const uint8_t* k_col, const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                          const uint8_t* do_data, const uint8_t* do_scale, const void* o, const void* dout,
+                          mx_dtype io_dtype, const float* lse, int B, int S, int H, int D, float softmax_scale,
+                          int causal, int dq_scale_log2, mx_elem qk_format, void* dq, void* dk, void* dv,
+                          mx_dtype grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (qk_format == MX_E4M3)
+    return mx_attn_bwd(q_row, q_scale, k_row, k_scale, v_data, v_scale, do_data, do_scale, o, dout, io_dtype, lse, B,
+                       S, H, D, softmax_scale, causal, dq_scale_log2, dq, dk, dv, grad_dtype, workspace,
+                       workspace_bytes, stream);
+  if (!small_elem(qk_format) || D != 128) return MX_EINVAL;
+  if (B < 0 || S < 0) return MX_EINVAL;
+  if ((long)B * S * H * D > kMaxElems || (long)B * S > kMaxTokens) return MX_EINVAL;
+  if ((long)B * S == 0) return MX_OK;
+  if (!all_aligned({q_col, k_col})) return MX_EINVAL;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_common(q_row, q_scale, k_row, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                                io_dtype, lse, H, D, softmax_scale, dq_scale_log2, dq, dk, dv, grad_dtype, workspace,
+                                workspace_bytes, B * S, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.qc = q_col;
+  a.kc = k_col;
+  a.seq.cu = nullptr;
+  a.seq.csr = nullptr;
+  a.seq.S = S;
+  a.seq.nblk = (S + 31) / 32;
+  a.nseq = B;
+  a.T = B * S;
+  return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, S, stream, (int)qk_format));
+}
+
+mx_status mx_attn_bwd_fmt_varlen(const uint8_t* q_row, const uint8_t* q_col, const uint8_t* q_scale,
+                                 const uint8_t* k_row, const uint8_t* k_col, const uint8_t* k_scale,
+                                 const uint8_t* v_data, const uint8_t* v_scale, const uint8_t* do_data,
+                                 const uint8_t* do_scale, const void* o, const void* dout, mx_dtype io_dtype,
+                                 const float* lse, const int32_t* cu_seqlens, const int32_t* cu_scale_rows, int nseq,
+                                 int total_tokens, int max_seqlen, int H, int D, float softmax_scale, int causal,
+                                 int dq_scale_log2, mx_elem qk_format, void* dq, void* dk, void* dv,
+                                 mx_dtype grad_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (qk_format == MX_E4M3)
+    return mx_attn_bwd_varlen(q_row, q_scale, k_row, k_scale, v_data, v_scale, do_data, do_scale, o, dout, io_dtype,
+                              lse, cu_seqlens, cu_scale_rows, nseq, total_tokens, max_seqlen, H, D, softmax_scale,
+                              causal, dq_scale_log2, dq, dk, dv, grad_dtype, workspace, workspace_bytes, stream);
+  if (!small_elem(qk_format) || D != 128) return MX_EINVAL;
+  if (nseq < 1 || total_tokens < 0 || max_seqlen < 0 || !cu_seqlens || !cu_scale_rows) return MX_EINVAL;
+  if ((long)total_tokens * H * D > kMaxElems) return MX_EINVAL;
+  if (total_tokens == 0 || max_seqlen == 0) return MX_OK;
+  if (!all_aligned({q_col, k_col})) return MX_EINVAL;
+  mxk::BwdArgs a{};
+  if (mx_status st = bwd_common(q_row, q_scale, k_row, k_scale, v_data, v_scale, do_data, do_scale, o, dout,
+                                io_dtype, lse, H, D, softmax_scale, dq_scale_log2, dq, dk, dv, grad_dtype, workspace,
+                                workspace_bytes, total_tokens, a))
+    return st;
+  if (mx_status st = check_device()) return st;
+  a.qc = q_col;
+  a.kc = k_col;
+  a.seq.cu = cu_seqlens;
+  a.seq.csr = cu_scale_rows;
+  a.seq.S = 0;
+  a.seq.nblk = 0;
+  a.nseq = nseq;
+  a.T = total_tokens;
+  return from_hip(mxk::launch_attn_bwd(D, causal != 0, io_dtype == MX_F32, a, max_seqlen, stream, (int)qk_format));
+}
+
 // ---------------------------------------------------------------- no-allocation backward
 // The backward's scratch (range flag, fp16 dQ accumulator, D_i) for callers that cannot allocate:
 // one file-scope device array, so each GPU the library runs on holds its own copy until the

@@ -42,6 +42,7 @@ struct GemmArgs {
 
 struct BwdArgs {
   const uint8_t *q, *qs, *k, *ks, *v, *vs, *dob, *dos;   // SQ32 Q, K, dO; ROW32 V
+  const uint8_t *qc, *kc;   // small-format Q, K: column-packed copies [block row][H][D][32 w / 8]
   const void* o;        // forward output [tokens, H, D]
   const void* dout;     // incoming gradient [tokens, H, D]
   const float* lse;     // [B, H, S] or [H, T]
@@ -66,7 +67,7 @@ hipError_t launch_quantize(const void* x, bool fp32, int D, bool rmsnorm, const 
 hipError_t launch_scale_offsets(const int32_t* cu, int nseq, int32_t* csr, hipStream_t st);
 hipError_t launch_attn_fwd(int D, bool causal, bool out_bf16, int qk_fmt, FwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_attn_fwd_bf16(int D, bool causal, bool out_bf16, FwdArgs a, int max_len, hipStream_t st);
-hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st);
+hipError_t launch_attn_bwd(int D, bool causal, bool io_f32, BwdArgs a, int max_len, hipStream_t st, int qk_fmt = 0);
 hipError_t launch_bwd_pre(int D, bool io_f32, const BwdArgs& a, hipStream_t st);
 hipError_t launch_attn_bwd_bf16(int D, bool causal, BwdArgs a, int max_len, hipStream_t st);
 hipError_t launch_quantize_rows(const void* x, bool fp32, long rows, int K, int fmt, uint8_t* data, uint8_t* scale,

@@ -330,3 +330,23 @@ def test_quantize_sq_fmt_varlen_validation():
                 dict(fmt=mx.E4M3), dict(dt=mx.F16), dict(H=0), dict(x=None), dict(r=24), dict(c=None), dict(s=None)):
         assert call(**bad) == EINVAL, bad
     assert call(T=0) == 0
+
+
+def test_attn_bwd_fmt_validation():
+    """The small-format backward rejects what it cannot take before touching the device: a format
+    outside E4M3 / E2M3 / E3M2 / E2M1, D != 128 with a small format, null column-packed payloads."""
+    L = mx.lib()
+    ws = 1 << 20
+
+    def call(fmt=mx.E2M1, D=128, qc=16, kc=16, B=1, S=64):
+        return L.mx_attn_bwd_fmt(16, qc, 16, 16, kc, 16, 16, 16, 16, 16, 16, 16, mx.BF16, 16, B, S, 2, D, 0.125, 1, 8,
+                                 fmt, 16, 16, 16, mx.BF16, 16, ws, None)
+    for bad in (dict(fmt=1), dict(fmt=5), dict(D=64), dict(qc=None), dict(kc=None), dict(qc=24), dict(B=-1)):
+        assert call(**bad) == EINVAL, bad
+    assert call(B=0) == 0 and call(S=0) == 0
+
+    def callv(fmt=mx.E2M3, D=128, nseq=2, cu=16):
+        return L.mx_attn_bwd_fmt_varlen(16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, mx.BF16, 16, cu, 16, nseq,
+                                        100, 64, 2, D, 0.125, 1, 8, fmt, 16, 16, 16, mx.BF16, 16, ws, None)
+    for bad in (dict(fmt=7), dict(D=64), dict(nseq=0), dict(cu=None)):
+        assert callv(**bad) == EINVAL, bad
