@@ -334,6 +334,30 @@ def main():
         del qf, kf
     del of
 
+    # the backward with Q and K in MXFP6 / MXFP4 (square blocks; dO, V, P, dS MXFP8) on the same
+    # inputs and the step's O and LSE, timed alone
+    bwd_fmt = {}
+    if do_bwd:
+        for name, fmt in (("mxfp6_e2m3", mx.E2M3), ("mxfp4_e2m1", mx.E2M1)):
+            qf, kf = mx.quantize_sq_fmt(x["q"], fmt), mx.quantize_sq_fmt(x["k"], fmt)
+
+            def bwd_f(qf=qf, kf=kf, fmt=fmt):
+                mx.mx_attn_bwd_fmt(qf[0], qf[1], qf[2], kf[0], kf[1], kf[2], qz["v"][ROW][0], qz["v"][ROW][1],
+                                   qz["do"][SQ][0], qz["do"][SQ][1], o, x["do"], lse, B, S, H, D, sigma, True, 8, fmt,
+                                   dq, dk, dv, ws)
+
+            bwd_f()
+            r0, r1 = ev(), ev()
+            r0.record(stream)
+            for _ in range(3):
+                bwd_f()
+            r1.record(stream)
+            torch.cuda.synchronize()
+            ms_ = r0.elapsed_time(r1) / 3
+            bwd_fmt[name] = {"ms": round(ms_, 4),
+                             "tflops": round(10.0 * D * B * H * S * (S + 1) / 2 / (ms_ * 1e-3) / 1e12, 2)}
+            del qf, kf
+
     # BF16 attention forward on the same inputs (the baseline of the MX speed-up), timed alone
     o16 = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
 
@@ -414,6 +438,7 @@ def main():
                           "tflops": round(g_tflops, 2), "pct_peak": round(100 * g_tflops / MXFP8_PEAK_TFLOPS, 2),
                           **g_fmt},
         "fwd_qk_formats": fwd_fmt,
+        "bwd_qk_formats": bwd_fmt,
         "bf16_fwd": {"ms": round(f16_ms, 4), "tflops": round(f_flop / (f16_ms * 1e-3) / 1e12, 2),
                      "pct_bf16_peak": round(100 * f_flop / (f16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
                      "mx_speedup": round(f16_ms / f_ms, 3)},

@@ -115,3 +115,52 @@ def test_backward_fmt_e4m3_is_the_mxfp8_backward():
     torch.cuda.synchronize()
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
     assert torch.allclose(a[0], b[0], rtol=2e-3, atol=1e-6 * float(a[0].abs().max()))
+
+
+@pytest.mark.timeout(600)
+def test_backward_fmt_llm_shape_sampled_blocks():
+    """MXFP4 (E2M1) Q and K at the metric shape (B8 H32 S8192 D128, causal): two seeded (batch, head)
+    pairs carry O and LSE from the oracle forward (Q, K in the same format); the other heads an inert
+    filler (O = 0, LSE = 30).  dQ of sampled query blocks and dK, dV of sampled key blocks against the
+    oracle's block-subset gradients and admissible intervals."""
+    import synth
+
+    w = synth.workload("llm")
+    B, S, H, D = w.B, w.S, w.H, w.D
+    sigma = 1 / math.sqrt(D)
+    pairs = synth.draw_sample_pairs(w.seed, B, H, 2)
+    log(f"bwd e2m1 llm {w.shape()} heads {pairs}")
+    o = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, S), 30.0, device="cuda")
+    heads = {}
+    for b, h in pairs:
+        qn, kn, vn, dn = (synth.head_slice_np(w, t, b, h).double().numpy() for t in ("q", "k", "v", "do"))
+        on = np.zeros((S, D))
+        ln = np.zeros(S)
+        for r0 in range(0, S, 1024):       # the oracle forward in row chunks (every step is row-wise)
+            rows = np.arange(r0, min(S, r0 + 1024))
+            f = at.forward_head(qn, kn, vn, sigma, True, q_rows=rows, qk_fmt="e2m1")
+            on[rows], ln[rows] = at.bf16(f["O"]), at.fl32(f["LSE"])
+        o[b, :, h, :] = torch.from_numpy(on.astype(np.float32)).to(torch.bfloat16).cuda()
+        lse[b, h, :] = torch.from_numpy(ln.astype(np.float32)).cuda()
+        heads[(b, h)] = (qn, kn, vn, on, dn, ln)
+    x = {t: synth.tensor_torch(w, t, "cuda") for t in ("q", "k", "v", "do")}
+    qf, kf = mx.quantize_sq_fmt(x["q"], mx.E2M1), mx.quantize_sq_fmt(x["k"], mx.E2M1)
+    vr = mx.quantize(x["v"], mx.ROW32)[mx.ROW32]
+    dos = mx.quantize(x["do"], mx.SQ32)[mx.SQ32]
+    dq, dk, dv = mx.attn_bwd_fmt(qf, kf, vr, dos, o, x["do"], lse, sigma, True, 8, mx.E2M1, torch.float32)
+    torch.cuda.synchronize()
+    del qf, kf, vr, dos, x
+    rng = np.random.default_rng(12)
+    nb = S // 32
+    for (b, h), (qn, kn, vn, on, dn, ln) in heads.items():
+        gq, gk, gv = (t[b, :, h, :].double().cpu().numpy() for t in (dq, dk, dv))
+        qb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        kb = sorted({0, nb - 1, *rng.choice(nb, 2, replace=False).tolist()})
+        args = (qn, kn, vn, on, dn, ln, sigma, True)
+        ex = at.backward_head_blocks(*args, q_blocks=qb, k_blocks=kb, qk_fmt="e2m1")
+        bd = at.backward_bounds(*args, q_blocks=qb, k_blocks=kb, qk_fmt="e2m1")
+        for name, g_, bl in (("dQ", gq, qb), ("dK", gk, kb), ("dV", gv, kb)):
+            rows = np.concatenate([np.arange(32 * i, min(S, 32 * i + 32)) for i in bl])
+            check_grad_bounds(g_[rows], *bd[name], np.concatenate([ex[name][i] for i in bl]),
+                              f"e2m1 llm b{b} h{h} {name} blocks {bl}")
