@@ -95,17 +95,18 @@ MX_DEV void static_for(F&& f) {
 template <int FMT>
 constexpr int fmt_bits() { return FMT == 0 ? 8 : FMT == 4 ? 4 : 6; }
 
-// lane (n, g)'s operand from its row's 8w-byte K chunk in LDS
+// lane (n, g)'s operand from its row's 8w-byte K chunk in LDS; for E4M3 and E2M1 the row's 16-byte
+// chunk c sits in slot c ^ sw (sw: the row's swizzle), for E2M3 / E3M2 in slot c of a padded row
 template <int FMT>
-MX_DEV v8i load_operand(const uint8_t* row, int g) {
+MX_DEV v8i load_operand(const uint8_t* row, int g, int sw) {
   if constexpr (FMT == 0) {
-    return pack8g(*(const uint4*)(row + 16 * g), *(const uint4*)(row + 32 + 16 * g));
+    return pack8g(*(const uint4*)(row + 16 * (g ^ sw)), *(const uint4*)(row + 16 * ((2 + g) ^ sw)));
   } else if constexpr (fmt_bits<FMT>() == 6) {
     const uint2* p = (const uint2*)(row + 24 * g);
     const uint2 a = p[0], b = p[1], c = p[2];
     return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
   } else {
-    const uint4 a = *(const uint4*)(row + 16 * g);
+    const uint4 a = *(const uint4*)(row + 16 * (g ^ sw));
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   }
 }
@@ -122,15 +123,21 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   constexpr int BM = 256, BN = 256;
   constexpr int W = fmt_bits<FMT>();
   constexpr int RBK = 8 * W;                        // bytes of one row per 64-deep K step
-  constexpr int KST = RBK + (W == 6 ? 32 : 16);     // LDS row stride: 16-byte aligned, rows on distinct banks
   constexpr int CPR = RBK / 16;                     // 16-byte chunks per row and step
-  constexpr int SL = KST / 16;                      // 16-byte slots per padded LDS row
+  // E4M3 (4 chunks) and E2M1 (2 chunks): unpadded rows, chunk c of row r in slot c ^ swz(r), so the 16
+  // rows one read instruction serves per pass cover all 64 banks; E2M3 / E3M2 (3 chunks, read in 8-byte
+  // pieces): rows padded to 80 bytes
+  constexpr bool SWZ = W != 6;
+  constexpr int KST = SWZ ? RBK : RBK + 32;         // LDS row stride
+  constexpr int RPS = 16 / CPR;                     // rows per 256 bytes (E4M3: 4, E2M1: 8)
+  auto swz = [](int r) { return SWZ ? (r / RPS) % CPR : 0; };
+  constexpr int SL = KST / 16;                      // 16-byte slots per LDS row
   constexpr int NB = BM * KST / 1024;               // 1 KB DMA blocks per tile and step
   static_assert(BM == BN && BM * KST % 1024 == 0 && 2 * NB % NW == 0, "tiles must be whole DMA blocks");
   static_assert(BM <= NTH, "one scale row per thread");
   // A and B step tiles arrive by 16-byte DMA (buffer loads straight into LDS; lane l of an
-  // instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block): a padded row is SL slots, the
-  // ones past the payload a copy of its last chunk (never read).  One array per buffer keeps the
+  // instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block), each lane fetching the chunk its
+  // slot holds: a padded row's slots past the payload hold a copy of its last chunk (never read).  One array per buffer keeps the
   // LDS reads of one buffer independent of the DMA into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * KST];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * KST];
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
       const bool isa = blk < NB;
       const int b = isa ? blk : blk - NB;
       const int ch = b * 64 + lane, r = ch / SL;
-      const int off = r * rowb + kt * RBK + 16 * min(ch % SL, CPR - 1);
+      const int off = r * rowb + kt * RBK + 16 * (SWZ ? (ch % SL) ^ swz(r) : min(ch % SL, CPR - 1));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb,
                                                (__attribute__((address_space(3))) void*)((isa ? dA : dB) + 1024 * b),
                                                16, off, 0, 0, 0);
@@ -242,12 +249,12 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
     int sa[WM], sb[WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      ao[i] = load_operand<FMT>(bufA(cur) + (wr + 32 * i + n) * KST, g);
+      ao[i] = load_operand<FMT>(bufA(cur) + (wr + 32 * i + n) * KST, g, swz(n));
       sa[i] = (int)(sAs[cur][wr + 32 * i + n] >> (8 * g));
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      bo[j] = load_operand<FMT>(bufB(cur) + (wc + 32 * j + n) * KST, g);
+      bo[j] = load_operand<FMT>(bufB(cur) + (wc + 32 * j + n) * KST, g, swz(n));
       sb[j] = (int)(sBs[cur][wc + 32 * j + n] >> (8 * g));
     }
 #pragma unroll
