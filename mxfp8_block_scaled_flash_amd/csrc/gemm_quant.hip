@@ -181,17 +181,25 @@ __global__ __launch_bounds__(64 * GEMM_NW, 1) void gemm_quant_kernel(GemmArgs a)
   const bool wide_scales = (kb32 & 15) == 0;
   uint4 scw = make_uint4(0, 0, 0, 0);   // 8 steps of this row's scale pairs
   int kfirst = 0;                       // the first load always fetches
+  // unpadded rows: block b holds rows 64 b / CPR + l / CPR, and lane l's chunk depends on l alone
+  // (the swizzle of row r is (r / RPS) mod CPR = (4 b + l / 16) mod CPR), so one per-lane offset
+  // serves every block, the block's part going in the scalar offset
+  const int lane_off = SWZ ? (lane / CPR) * rowb + 16 * ((lane % CPR) ^ ((lane / 16) % CPR)) : 0;
   auto dma = [&](int kt, uint8_t* dA, uint8_t* dB) {
 #pragma unroll
     for (int j = 0; j < 2 * NB / NW; ++j) {
       const int blk = w + NW * j;   // A blocks first, then B
       const bool isa = blk < NB;
       const int b = isa ? blk : blk - NB;
-      const int ch = b * 64 + lane, r = ch / SL;
-      const int off = r * rowb + kt * RBK + 16 * (SWZ ? (ch % SL) ^ swz(r) : min(ch % SL, CPR - 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb,
-                                               (__attribute__((address_space(3))) void*)((isa ? dA : dB) + 1024 * b),
-                                               16, off, 0, 0, 0);
+      auto* dst = (__attribute__((address_space(3))) void*)((isa ? dA : dB) + 1024 * b);
+      if constexpr (SWZ) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb, dst, 16, lane_off,
+                                                 __builtin_amdgcn_readfirstlane(b * (64 / CPR) * rowb + kt * RBK), 0, 0);
+      } else {
+        const int ch = b * 64 + lane, r = ch / SL;
+        const int off = r * rowb + kt * RBK + 16 * min(ch % SL, CPR - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isa ? ra : rb, dst, 16, off, 0, 0, 0);
+      }
     }
   };
   auto load = [&](int kt, Stage& st) {
