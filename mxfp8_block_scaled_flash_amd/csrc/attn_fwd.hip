@@ -115,16 +115,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int ND = D / 32;    // 32-feature chunks of O
   constexpr int KRB = D * qk_bits<QF>() / 8;   // payload bytes of one Q or K row
   // K and V tiles arrive by 16-byte DMA (buffer loads straight into LDS, no staging registers).
-  // Rows of a power-of-two number of 16-byte chunks are stored unpadded with chunk j of row r in
-  // slot j ^ (r mod chunks), so the operand reads spread over the banks; MXFP6 K rows (3 or 6
-  // chunks) get one spare slot instead (a copy of the last chunk, never read), which staggers
-  // the rows across the banks.
+  // Rows of a power-of-two number of 16-byte chunks are stored unpadded, chunk j of a row in a
+  // slot XOR-swizzled by the row, so the operand reads spread over the banks: K, read a row per
+  // lane (16-byte reads, 16 lanes a pass), swizzles by (r / rows per 256 bytes) mod chunks, which
+  // gives the 16 rows of a pass 16 distinct bank groups; V, read by 8-byte transpose reads, by
+  // r mod chunks (measured conflict-free for both; K swizzled by r mod chunks instead took 1.75x
+  // (128-byte rows) and 3.3x (64-byte rows) the time per read).  MXFP6 K rows (3 or 6 chunks) get
+  // one spare slot instead (a copy of the last chunk, never read), which staggers the rows across
+  // the banks.
   constexpr int CPRV = D / 16;                        // chunks per V row
   constexpr int CPRK = KRB / 16;                      // chunks of payload per K row
   constexpr bool KPOW2 = (CPRK & (CPRK - 1)) == 0;
   constexpr int SLK = KPOW2 ? CPRK : CPRK + 1;        // K row slots (MXFP6: one spare slot)
   constexpr int KRS = 16 * SLK;                       // LDS row stride of the K tile
   constexpr int SWZV = CPRV - 1, SWZK = KPOW2 ? SLK - 1 : 0;
+  constexpr int RPWK = KRS >= 256 ? 1 : 256 / KRS;     // K rows per 256 bytes (one pass of the banks)
+  auto swzk = [](int r) { return (r / RPWK) & SWZK; };
   constexpr int NBK = BN * KRS / 1024, NBV = BN * D / 1024;   // 1 KB DMA blocks (one wave instruction each)
   static_assert(BN * KRS % 1024 == 0 && BN * D % 1024 == 0, "tiles must be whole DMA blocks");
   constexpr float kLazy = 8.f;  // largest log2 of p before the frame moves
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       const int blk = w + NW * j;
       if (NBK % NW == 0 || blk < NBK) {
         const int ch = blk * 64 + lane, r = ch / SLK;
-        const int lc = (ch % SLK) ^ (r & SWZK);   // chunk this slot holds
+        const int lc = (ch % SLK) ^ swzk(r);      // chunk this slot holds
         const int off = r * (int)rowHk + 16 * min(lc, CPRK - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dK + 1024 * blk), 16,
                                                  off, 0, 0, 0);
@@ -253,11 +259,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // 32 kb rows, a whole number of swizzle periods, so its chunks sit at a constant distance.  An
   // empty asm statement hides their arithmetic, so each tile's reads use these four registers plus
   // constant offsets (otherwise every read's full address is kept or recomputed).
-  static_assert(32 % (SWZK + 1) == 0, "key blocks span whole swizzle periods");
+  static_assert(32 % (RPWK * (SWZK + 1)) == 0, "key blocks span whole swizzle periods");
   int kofs[NC][2];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int x = n & SWZK;
+    const int x = swzk(n);
     if constexpr (QF == 0) {
       kofs[c][0] = n * KRS + 16 * ((4 * c + g) ^ x);
       kofs[c][1] = n * KRS + 16 * ((4 * c + 2 + g) ^ x);
