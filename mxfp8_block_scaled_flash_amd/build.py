@@ -69,20 +69,21 @@ def build(verbose: bool = False) -> str:
 
 def _build_test_probe(verbose: bool = False) -> None:
     """tests/hw/libmfmaprobe.so: runs the scaled-MFMA instruction alone, for the
-    GPU tests that measure the instruction against the oracle's stated product bound
-    (test infrastructure)."""
-    src = os.path.join(ROOT, "tests", "hw", "mfma_probe.hip")
-    if not os.path.exists(src):
-        return
-    out = os.path.join(ROOT, "tests", "hw", "libmfmaprobe.so")
-    cmd = [HIPCC, *FLAGS, "-shared", src, "-o", out + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("build of the MFMA probe failed")
-    os.replace(out + ".tmp", out)
-    if verbose:
-        print("built", out)
+    GPU tests that measure the instruction against the oracle's stated product bound;
+    tests/hw/libldsprobe.so: times LDS read patterns (test and measurement infrastructure)."""
+    for name, lib in (("mfma_probe.hip", "libmfmaprobe.so"), ("lds_probe.hip", "libldsprobe.so")):
+        src = os.path.join(ROOT, "tests", "hw", name)
+        if not os.path.exists(src):
+            continue
+        out = os.path.join(ROOT, "tests", "hw", lib)
+        cmd = [HIPCC, *FLAGS, "-shared", src, "-o", out + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"build of {name} failed")
+        os.replace(out + ".tmp", out)
+        if verbose:
+            print("built", out)
 
 
 if __name__ == "__main__":
