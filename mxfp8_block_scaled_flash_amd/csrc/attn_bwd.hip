@@ -595,7 +595,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           keep(qsa); keep(dsa); keep(ksc); keep(vsc);
           keep(dow_prev); keep(qw_prev); keep(psc_prev); keep(ssc_prev);
           // ---- MX codes (nothing visible: zero codes, scale 1)
-          const int kp = max(exp2_scale_code(amax), 1);
+          const int kp = exp2_scale_code(amax);
           const int ks2 = max(scale_code(smax), 1);
           const float psc = e8m0_f32(kp), ssc = e8m0_f32(ks2);   // the converts saturate (wave MODE)
           uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3

@@ -373,14 +373,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       // ---- p = 2^(S c - M), running sum
       // four partial sums: independent add chains (one chain held every p live until its add,
       // which pushed the kernel past its register budget)
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      float ps[4];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, negM));
           st[kb][i] = p;
-          ps[i & 3] += p;
+          if (kb == 0 && i < 4) ps[i] = p;   // (0 + p would cost an add: -0 + 0 is +0)
+          else ps[i & 3] += p;
         }
       l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       int kc[KB];
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // block amax of p is 2^(block max of t - M): its scale straight from that exponent
-        kc[kb] = max(exp2_scale_code(fmaf(bm[kb], c, negM)), 1);
+        kc[kb] = exp2_scale_code(fmaf(bm[kb], c, negM));
         sc[kb] = e8m0_f32(kc[kb]);
       }
       // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3

@@ -46,16 +46,23 @@ MX_DEV int scale_code(float amax) {
 
 // E8M0 code of a block of values p = fl32(2^a), from the block's largest
 // exponent a_max alone: the code clamp(floor(log2 fl32(2^a_max)) + 119, 0, 254)
-// that scale_code() would pick from the rounded maximum.  floor(log2) of the
-// rounded value is floor(a_max), except on [log2(1 - 2^-25), 0), where 2^a
-// rounds up to 1.0 (the fp32 bound below is the smallest float in that
-// interval).  No other fp32 a lies that close below an integer.  This makes
-// the decision independent of the accuracy of the hardware exp2.
+// that scale_code() would pick from the rounded maximum, raised to at least 1
+// (the attention kernels give an empty or fully masked block, code 0, scale 1).
+// floor(log2) of the rounded value is floor(a_max), except on
+// [log2(1 - 2^-25), 0), where 2^a rounds up to 1.0 (0xB338AA3B is the
+// smallest float in that interval, so these are the negative floats whose bit
+// patterns lie in [0x80000000, 0xB338AA3B]).  No other fp32 a lies that close
+// below an integer.  This makes the decision independent of the accuracy of the
+// hardware exp2.  Six VALU instructions: v_cvt_flr_i32_f32 floors and converts
+// in one (-inf gives INT_MIN, which the clamp takes to 1); the same codes as
+// floor / clamp / convert written out, for every fp32 input but NaN (checked
+// exhaustively on the CPU).
 MX_DEV int exp2_scale_code(float a_max) {
-  // branch-free: an empty or fully masked block (a_max = -inf) ends at code 0
-  float f = fmaxf(floorf(a_max), -256.f);
-  f = (a_max < 0.f && a_max >= __uint_as_float(0xB338AA3Bu)) ? 0.f : f;
-  return min(max((int)f + 119, 0), 254);
+  int fl;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(fl) : "v"(a_max));
+  const bool near_zero = (__float_as_uint(a_max) ^ 0x80000000u) <= 0x3338AA3Bu;   // a_max in [-T, -0]
+  const int code = near_zero ? 119 : (int)((uint32_t)fl + 119u);
+  return min(max(code, 1), 254);
 }
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));

@@ -57,6 +57,14 @@ PATTERNS = [
      tr_pattern(lambda r, G, i: 128 * r + 16 * ((G & 1) ^ (r & 7)) + 8 * (i & 1))),
     (TR8, "rows 128 B, slot ^ ((r >> 1) & 7)",
      tr_pattern(lambda r, G, i: 128 * r + 16 * ((G & 1) ^ ((r >> 1) & 7)) + 8 * (i & 1))),
+    (B128, "rows 128 B, chunk g in slot g ^ ((n & 6) | ((n >> 3) & 1))",
+     row_pattern(lambda n, g: 128 * n + 16 * (g ^ ((n & 6) | ((n >> 3) & 1))))),
+    (TR8, "rows 128 B, slot ^ ((r & 6) | ((r >> 3) & 1))",
+     tr_pattern(lambda r, G, i: 128 * r + 16 * ((G & 1) ^ ((r & 6) | ((r >> 3) & 1))) + 8 * (i & 1))),
+    (TR8, "rows 128 B, slot ^ ((r & 6) | ((r >> 3) & 1)), rows r + 8",
+     tr_pattern(lambda r, G, i: 128 * (r + 8) + 16 * ((G & 1) ^ (((r + 8) & 6) | (((r + 8) >> 3) & 1))) + 8 * (i & 1))),
+    (TR8, "rows 64 B, slot ^ (2 ((r >> 2) & 1))",
+     tr_pattern(lambda r, G, i: 64 * r + 16 * ((G & 1) ^ (2 * ((r >> 2) & 1))) + 8 * (i & 1))),
     (TR8, "rows 64 B, slot ^ (r & 3) (backward small-format dS)",
      tr_pattern(lambda r, G, i: 64 * r + 16 * ((G & 1) ^ (r & 3)) + 8 * (i & 1))),
 ]
