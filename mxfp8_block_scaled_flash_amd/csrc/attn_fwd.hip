@@ -110,6 +110,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;   // queries per workgroup
   constexpr int BN = FWD_BN;    // keys per tile
   constexpr int KB = BN / 32;   // 32-key blocks per tile
+  static_assert(KB % 2 == 0, "block maxima are exchanged in pairs of blocks");
   constexpr int KH = BN / 64;   // 64-key halves per tile (one P V contraction each)
   constexpr int NC = D / 64;    // 64-feature chunks of the QK^T contraction
   constexpr int ND = D / 32;    // 32-feature chunks of O
@@ -338,13 +339,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         }
       }
       // ---- block maxima, frame update
+      // per lane the max of its 16 keys of each block; then blocks in pairs: one half swap gives
+      // lanes 0-31 both halves of block 2j and lanes 32-63 both halves of block 2j + 1, a second
+      // (of the pairwise maximum with itself) hands each lane both blocks' maxima
       float bm[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float m = st[kb][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) m = fmaxf(m, st[kb][i]);
-        bm[kb] = half_swap_max(m);
+        bm[kb] = m;
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 2) {
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm[kb]), __float_as_uint(bm[kb + 1]), false, false);
+        const float x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        bm[kb] = __uint_as_float(b[0]);
+        bm[kb + 1] = __uint_as_float(b[1]);
       }
       // S has been read: this tile's S products and the previous tile's P V products are done
 #pragma unroll
