@@ -174,8 +174,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   // ---- staging of one K/V tile: buffer loads into registers, then LDS stores.
   // Each tile gets scalar buffer resources that end with the sequence, so rows
   // (and scale blocks) past its end read as zero: no clamps, no branches, and no
-  // wait on the loads before the tile being computed needs them.  Wave 0 fetches
-  // and stores the K scales of key `lane`, wave 1 the V ones.
+  // wait on the loads before the tile being computed needs them.  Every wave
+  // fetches the scales of key `lane` (loading them on the storing waves only put
+  // the staging registers in scratch memory); wave 0 stores the K ones, wave 1 the V ones.
   const int KSB = D / 32;   // bytes per K ROW32 scale word
   using Scales = ScaleStage<D, BN>;
   // lane l of a DMA instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block (measured)
@@ -231,18 +232,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rks = buffer_rsrc(nt.ks, (rows - 1) * a.H * KSB + KSB);
     const int nblk = (rows + 31) / 32;
     const __amdgpu_buffer_rsrc_t rvs = buffer_rsrc(nt.vs, (nblk - 1) * a.H * D + D);
-    // only the waves that store them load them: wave 0 the K scales, wave 1 the V scales
 #pragma unroll
     for (int hh = 0; hh < KH; ++hh) {
       const int kk = 64 * hh + lane;   // key of this lane in the tile
-      if (w == 0) {
-        st.ks[hh] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, kk * a.H * KSB, 0, 0)
-                               : __builtin_amdgcn_raw_buffer_load_b16(rks, kk * a.H * KSB, 0, 0);
-      } else if (w == 1) {
-        const int voff = (kk >> 5) * a.H * D + (kk & 31);
+      st.ks[hh] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, kk * a.H * KSB, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b16(rks, kk * a.H * KSB, 0, 0);
+      const int voff = (kk >> 5) * a.H * D + (kk & 31);
 #pragma unroll
-        for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
-      }
+      for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
     }
   };
   auto store_scales = [&](int buf, const Scales& st) {
