@@ -3,7 +3,9 @@ known to be complete (CPU: compiles the kernel sources to gfx950 assembly with t
 flags and walks it; tests/hw/scale_hazard.py states the hazard and the rule).  The checker is pinned
 on hand-written assembly first: one sequence that overwrites a scale register right after the
 instruction, and the same sequence with the result read before the write."""
+import functools
 import os
+import re
 import subprocess
 import tempfile
 
@@ -32,8 +34,8 @@ def test_checker_flags_an_early_write_and_clears_a_read_first():
     assert sh.violations(BAD.replace("v40, 0", "v44, 0")) == []
 
 
-@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "gemm_quant.hip"])
-def test_kernels_keep_scale_registers_until_complete(src):
+@functools.lru_cache(maxsize=None)
+def _device_asm(src):
     path = os.path.join(bld.CSRC, src)
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
@@ -41,7 +43,24 @@ def test_kernels_keep_scale_registers_until_complete(src):
                "-S", path, "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
-        asm = open(out).read()
+        return open(out).read()
+
+
+@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "gemm_quant.hip"])
+def test_kernels_keep_scale_registers_until_complete(src):
+    asm = _device_asm(src)
     assert "v_mfma_scale" in asm
     bad = sh.violations(asm)
     assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", ["attn_fwd.hip", "gemm_quant.hip"])
+def test_forward_and_gemm_kernels_use_no_scratch_memory(src):
+    """The forward and GEMM kernels keep everything in registers and LDS: a private segment there
+    means spilled registers or an array the compiler could not keep in registers, each access a
+    memory round trip inside the main loop."""
+    asm = _device_asm(src)
+    sizes = re.findall(r"\.name:\s+(\S+)\s+\.private_segment_fixed_size:\s+(\d+)", asm)
+    assert sizes, "no kernel metadata found"
+    used = [(n, int(b)) for n, b in sizes if int(b) != 0]
+    assert not used, used
