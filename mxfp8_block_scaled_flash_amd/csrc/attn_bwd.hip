@@ -601,15 +601,21 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            // the two converts fill both halves, so any register serves as the old value
-            v2s z = __builtin_bit_cast(v2s, st[4 * q]);
-            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
-            z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
-            pw[q] = __builtin_bit_cast(uint32_t, z);
-            v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
-            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
-            y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
-            sw[q] = __builtin_bit_cast(uint32_t, y);
+            if constexpr (W != 6) {
+              pw[q] = cvt4_scaled_fp8(st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3], psc);
+              sw[q] = cvt4_scaled_fp8(dpt[4 * q], dpt[4 * q + 1], dpt[4 * q + 2], dpt[4 * q + 3], ssc);
+            } else {
+              // MXFP6 Q, K: through the builtins (the asm form raised this variant's spills from 40 to
+              // 113 registers, +28% time; it lowers the E4M3 and E2M1 ones, E2M1 -8%)
+              v2s z = __builtin_bit_cast(v2s, st[4 * q]);
+              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
+              z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
+              pw[q] = __builtin_bit_cast(uint32_t, z);
+              v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
+              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
+              y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
+              sw[q] = __builtin_bit_cast(uint32_t, y);
+            }
           }
           // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
           auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);

@@ -411,14 +411,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // the two converts fill both halves of the dword: written as one statement with an
-          // early-clobbered output and no tied old value (the builtin ties one, and the compiler
-          // then copied a register into each destination first: 36 moves per kernel)
-          uint32_t r;
-          asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\tv_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]"
-              : "=&v"(r)
-              : "v"(st[kb][4 * q]), "v"(st[kb][4 * q + 1]), "v"(st[kb][4 * q + 2]), "v"(st[kb][4 * q + 3]), "v"(sc[kb]));
-          dw[kb][q] = r;
+          dw[kb][q] = cvt4_scaled_fp8(st[kb][4 * q], st[kb][4 * q + 1], st[kb][4 * q + 2], st[kb][4 * q + 3], sc[kb]);
         }
       // ---- per 64-key half hh: swap lane halves so lane half g holds keys 16g + 0..15 of each of
       // its two blocks, in order; then O^T += V^T P^T (V^T rows d = 32 dc + lane%32, through LDS

@@ -101,6 +101,18 @@ MX_DEV uint32_t f32_to_bf16(float f) {
 
 MX_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
+// Four fp32 values divided by the E8M0 scale `scale` (as fp32) and converted to E4M3 codes, little-
+// endian in one dword: two v_cvt_scalef32_pk_fp8_f32 (low, then high half of the dword), written as one
+// statement with an early-clobbered output and no tied old value (through the builtin, which ties one,
+// the compiler first copied a register into each destination).
+MX_DEV uint32_t cvt4_scaled_fp8(float a, float b, float c, float d, float scale) {
+  uint32_t r;
+  asm("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\tv_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]"
+      : "=&v"(r)
+      : "v"(a), "v"(b), "v"(c), "v"(d), "v"(scale));
+  return r;
+}
+
 // max of v and the value of the lane 32 apart (v_permlane32_swap exchanges the wave's halves)
 MX_DEV float half_swap_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
