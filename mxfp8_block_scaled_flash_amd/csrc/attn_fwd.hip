@@ -23,9 +23,10 @@
 //    dependence on the accuracy of the hardware exp2).  The fp32->fp8 convert
 //    (which divides by the E8M0 scale) saturates through the wave's MODE
 //    setting, so no clamp precedes it.
-//  * P is re-packed between lane halves with v_permlane32_swap so each lane
-//    holds 16 consecutive keys per block; V^T comes from a row-major LDS tile
-//    through ds_read_b64_tr_b8, in the same key order.
+//  * The K rows of each 32-key block sit in LDS in an order that makes each
+//    lane half's 16 elements of S^T 16 consecutive keys, the order in which
+//    the P V product takes P (no lane-half exchange of P); V^T comes from a
+//    row-major LDS tile through ds_read_b64_tr_b8, in that key order.
 //  * K and V tiles of 128 keys go from HBM straight into LDS (16-byte buffer
 //    loads with the LDS as destination, no staging registers), into rows
 //    whose 16-byte chunks are XOR-swizzled by row so the operand reads spread
@@ -132,6 +133,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int SWZV = CPRV - 1, SWZK = KPOW2 ? SLK - 1 : 0;
   constexpr int RPWK = KRS >= 256 ? 1 : 256 / KRS;     // K rows per 256 bytes (one pass of the banks)
   auto swzk = [](int r) { return (r / RPWK) & SWZK; };
+  // K rows of each 32-key block are stored in the order that makes the S^T product's output element
+  // i of lane half g key 16 g + i of the block: LDS row p (= output row 8(i/4) + 4g + i%4) holds key
+  // korder(p).  P then comes out of the softmax with each lane half holding its 16 consecutive keys,
+  // the order the P V product takes them in, with no lane-half exchange.
+  auto korder = [](int p) { return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3); };
   constexpr int NBK = BN * KRS / 1024, NBV = BN * D / 1024;   // 1 KB DMA blocks (one wave instruction each)
   static_assert(BN * KRS % 1024 == 0 && BN * D % 1024 == 0, "tiles must be whole DMA blocks");
   constexpr float kLazy = 8.f;  // largest log2 of p before the frame moves
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       if (NBK % NW == 0 || blk < NBK) {
         const int ch = blk * 64 + lane, r = ch / SLK;
         const int lc = (ch % SLK) ^ swzk(r);      // chunk this slot holds
-        const int off = r * (int)rowHk + 16 * min(lc, CPRK - 1);
+        const int off = korder(r) * (int)rowHk + 16 * min(lc, CPRK - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dK + 1024 * blk), 16,
                                                  off, 0, 0, 0);
       }
@@ -315,13 +321,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     if (compute) {
       const uint8_t* sKc = cur ? sK1 : sK0;
       const uint8_t* sVc = cur ? sV1 : sV0;
-      // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 8(i/4) + 4g + i%4, query qi
+      // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 16g + i (K rows in korder), query qi
       v16f st[KB];
       uint32_t ksc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint8_t* kt = sKc + kb * 32 * KRS;
-        ksc[kb] = sKs[cur][kb * 32 + n] >> (8 * g);
+        ksc[kb] = sKs[cur][kb * 32 + korder(n)] >> (8 * g);
         v16f acc = v16f{};
         acc = mfma32<0, 0, QF>(qk_operand_at<QF>(kt, kofs[0][0], kofs[0][1]), qa[0], acc, ksc[kb], qsc);
         if constexpr (NC > 1)
@@ -330,13 +336,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       const bool need_mask = (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > q0);
       if (need_mask) {
-        // element i is key k0 + 32 kb + 4g + c_i, c_i = 8(i/4) + i%4: visible iff c_i < hi
+        // element i is key k0 + 32 kb + 16 g + i: visible iff i < hi
         const int last = CAUSAL ? min(L - 1, qi) : L - 1;   // last visible key of this query
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const int hi = last - k0 - 32 * kb - 4 * g + 1;
+          const int hi = last - k0 - 32 * kb - 16 * g + 1;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) st[kb][i] = (8 * (i >> 2) + (i & 3) < hi) ? st[kb][i] : -INFINITY;
+          for (int i = 0; i < 16; ++i) st[kb][i] = (i < hi) ? st[kb][i] : -INFINITY;
         }
       }
       // ---- block maxima, frame update
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         kc[kb] = exp2_scale_code(fmaf(bm[kb], c, negM));
         sc[kb] = e8m0_f32(kc[kb]);
       }
-      // ---- P -> E4M3 codes: dword q of block kb holds keys 8q + 4g + 0..3
+      // ---- P -> E4M3 codes: dword q of block kb holds keys 16g + 4q + 0..3
       uint32_t dw[KB][4];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -413,8 +419,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         for (int q = 0; q < 4; ++q) {
           dw[kb][q] = cvt4_scaled_fp8(st[kb][4 * q], st[kb][4 * q + 1], st[kb][4 * q + 2], st[kb][4 * q + 3], sc[kb]);
         }
-      // ---- per 64-key half hh: swap lane halves so lane half g holds keys 16g + 0..15 of each of
-      // its two blocks, in order; then O^T += V^T P^T (V^T rows d = 32 dc + lane%32, through LDS
+      // ---- per 64-key half hh: lane half g holds keys 16g + 0..15 of each of its two blocks, in
+      // order (the K row order above); O^T += V^T P^T (V^T rows d = 32 dc + lane%32, through LDS
       // transpose reads)
       const int G = lane >> 4, i16 = lane & 15;
       const int rowofs = 16 * (G >> 1) + (i16 >> 1);
@@ -422,15 +428,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int hh = 0; hh < KH; ++hh) {
         v8i pb;
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-          const int kb = 2 * hh + b2;
-          auto s02 = __builtin_amdgcn_permlane32_swap(dw[kb][0], dw[kb][2], false, false);
-          auto s13 = __builtin_amdgcn_permlane32_swap(dw[kb][1], dw[kb][3], false, false);
-          pb[4 * b2 + 0] = s02[0];
-          pb[4 * b2 + 1] = s02[1];
-          pb[4 * b2 + 2] = s13[0];
-          pb[4 * b2 + 3] = s13[1];
-        }
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pb[4 * b2 + q] = dw[2 * hh + b2][q];
         const int psc = g ? kc[2 * hh + 1] : kc[2 * hh];
         const uint32_t vsc = sVs[cur][64 * hh + lane];
 #pragma unroll
