@@ -512,7 +512,8 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       const uint8_t* sQb = sQ[buf];
       const uint8_t* sDOb = sDO[buf];
       if (EARLY && j > 0) phase_c(q0 - BQ, buf ^ 1);   // half the waves: the previous step's dQ first
-      // ---- A. S and dP for (key block w, query block t): element e = query q0 + 32t + 8(e/4) + 4g + e%4
+      // ---- A. S and dP for (key block w, query block t): element e = query q0 + 32t + 16g + e (E4M3;
+      // small formats: q0 + 32t + 8(e/4) + 4g + e%4)
       v8i pB, sB;        // P and dS codes as B operands: bytes 16t + 0..15 = queries 32t + 16g + 0..15
       int kpc[2], ksc2[2];
       const bool live = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);   // a key of the block sees a query
@@ -524,19 +525,29 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         const uint8_t* vrs = sV + (32 * w + n) * VST;
         auto vchunk = [&](int j) __attribute__((always_inline)) { return *(const uint4*)(vrs + 16 * (j ^ (n & 7))); };
         const uint32_t ksc = sKs[w] >> (8 * g), vsc = sVs[32 * w + n] >> (8 * g);
+        // E4M3: lane n supplies query row qrow of each 32-query block to the S and dP products: output
+        // row 8(e/4) + 4g + e%4 then holds query 16g + e, so each lane half's P and dS codes are its
+        // 16 consecutive queries, the order the dV / dK products and the dS tile take them in (no
+        // lane-half exchange).  The small formats keep the natural rows and exchange the codes (with
+        // the permuted rows their spills rose from 15-40 to 49-118 registers).
+        constexpr bool QPERM = !SMALL;
+        const int qrow = QPERM ? ((((n >> 2) & 1) << 4) | (((n >> 3) & 3) << 2) | (n & 3)) : n;
+        // element e of lane half g: query qa0 + qoff + qe(e)
+        const int qoff = QPERM ? 16 * g : 4 * g;
+        auto qe = [](int e) { return QPERM ? e : 8 * (e >> 2) + (e & 3); };
   #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int qa0 = q0 + 32 * t;
           const bool act = qa0 < L && !(CAUSAL && kw0 > qa0 + 31);
           const bool edge = !act || qa0 + 31 >= L || kw0 + 31 >= L || (CAUSAL && kw0 + 31 > qa0);
-          // element e is query qa0 + 4g + c_e, c_e = 8(e/4) + e%4: visible iff lo <= c_e < hi
-          const int lo = (!act || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - 4 * g : -64);
-          const int hi = L - qa0 - 4 * g;
+          // element e is query qa0 + qoff + qe(e): visible iff lo <= qe(e) < hi
+          const int lo = (!act || kj >= L) ? 64 : (CAUSAL ? kj - qa0 - qoff : -64);
+          const int hi = L - qa0 - qoff;
           const uint32_t qsa = sQs[buf][t] >> (8 * g), dsa = sDOs[buf][t] >> (8 * g);
           // computed for every block (rows past either end are zero, so the values are
           // finite); the mask zeroes p and dS where nothing is visible
-          const uint8_t* qp = sQb + (32 * t + n) * KST + 16 * g;
-          const uint8_t* op = sDOb + (32 * t + n) * KST + 16 * g;
+          const uint8_t* qp = sQb + (32 * t + qrow) * KST + 16 * g;
+          const uint8_t* op = sDOb + (32 * t + qrow) * KST + 16 * g;
           v16f st, dpt;
           if constexpr (!SMALL) {
             st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
@@ -551,7 +562,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
             }
           } else {
             // S from the packed rows (lane half g: 32-element block 2 c + g); dP as above with V swizzled
-            const uint8_t* qps = sQb + (32 * t + n) * QRS + g * BB;
+            const uint8_t* qps = sQb + (32 * t + qrow) * QRS + g * BB;
             st = mfma32f<QF, QF, 0, 0>(small_operand<W>(qps), small_operand<W>(krs), v16f{}, qsa, ksc);
             dpt = mfma32b<0, 0>(pack8b(*(const uint4*)op, *(const uint4*)(op + 32)), pack8b(vchunk(g), vchunk(2 + g)),
                                 v16f{}, dsa, vsc);
@@ -567,16 +578,15 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   #pragma unroll
             for (int q = 0; q < 4; ++q) {
               if (q == 2) __builtin_amdgcn_sched_barrier(0);
-              const float4 l4 = *(const float4*)(&sL[buf][32 * t + 8 * q + 4 * g]);
-              const float4 d4 = *(const float4*)(&sDv[buf][32 * t + 8 * q + 4 * g]);
+              const float4 l4 = *(const float4*)(&sL[buf][32 * t + qoff + qe(4 * q)]);
+              const float4 d4 = *(const float4*)(&sDv[buf][32 * t + qoff + qe(4 * q)]);
               const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
   #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int e = 4 * q + r;
                 float arg = fmaf(st[e], cl, -lq[r]);
                 if constexpr (decltype(masked)::value) {
-                  const int ce = 8 * q + r;
-                  arg = (ce >= lo && ce < hi) ? arg : -INFINITY;
+                  arg = (qe(e) >= lo && qe(e) < hi) ? arg : -INFINITY;
                 }
                 const float p = __builtin_amdgcn_exp2f(arg);
                 const float ds = p * (dpt[e] - dq[r]);
@@ -598,7 +608,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           const int kp = exp2_scale_code(amax);
           const int ks2 = max(scale_code(smax), 1);
           const float psc = e8m0_f32(kp), ssc = e8m0_f32(ks2);   // the converts saturate (wave MODE)
-          uint32_t pw[4], sw[4];   // dword q holds queries 8q + 4g + 0..3
+          uint32_t pw[4], sw[4];   // dword q holds queries qoff + qe(4q) + 0..3
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if constexpr (W != 6) {
@@ -617,18 +627,25 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
               sw[q] = __builtin_bit_cast(uint32_t, y);
             }
           }
-          // ---- swap lane halves: half g then holds queries 16g + 0..15 of the block, in order
-          auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-          auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-          auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
-          auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
-          pB[4 * t + 0] = a02[0]; pB[4 * t + 1] = a02[1]; pB[4 * t + 2] = a13[0]; pB[4 * t + 3] = a13[1];
-          sB[4 * t + 0] = b02[0]; sB[4 * t + 1] = b02[1]; sB[4 * t + 2] = b13[0]; sB[4 * t + 3] = b13[1];
+          // lane half g holds queries 16g + 0..15 of the block, in order (small formats: after swapping
+          // lane halves)
+          if constexpr (!QPERM) {
+            auto a02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+            auto a13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+            auto b02 = __builtin_amdgcn_permlane32_swap(sw[0], sw[2], false, false);
+            auto b13 = __builtin_amdgcn_permlane32_swap(sw[1], sw[3], false, false);
+            pw[0] = a02[0]; pw[1] = a02[1]; pw[2] = a13[0]; pw[3] = a13[1];
+            sw[0] = b02[0]; sw[1] = b02[1]; sw[2] = b13[0]; sw[3] = b13[1];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pB[4 * t + q] = pw[q];
+            sB[4 * t + q] = sw[q];
+          }
           if constexpr (!SMALL)
-            *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(b02[0], b02[1], b13[0], b13[1]);
+            *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
           else
-            *(uint4*)(sDS[buf] + (32 * w + n) * DST + 16 * ((2 * t + g) ^ (n & 3))) =
-                make_uint4(b02[0], b02[1], b13[0], b13[1]);
+            *(uint4*)(sDS[buf] + (32 * w + n) * DST + 16 * ((2 * t + g) ^ (n & 3))) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
           if (lane == 0) sDSs[buf][t][w] = ks2;
           kpc[t] = kp;
           ksc2[t] = ks2;
