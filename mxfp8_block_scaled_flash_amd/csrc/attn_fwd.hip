@@ -27,12 +27,12 @@
 //    lane half's 16 elements of S^T 16 consecutive keys, the order in which
 //    the P V product takes P (no lane-half exchange of P); V^T comes from a
 //    row-major LDS tile through ds_read_b64_tr_b8, in that key order.
-//  * K and V tiles of 128 keys go from HBM straight into LDS (16-byte buffer
-//    loads with the LDS as destination, no staging registers), into rows
-//    whose 16-byte chunks are XOR-swizzled by row so the operand reads spread
-//    over the banks; two LDS buffers, the next tile's loads in flight while
-//    the current one is computed, one barrier per tile, and two workgroups
-//    per CU so one's softmax overlaps the other's MFMAs.  Workgroups are ordered so that each XCD works
+//  * K and V tiles of 64 or 128 keys go from HBM straight into LDS (16-byte
+//    buffer loads with the LDS as destination, no staging registers), into
+//    rows whose 16-byte chunks are XOR-swizzled by row so the operand reads
+//    spread over the banks; two LDS buffers, the next tile's loads in flight
+//    while the current one is computed, one barrier per tile, and three (or
+//    two) workgroups per CU so one's softmax overlaps another's MFMAs.  Workgroups are ordered so that each XCD works
 //    through whole heads, longest (causal) query tiles first, keeping a
 //    head's K/V in that XCD's L2.
 #include "mx_common.h"
