@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
 #pragma unroll
   for (int hh = 0; hh < KH; ++hh) vsc_prev[hh] = psc_prev[hh] = 0;
 
-  // one tile's products and softmax from LDS buffer cur; hook() (the next tile's DMA) runs right after
+  // one tile's products and softmax from LDS buffer cur; hook() (the next tile's scale loads and DMA) runs right after
   // the S products are issued, or at once on a wave with nothing to compute: a wave's DMA issue can
   // wait on the CU's memory pipe, and its S products then already run (measured -3% against issuing
   // it before them)
@@ -477,14 +477,12 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
     Scales s1;
-    load_scales(s1);
-    tile_body(t, 0, [&]() { dma_tile(sK1, sV1); });
+    tile_body(t, 0, [&]() { load_scales(s1); dma_tile(sK1, sV1); });
     advance();
     store_scales(1, s1);
     __syncthreads();
     Scales s2;
-    load_scales(s2);
-    tile_body(t + 1, 1, [&]() { dma_tile(sK0, sV0); });
+    tile_body(t + 1, 1, [&]() { load_scales(s2); dma_tile(sK0, sV0); });
     advance();
     store_scales(0, s2);
     __syncthreads();
