@@ -103,14 +103,6 @@ constexpr bool fwd_three_waves() {
   return D == 64 || QF != 0 || (CAUSAL && OUT_BF16);
 }
 
-// The E8M0 scales of one BN-key tile in flight between HBM and LDS (the payload goes by DMA).
-template <int D, int BN>
-struct ScaleStage {
-  static constexpr int KH = BN / 64;   // 64-key halves: one scale word per lane and half
-  uint32_t ks[KH];
-  uint32_t vb[KH][D / 32];   // V COL32 scale bytes, combined only when stored (no wait at the load)
-};
-
 template <int D, int NW, bool CAUSAL, bool OUT_BF16, int QF>
 __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>() ? 3 : 2)) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 32 * NW;   // queries per workgroup
@@ -154,8 +146,12 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[BN * KRS];
   __shared__ __attribute__((aligned(1024))) uint8_t sV0[BN * D];
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[BN * D];
-  __shared__ uint32_t sKs[2][BN];   // K ROW32 scale bytes of each key
-  __shared__ uint32_t sVs[2][BN];   // [key block b][r]: byte dc = V COL32 scale of (b, d = 32 dc + r)
+  // The tile's E8M0 scales arrive by DMA too, one 4-byte LDS word per lane: K's ROW32 scale word of
+  // each key; V's COL32 scale bytes (zero-extended by the byte-sized DMA) as [dc][64 hh + l] = the
+  // scale of (key block 2 hh + l / 32, d = 32 dc + l % 32).  One array per buffer, so the reads of one
+  // carry no dependence on the DMA into the other.
+  __shared__ uint32_t sKs0[BN], sKs1[BN];
+  __shared__ uint32_t sVs0[ND][BN], sVs1[ND][BN];
 
   saturating_fp8_converts();
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, n = lane & 31;
@@ -182,14 +178,13 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
   const long rowH = (long)a.H * D;       // V and O row stride
   const long rowHk = (long)a.H * KRB;    // Q and K payload row stride
 
-  // ---- staging of one K/V tile: buffer loads into registers, then LDS stores.
+  // ---- staging of one K/V tile: payload and scales by buffer loads whose destination is the LDS.
   // Each tile gets scalar buffer resources that end with the sequence, so rows
   // (and scale blocks) past its end read as zero: no clamps, no branches, and no
-  // wait on the loads before the tile being computed needs them.  Every wave
-  // fetches the scales of key `lane` (loading them on the storing waves only put
-  // the staging registers in scratch memory); wave 0 stores the K ones, wave 1 the V ones.
+  // staging registers.  (Through registers, the scales cost 4.5% of the kernel's time and five
+  // registers held across the tile; a byte-sized load into LDS writes its byte zero-extended to a
+  // 4-byte word per lane, measured, so the V scales land one per word.)
   const int KSB = D / 32;   // bytes per K ROW32 scale word
-  using Scales = ScaleStage<D, BN>;
   // lane l of a DMA instruction fills bytes 16 l .. 16 l + 15 of its 1 KB block (measured)
   const int kend = CAUSAL ? min(L, qbase + BM) : L;   // keys this workgroup visits
   const int ntiles = (kend + BN - 1) / BN;
@@ -238,7 +233,9 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
                                                off, 0, 0, 0);
     }
   };
-  auto load_scales = [&](Scales& st) {
+  // the tile's scales by DMA: per 64-key half one dword (K) and ND byte (V) instructions, spread
+  // over the waves
+  auto dma_scales = [&](uint32_t* dKs, uint32_t (*dVs)[BN]) {
     const int rows = min(BN, L - nt.t * BN);
     const __amdgpu_buffer_rsrc_t rks = buffer_rsrc(nt.ks, (rows - 1) * a.H * KSB + KSB);
     const int nblk = (rows + 31) / 32;
@@ -246,24 +243,18 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
 #pragma unroll
     for (int hh = 0; hh < KH; ++hh) {
       const int kk = 64 * hh + lane;   // key of this lane in the tile
-      st.ks[hh] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(rks, kk * a.H * KSB, 0, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b16(rks, kk * a.H * KSB, 0, 0);
-      const int voff = (kk >> 5) * a.H * D + (kk & 31);
 #pragma unroll
-      for (int dc = 0; dc < ND; ++dc) st.vb[hh][dc] = __builtin_amdgcn_raw_buffer_load_b8(rvs, voff + 32 * dc, 0, 0);
-    }
-  };
-  auto store_scales = [&](int buf, const Scales& st) {
-    if (w == 0) {
-#pragma unroll
-      for (int hh = 0; hh < KH; ++hh) sKs[buf][64 * hh + lane] = st.ks[hh];
-    } else if (w == 1) {
-#pragma unroll
-      for (int hh = 0; hh < KH; ++hh) {
-        uint32_t vs = 0;
-#pragma unroll
-        for (int dc = 0; dc < ND; ++dc) vs |= st.vb[hh][dc] << (8 * dc);
-        sVs[buf][64 * hh + lane] = vs;
+      for (int j = 0; j <= ND; ++j) {
+        if (((1 + ND) * hh + j) % NW != w) continue;
+        if (j == 0) {
+          auto* dst = (__attribute__((address_space(3))) void*)(dKs + 64 * hh);
+          if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, dst, 4, kk * a.H * KSB, 0, 0, 0);
+          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, dst, 2, kk * a.H * KSB, 0, 0, 0);
+        } else {
+          const int dc = j - 1;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, (__attribute__((address_space(3))) void*)(dVs[dc] + 64 * hh),
+                                                   1, (kk >> 5) * a.H * D + (kk & 31) + 32 * dc, 0, 0, 0);
+        }
       }
     }
   };
@@ -329,13 +320,15 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
     if (compute) {
       const uint8_t* sKc = cur ? sK1 : sK0;
       const uint8_t* sVc = cur ? sV1 : sV0;
+      const uint32_t* sKsc = cur ? sKs1 : sKs0;
+      const uint32_t (*sVsc)[BN] = cur ? sVs1 : sVs0;
       // ---- S^T = K Q^T : st[kb] element i holds key k0 + 32 kb + 16g + i (K rows in korder), query qi
       v16f st[KB];
       uint32_t ksc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const uint8_t* kt = sKc + kb * 32 * KRS;
-        ksc[kb] = sKs[cur][kb * 32 + korder(n)] >> (8 * g);
+        ksc[kb] = sKsc[kb * 32 + korder(n)] >> (8 * g);
         v16f acc = v16f{};
         acc = mfma32<0, 0, QF>(qk_operand_at<QF>(kt, kofs[0][0], kofs[0][1]), qa[0], acc, ksc[kb], qsc);
         if constexpr (NC > 1)
@@ -441,7 +434,9 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
 #pragma unroll
           for (int q = 0; q < 4; ++q) pb[4 * b2 + q] = dw[2 * hh + b2][q];
         const int psc = g ? kc[2 * hh + 1] : kc[2 * hh];
-        const uint32_t vsc = sVs[cur][64 * hh + lane];
+        uint32_t vsc = 0;
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) vsc |= sVsc[dc][64 * hh + lane] << (8 * dc);
 #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
           // rows vrow, +8, +32, +40 share vrow's swizzle; chunk 2 dc + (G & 1), half i16 & 1
@@ -463,28 +458,20 @@ __global__ __launch_bounds__(NW * 64, (fwd_three_waves<D, CAUSAL, OUT_BF16, QF>(
       hook();
     }
   };
-  {
-    Scales s0;
-    load_scales(s0);
-    dma_tile(sK0, sV0);
-    advance();
-    store_scales(0, s0);
-  }
+  dma_scales(sKs0, sVs0);
+  dma_tile(sK0, sV0);
+  advance();
   __syncthreads();
   // the next tile's DMA and scale loads are in flight while this one is computed (past the last
   // tile the last one is fetched again into the free buffer, which keeps the loop free of branches
   // around them); two tiles per iteration so each buffer is named at compile time
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    Scales s1;
-    tile_body(t, 0, [&]() { load_scales(s1); dma_tile(sK1, sV1); });
+    tile_body(t, 0, [&]() { dma_scales(sKs1, sVs1); dma_tile(sK1, sV1); });
     advance();
-    store_scales(1, s1);
     __syncthreads();
-    Scales s2;
-    tile_body(t + 1, 1, [&]() { load_scales(s2); dma_tile(sK0, sV0); });
+    tile_body(t + 1, 1, [&]() { dma_scales(sKs0, sVs0); dma_tile(sK0, sV0); });
     advance();
-    store_scales(0, s2);
     __syncthreads();
   }
   if (t < ntiles) tile_body(t, 0, [&]() {});
