@@ -91,6 +91,46 @@ MX_DEV v8i tr_operand_swz64(const uint8_t* rows, int chunk0, int lane) {
   return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
+// The same four transpose reads from a lane's first row address p, the rows 8, 32 and 40 further
+// down at byte offsets O8, O32, O40 (tiles whose rows are not equally spaced).
+template <int O8, int O32, int O40>
+MX_DEV v8i tr_operand_rows(const uint8_t* p) {
+  v2i r0 = tr8(p), r1 = tr8(p + O8), r2 = tr8(p + O32), r3 = tr8(p + O40);
+  return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Paired-row layouts of the E4M3 K, Q and dO tiles at D = 128: rows 2j and 2j + 1 adjacent, two
+// spare 16-byte slots after each pair (the 144-byte average of a padded row), and one more slot
+// shifting every other 8-row (K) or 16-row (Q, dO) group by 16 bytes.  A transpose read pass
+// (8 consecutive rows, 32 bytes each) then covers all 64 banks once, and so does a row read pass
+// (16 lanes, 16 bytes each) over the rows the lanes read: 16 consecutive keys of K, or the 16
+// permuted query rows {0..7, 16..23} (and {8..15, 24..31}) of Q and dO.  With 144-byte rows the
+// transpose reads and the permuted row reads hit bank pairs twice (2-way conflicts).  Slot of row
+// r from the tile start:
+MX_DEV constexpr int krow_slot(int r) { return 8 * r + 2 * (r >> 1) + ((r >> 3) & 1); }
+MX_DEV constexpr int qrow_slot(int r) { return 8 * r + 2 * (r >> 1) + ((r >> 4) & 1); }
+// rows r, r + 8, r + 32, r + 40 for the transpose reads' first rows r (r % 16 < 8)
+static_assert(krow_slot(8) - krow_slot(0) == 73 && krow_slot(24) - krow_slot(16) == 73 && krow_slot(32) == 288 &&
+              krow_slot(47) - krow_slot(7) == 361 && krow_slot(64) == 576, "K row slots");
+static_assert(qrow_slot(8) - qrow_slot(0) == 72 && qrow_slot(31) - qrow_slot(23) == 72 && qrow_slot(32) == 288 &&
+              qrow_slot(63) - qrow_slot(23) == 360 && qrow_slot(64) == 576, "Q row slots");
+
+// The E4M3 dS code tile [key][query]: 64-byte rows with 32 spare bytes after every fourth, so
+// row r starts at 64 r + 32 (r >> 2).  A transpose read pass (8 consecutive rows, 32 bytes of
+// each) then covers all 64 banks once (80-byte rows: 1.80 ns per read, a conflict-free pass 1.34),
+// and every address of the tile stays a lane offset plus constants.
+constexpr int kDsGroupBytes = 4 * 64 + 32;
+MX_DEV constexpr int ds_row(int r) { return 64 * r + 32 * (r >> 2); }
+
+// 64-deep operand whose K index runs down rows {0..15} and 32 + {0..15} of such a tile from row
+// 0 of `base` (a multiple of 8), lane column `col0 + lane % 32`: four transpose reads.
+MX_DEV v8i tr_operand_ds(const uint8_t* base, int col0, int lane) {
+  const int G = lane >> 4, i16 = lane & 15;
+  const uint8_t* p = base + ds_row(16 * (G >> 1) + (i16 >> 1)) + col0 + 16 * (G & 1) + 8 * (i16 & 1);
+  v2i r0 = tr8(p), r1 = tr8(p + ds_row(8)), r2 = tr8(p + ds_row(32)), r3 = tr8(p + ds_row(40));
+  return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
 MX_DEV uint32_t ld_scale_word(const uint8_t* p, int nbytes) {
   return nbytes == 4 ? *(const uint32_t*)p : *(const uint16_t*)p;
 }
@@ -213,14 +253,18 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   constexpr int NC = D / 64;    // 64-feature chunks of the S / dP contraction
   constexpr int ND = D / 32;    // 32-feature chunks of dK, dV, dQ
   constexpr int NB = D / 32;    // scale bytes per SQ32 / ROW32 scale word
-  constexpr int KST = D + 16;   // LDS row stride of K, V, Q, dO tiles
-  constexpr int SST = BQ + 16;  // LDS row stride of the dS code tile [key][query]
+  constexpr int KST = D + 16;   // LDS row stride of the V tile, and of K, Q, dO where not paired (below)
   constexpr int NT = NW * 64;
   constexpr int SLQ = KST / 16;                 // 16-byte slots per padded Q / dO row
   constexpr int NBQ = BQ * KST / 1024;          // 1 KB DMA blocks per tile (one wave instruction each)
   static_assert(BQ * KST % 1024 == 0, "tiles must be whole DMA blocks");
+  constexpr bool PAIRED = !SMALL && D == 128;   // paired-row K, Q, dO tiles (krow_slot, qrow_slot)
+  // byte offsets of rows 8, 32, 40 past a transpose read's first row
+  constexpr int KO8 = PAIRED ? 16 * 73 : 8 * KST, KO32 = 32 * (PAIRED ? 144 : KST), KO40 = PAIRED ? 16 * 361 : 40 * KST;
+  constexpr int QO8 = PAIRED ? 16 * 72 : 8 * KST, QO32 = 32 * (PAIRED ? 144 : KST), QO40 = PAIRED ? 16 * 360 : 40 * KST;
   constexpr int VST = SMALL ? D : KST;          // V row stride (small formats: chunk j of row r in slot j ^ (r & 7))
-  constexpr int DST = SMALL ? BQ : SST;         // dS row stride (small formats: chunk j in slot j ^ (r & 3))
+  constexpr int DST = BQ;                       // small formats: dS row stride (chunk j in slot j ^ (r & 3))
+  constexpr int DSB = SMALL ? BN * DST : BN / 4 * kDsGroupBytes;   // dS code tile bytes
   constexpr int KRS = W == 6 ? 104 : KRB;       // small formats: LDS row stride of the packed K rows
   constexpr int QRS = KRB;                      // small formats: LDS row stride of the packed Q rows
   constexpr int KROW = SMALL ? BN * KRS : BN * KST;   // row-major K tile bytes
@@ -234,10 +278,11 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[KROW + KCOL];
   __shared__ __attribute__((aligned(16))) uint8_t sV[BN * VST];
   // Q^ and dO^ step tiles arrive by 16-byte DMA (buffer loads straight into LDS): a padded row
-  // is KST / 16 slots, the last one a copy of the row's last chunk (never read)
+  // is KST / 16 slots, the last one a copy of the row's last chunk (never read); in the paired layout
+  // (E4M3, D = 128) the spare slots hold copies too
   __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][QROW + QCOL];
   __shared__ __attribute__((aligned(1024))) uint8_t sDO[2][BQ * KST];
-  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][BN * DST];   // [step parity]
+  __shared__ __attribute__((aligned(16))) uint8_t sDS[2][DSB];   // [step parity]
   __shared__ uint32_t sKs[NW];                 // K SQ32 scale word (bytes = feature blocks) per key block
   __shared__ uint32_t sVs[BN];                 // V ROW32 scale word per key
   __shared__ uint32_t sQs[2][2], sDOs[2][2];   // [buffer][query block]
@@ -275,7 +320,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         kv = *(const uint4*)(a.k + off);
         vv = *(const uint4*)(a.v + off);
       }
-      *(uint4*)(sK + r * KST + cx * 16) = kv;
+      *(uint4*)(sK + (PAIRED ? 16 * krow_slot(r) : r * KST) + cx * 16) = kv;
       *(uint4*)(sV + r * KST + cx * 16) = vv;
     }
   } else {
@@ -340,8 +385,22 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         if (w < DW && (2 * NBQ % DW == 0 || blk < 2 * NBQ)) {
           const bool isq = blk < NBQ;
           const int b = isq ? blk : blk - NBQ;
-          const int ch = b * 64 + lane, r = ch / SLQ;
-          const int off = r * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+          const int ch = b * 64 + lane;   // 16-byte slot of the tile
+          int r, c;
+          if constexpr (PAIRED) {
+            // the row and chunk of slot ch (qrow_slot inverted: 32-row halves of 288 slots, rows 16-31
+            // of a half from slot 145, pairs of rows 18 slots apart); spare slots load a copy
+            const int hf = ch / 288, s1 = ch - 288 * hf;
+            const int up = s1 >= 144 ? 1 : 0;
+            const int u = max(s1 - 145 * up, 0);
+            const int pr = u / 18, o = min(u - 18 * pr, 15);
+            r = 32 * hf + 16 * up + 2 * pr + (o >> 3);
+            c = o & 7;
+          } else {
+            r = ch / SLQ;
+            c = min(ch % SLQ, D / 16 - 1);
+          }
+          const int off = r * (int)rowH + 16 * c;
           uint8_t* dst = (isq ? sQ[buf] : sDO[buf]) + 1024 * b;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(isq ? rq : rdo, (__attribute__((address_space(3))) void*)dst, 16,
                                                    off, 0, 0, 0);
@@ -432,6 +491,11 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   }
   __syncthreads();
 
+  // lane offsets of the transpose reads' first rows (row 16 (G / 2) + i16 / 2, bytes 16 (G & 1) + 8 (i16 & 1))
+  const int trl = 16 * (lane >> 5) + ((lane & 15) >> 1), trb = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  const int trk = (PAIRED ? 16 * krow_slot(trl) : trl * KST) + trb;
+  const int trq = (PAIRED ? 16 * qrow_slot(trl) : trl * KST) + trb;
+
   // ---- C. dQ tile (query block t, feature chunk dc) = (w / ND, w % ND) over the 256 keys of the step
   // at q0, from dS buffer bufc, into the head-major fp16 accumulator [H, T, D] (a head's rows are
   // contiguous).  Output element e of lane l: query 32t + 8(e/4) + 4g + e%4, feature 32 dc + l%32.
@@ -450,8 +514,9 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           sscale[kk] = sDSs[bufc][t][2 * kk + g];
           kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
           if constexpr (!SMALL) {
-            sbv[kk] = tr_operand(sDS[bufc] + (64 * kk) * SST + 32 * t, SST, lane);   // rows: queries, K: keys
-            kav[kk] = tr_operand(sK + (64 * kk) * KST + 32 * dc, KST, lane);         // columns: features
+            sbv[kk] = tr_operand_ds(sDS[bufc] + ds_row(64 * kk), 32 * t, lane);   // rows: queries, K: keys
+            kav[kk] = tr_operand_rows<KO8, KO32, KO40>(sK + (PAIRED ? 16 * krow_slot(64 * kk) : 64 * kk * KST) + 32 * dc +
+                                                       trk);   // columns: features
           } else {
             sbv[kk] = tr_operand_swz64(sDS[bufc] + (64 * kk) * DST, 2 * t, lane);
             // column-packed K: key block 2 kk + g of feature 32 dc + n
@@ -518,7 +583,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       int kpc[2], ksc2[2];
       const bool live = kw0 < L && !(CAUSAL && kw0 > q0 + BQ - 1);   // a key of the block sees a query
       if (live) {
-        const uint8_t* kr = sK + (32 * w + n) * KST + 16 * g;
+        const uint8_t* kr = sK + (PAIRED ? 16 * krow_slot(32 * w + n) : (32 * w + n) * KST) + 16 * g;
         const uint8_t* vr = sV + (32 * w + n) * KST + 16 * g;
         // small formats: packed K row of this lane's key (block 2 c + g at (2 c + g) BB); swizzled V row
         const uint8_t* krs = sK + (32 * w + n) * KRS + g * BB;
@@ -546,8 +611,9 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           const uint32_t qsa = sQs[buf][t] >> (8 * g), dsa = sDOs[buf][t] >> (8 * g);
           // computed for every block (rows past either end are zero, so the values are
           // finite); the mask zeroes p and dS where nothing is visible
-          const uint8_t* qp = sQb + (32 * t + qrow) * KST + 16 * g;
-          const uint8_t* op = sDOb + (32 * t + qrow) * KST + 16 * g;
+          const int qro = PAIRED ? 16 * (qrow_slot(qrow) + 288 * t) : (32 * t + qrow) * KST;
+          const uint8_t* qp = sQb + qro + 16 * g;
+          const uint8_t* op = sDOb + qro + 16 * g;
           v16f st, dpt;
           if constexpr (!SMALL) {
             st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
@@ -643,7 +709,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
             sB[4 * t + q] = sw[q];
           }
           if constexpr (!SMALL)
-            *(uint4*)(sDS[buf] + (32 * w + n) * SST + 32 * t + 16 * g) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+            *(uint4*)(sDS[buf] + ds_row(32 * w + n) + 32 * t + 16 * g) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
           else
             *(uint4*)(sDS[buf] + (32 * w + n) * DST + 16 * ((2 * t + g) ^ (n & 3))) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
           if (lane == 0) sDSs[buf][t][w] = ks2;
@@ -657,11 +723,11 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
   #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
-          const v8i oa = tr_operand(sDOb + 32 * dc, KST, lane);
+          const v8i oa = tr_operand_rows<QO8, QO32, QO40>(sDOb + 32 * dc + trq);
           // Q^T: the 64 queries of feature 32 dc + n; small formats from the column-packed blocks
           // (lane half g: query block g)
           const v8i qa = SMALL ? small_operand<W>(sQb + QROW + (g * D + 32 * dc + n) * BB)
-                               : tr_operand(sQb + 32 * dc, KST, lane);
+                               : tr_operand_rows<QO8, QO32, QO40>(sQb + 32 * dc + trq);
           if (dc == 0) { dvt[0] = mfma32b<0, 0>(oa, pB, dvt[0], dow, pscale); dkt[0] = mfma32f<QF, 0, 0, 0>(qa, sB, dkt[0], qw, sscale); }
           if (dc == 1) { dvt[1] = mfma32b<1, 0>(oa, pB, dvt[1], dow, pscale); dkt[1] = mfma32f<QF, 0, 1, 0>(qa, sB, dkt[1], qw, sscale); }
           if constexpr (ND > 2) {
@@ -674,7 +740,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         // every key of the block comes after every query of the step: dS is zero
         const uint4 z = make_uint4(0, 0, 0, 0);
         if constexpr (!SMALL) {
-          uint8_t* rowp = sDS[buf] + (32 * w + (lane >> 1)) * SST + 32 * (lane & 1);
+          uint8_t* rowp = sDS[buf] + ds_row(32 * w + (lane >> 1)) + 32 * (lane & 1);
           *(uint4*)rowp = z;
           *(uint4*)(rowp + 16) = z;
         } else {

@@ -18,6 +18,21 @@ B128, B64, TR8 = 0, 1, 2
 SIZE = {B128: 16, B64: 8, TR8: 8}
 
 
+def qrow(n):
+    """Query row that lane n feeds the backward's E4M3 S and dP products (rows of a 32-row block)."""
+    return (((n >> 2) & 1) << 4) | (((n >> 3) & 3) << 2) | (n & 3)
+
+
+def kslot(r):
+    """16-byte slot of row r in the backward's paired-row E4M3 K tile."""
+    return 8 * r + 2 * (r >> 1) + ((r >> 3) & 1)
+
+
+def qslot(r):
+    """16-byte slot of row r in the backward's paired-row E4M3 Q and dO tiles."""
+    return 8 * r + 2 * (r >> 1) + ((r >> 4) & 1)
+
+
 def row_pattern(f):
     return [f(l % 32, l // 32) for l in range(64)]
 
@@ -32,7 +47,10 @@ def tr_pattern(f):
 
 PATTERNS = [
     (B128, "linear 16 B per lane", [16 * l for l in range(64)]),
-    (B128, "rows 144 B (backward E4M3 Q, dO, K, V), chunk g", row_pattern(lambda n, g: 144 * n + 16 * g)),
+    (B128, "rows 144 B (backward E4M3 V), chunk g", row_pattern(lambda n, g: 144 * n + 16 * g)),
+    (B128, "rows 144 B, permuted query rows qrow(n)", row_pattern(lambda n, g: 144 * qrow(n) + 16 * g)),
+    (B128, "paired rows kslot(n) (backward E4M3 K)", row_pattern(lambda n, g: 16 * kslot(n) + 16 * g)),
+    (B128, "paired rows qslot(qrow(n)) (backward E4M3 Q, dO)", row_pattern(lambda n, g: 16 * qslot(qrow(n)) + 16 * g)),
     (B128, "rows 128 B, chunk g in slot g ^ (n & 7)", row_pattern(lambda n, g: 128 * n + 16 * (g ^ (n & 7)))),
     (B128, "rows 128 B, chunk g in slot g ^ ((n >> 1) & 7) (forward E4M3 K)",
      row_pattern(lambda n, g: 128 * n + 16 * (g ^ ((n >> 1) & 7)))),
@@ -51,8 +69,12 @@ PATTERNS = [
     (B64, "column blocks 24 B apart (backward E2M3 column-packed Q, K)",
      row_pattern(lambda n, g: 24 * (n + 32 * g))),
     (TR8, "rows 128 B unswizzled", tr_pattern(lambda r, G, i: 128 * r + 16 * (G & 1) + 8 * (i & 1))),
-    (TR8, "rows 144 B (backward E4M3 transposed Q, dO, K)", tr_pattern(lambda r, G, i: 144 * r + 16 * (G & 1) + 8 * (i & 1))),
-    (TR8, "rows 80 B (backward E4M3 dS)", tr_pattern(lambda r, G, i: 80 * r + 16 * (G & 1) + 8 * (i & 1))),
+    (TR8, "rows 144 B", tr_pattern(lambda r, G, i: 144 * r + 16 * (G & 1) + 8 * (i & 1))),
+    (TR8, "paired rows kslot(r) (backward E4M3 K)", tr_pattern(lambda r, G, i: 16 * kslot(r) + 16 * (G & 1) + 8 * (i & 1))),
+    (TR8, "paired rows qslot(r) (backward E4M3 Q, dO)", tr_pattern(lambda r, G, i: 16 * qslot(r) + 16 * (G & 1) + 8 * (i & 1))),
+    (TR8, "rows 80 B", tr_pattern(lambda r, G, i: 80 * r + 16 * (G & 1) + 8 * (i & 1))),
+    (TR8, "rows 64 B, 32 spare bytes after every fourth (backward E4M3 dS)",
+     tr_pattern(lambda r, G, i: 64 * r + 32 * (r >> 2) + 16 * (G & 1) + 8 * (i & 1))),
     (TR8, "rows 128 B, slot ^ (r & 7) (forward V)",
      tr_pattern(lambda r, G, i: 128 * r + 16 * ((G & 1) ^ (r & 7)) + 8 * (i & 1))),
     (TR8, "rows 128 B, slot ^ ((r >> 1) & 7)",
