@@ -71,18 +71,12 @@ MX_DEV v2i tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3)))*)(p));
 }
 
-// 64-deep operand whose K index runs down rows `row0 + {0..15}` (block 0) and
-// `row0 + 32 + {0..15}` (block 1) of a row-major byte tile, lane column
-// `col0 + lane % 32`: four transpose reads.
-MX_DEV v8i tr_operand(const uint8_t* base, int stride, int lane) {
-  const int G = lane >> 4, i16 = lane & 15;
-  const uint8_t* p = base + (16 * (G >> 1) + (i16 >> 1)) * stride + 16 * (G & 1) + 8 * (i16 & 1);
-  v2i r0 = tr8(p), r1 = tr8(p + 8 * stride), r2 = tr8(p + 32 * stride), r3 = tr8(p + 40 * stride);
-  return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-}
-
-// tr_operand over an unpadded 64-byte-row tile whose 16-byte chunks sit XOR-swizzled by (row & 3);
-// chunk0 = the operand's first chunk (2 t for query block t).  Rows r, r+8, r+32, r+40 share r & 3.
+// A 64-deep operand whose K index runs down rows {0..15} (block 0) and 32 + {0..15} (block 1) of
+// a byte tile, lane column lane % 32 of the chosen 32 columns: four transpose reads, lane (G, i16) =
+// (lane / 16, lane % 16) reading 8 bytes of row 16 (G / 2) + i16 / 2 (+ 8, 32, 40).
+//
+// Over an unpadded 64-byte-row tile whose 16-byte chunks sit XOR-swizzled by (row & 3); chunk0 =
+// the operand's first chunk (2 t for query block t).  Rows r, r+8, r+32, r+40 share r & 3.
 MX_DEV v8i tr_operand_swz64(const uint8_t* rows, int chunk0, int lane) {
   const int G = lane >> 4, i16 = lane & 15;
   const int r = 16 * (G >> 1) + (i16 >> 1);
@@ -91,8 +85,9 @@ MX_DEV v8i tr_operand_swz64(const uint8_t* rows, int chunk0, int lane) {
   return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
-// The same four transpose reads from a lane's first row address p, the rows 8, 32 and 40 further
-// down at byte offsets O8, O32, O40 (tiles whose rows are not equally spaced).
+// The same four transpose reads from a lane's first row address p (row 16 (G / 2) + i16 / 2 of the
+// operand, bytes 16 (G & 1) + 8 (i16 & 1) of its 32 columns), the rows 8, 32 and 40 further down at
+// byte offsets O8, O32, O40 (O8 = 8 x stride etc. for equally spaced rows).
 template <int O8, int O32, int O40>
 MX_DEV v8i tr_operand_rows(const uint8_t* p) {
   v2i r0 = tr8(p), r1 = tr8(p + O8), r2 = tr8(p + O32), r3 = tr8(p + O40);
@@ -137,20 +132,9 @@ MX_DEV uint32_t ld_scale_word(const uint8_t* p, int nbytes) {
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
-MX_DEV void atomic_add_h2(_Float16* p, float a, float b) {
-  h2v v = {(_Float16)a, (_Float16)b};
-  __builtin_amdgcn_global_atomic_fadd_v2f16((h2v __attribute__((address_space(1)))*)(p), v);
-}
-
-// Packed fp16 atomic add through a buffer resource: a 32-bit byte offset from
-// a scalar base (buffer_atomic_pk_add_f16).
-MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float a, float b) {
-  h2v v = {(_Float16)a, (_Float16)b};
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(v, r, (int)byte_off, 0, 0);
-}
-
-// The same with a wave-uniform part of the offset in an SGPR (soffset), so
-// per-element constants cost no vector registers.
+// Packed fp16 atomic add through a buffer resource (buffer_atomic_pk_add_f16): a 32-bit byte
+// offset from a scalar base, its wave-uniform part in an SGPR (soffset), so per-element constants
+// cost no vector registers.
 MX_DEV void atomic_add_h2_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t uniform_off, float a, float b) {
   h2v v = {(_Float16)a, (_Float16)b};
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(v, r, (int)byte_off, (int)__builtin_amdgcn_readfirstlane(uniform_off), 0);
