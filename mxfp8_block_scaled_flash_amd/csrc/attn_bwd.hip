@@ -110,7 +110,7 @@ static_assert(krow_slot(8) - krow_slot(0) == 73 && krow_slot(24) - krow_slot(16)
 static_assert(qrow_slot(8) - qrow_slot(0) == 72 && qrow_slot(31) - qrow_slot(23) == 72 && qrow_slot(32) == 288 &&
               qrow_slot(63) - qrow_slot(23) == 360 && qrow_slot(64) == 576, "Q row slots");
 
-// The E4M3 dS code tile [key][query]: 64-byte rows with 32 spare bytes after every fourth, so
+// The dS code tile [key][query] (E4M3 and MXFP4 Q, K): 64-byte rows with 32 spare bytes after every fourth, so
 // row r starts at 64 r + 32 (r >> 2).  A transpose read pass (8 consecutive rows, 32 bytes of
 // each) then covers all 64 banks once (80-byte rows: 1.80 ns per read, a conflict-free pass 1.34),
 // and every address of the tile stays a lane offset plus constants.
@@ -220,8 +220,8 @@ template <int D, bool CAUSAL, int QF>
 __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   // QF: element format of Q and K (0: MXFP8 E4M3; 2, 3: MXFP6 E2M3, E3M2; 4: MXFP4 E2M1).  In the small
   // formats (D = 128 only) Q and K arrive row-packed (S = Q^ K^T) and column-packed (dK = dS^T Q^ and
-  // dQ = dS^ K^ contract over tokens), and the V and dS tiles drop their padding for XOR-swizzled
-  // chunks so the larger tiles fit in LDS.  MXFP6 K rows (96 bytes, read as three 8-byte pieces, 32
+  // dQ = dS^ K^ contract over tokens), and the V tile drops its padding for XOR-swizzled chunks so
+  // the larger tiles fit in LDS (so does MXFP6's dS tile; MXFP4's keeps the E4M3 layout).  MXFP6 K rows (96 bytes, read as three 8-byte pieces, 32
   // lanes a pass) sit 104 bytes apart, stored through registers, so a pass hits distinct banks (at
   // 96 bytes lanes share bank pairs, 2.4x the time per read; the backward took 7% longer); the DMA'd MXFP6 Q rows
   // stay unpadded (a 16-byte spare slot does not fit in the LDS), as do the 64-byte MXFP4 rows (80-byte
@@ -246,9 +246,18 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   // byte offsets of rows 8, 32, 40 past a transpose read's first row
   constexpr int KO8 = PAIRED ? 16 * 73 : 8 * KST, KO32 = 32 * (PAIRED ? 144 : KST), KO40 = PAIRED ? 16 * 361 : 40 * KST;
   constexpr int QO8 = PAIRED ? 16 * 72 : 8 * KST, QO32 = 32 * (PAIRED ? 144 : KST), QO40 = PAIRED ? 16 * 360 : 40 * KST;
+  // the dO tile at D = 128 is paired too: like Q for E4M3 (permuted rows), like K (krow_slot) for
+  // MXFP6, whose lanes read its rows in natural order (11.5 -> 11.1 ms); MXFP4 keeps the padded
+  // rows (paired: 9.35 -> 9.47 ms, its spills 7 -> 11)
+  constexpr bool DOPAIR = D == 128 && (!SMALL || W == 6);
+  constexpr int DO8 = !DOPAIR ? QO8 : SMALL ? 16 * 73 : 16 * 72, DO32 = 32 * (DOPAIR ? 144 : KST),
+                DO40 = !DOPAIR ? QO40 : SMALL ? 16 * 361 : 16 * 360;
   constexpr int VST = SMALL ? D : KST;          // V row stride (small formats: chunk j of row r in slot j ^ (r & 7))
-  constexpr int DST = BQ;                       // small formats: dS row stride (chunk j in slot j ^ (r & 3))
-  constexpr int DSB = SMALL ? BN * DST : BN / 4 * kDsGroupBytes;   // dS code tile bytes
+  // dS code tile: 64-byte rows with a spare half row after every fourth (ds_row), or, where that
+  // does not fit in the LDS (MXFP6), unpadded rows with chunk j in slot j ^ (r & 3)
+  constexpr bool DSPAD = !(SMALL && W == 6);
+  constexpr int DST = BQ;
+  constexpr int DSB = DSPAD ? BN / 4 * kDsGroupBytes : BN * DST;   // dS code tile bytes
   constexpr int KRS = W == 6 ? 104 : KRB;       // small formats: LDS row stride of the packed K rows
   constexpr int QRS = KRB;                      // small formats: LDS row stride of the packed Q rows
   constexpr int KROW = SMALL ? BN * KRS : BN * KST;   // row-major K tile bytes
@@ -418,8 +427,17 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
             dst = sQ[buf] + QROW + 1024 * bb;
           } else {
             const int b = blk - NBQR - NBQC;
-            const int ch = b * 64 + lane, rr = ch / SLQ;
-            off = rr * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+            const int ch = b * 64 + lane;
+            if constexpr (DOPAIR) {
+              // the row and chunk of slot ch of the paired dO tile (krow_slot inverted: groups of 8
+              // rows, 72 slots each, odd groups from one slot later; pairs of rows 18 slots apart)
+              const int gk = ch / 72;
+              const int u = max(ch - 72 * gk - (gk & 1), 0);
+              const int pr = u / 18, o = min(u - 18 * pr, 15);
+              off = (8 * gk + 2 * pr + (o >> 3)) * (int)rowH + 16 * (o & 7);
+            } else {
+              off = (ch / SLQ) * (int)rowH + 16 * min(ch % SLQ, D / 16 - 1);
+            }
             dst = sDO[buf] + 1024 * b;
           }
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -479,6 +497,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
   const int trl = 16 * (lane >> 5) + ((lane & 15) >> 1), trb = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
   const int trk = (PAIRED ? 16 * krow_slot(trl) : trl * KST) + trb;
   const int trq = (PAIRED ? 16 * qrow_slot(trl) : trl * KST) + trb;
+  const int trdo = (DOPAIR ? 16 * (SMALL ? krow_slot(trl) : qrow_slot(trl)) : trl * KST) + trb;
 
   // ---- C. dQ tile (query block t, feature chunk dc) = (w / ND, w % ND) over the 256 keys of the step
   // at q0, from dS buffer bufc, into the head-major fp16 accumulator [H, T, D] (a head's rows are
@@ -497,12 +516,14 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         for (int kk = 0; kk < BN / 64; ++kk) {
           sscale[kk] = sDSs[bufc][t][2 * kk + g];
           kscale[kk] = (int)((sKs[2 * kk + g] >> (8 * dc)) & 0xFFu);
-          if constexpr (!SMALL) {
+          if constexpr (DSPAD)
             sbv[kk] = tr_operand_ds(sDS[bufc] + ds_row(64 * kk), 32 * t, lane);   // rows: queries, K: keys
+          else
+            sbv[kk] = tr_operand_swz64(sDS[bufc] + (64 * kk) * DST, 2 * t, lane);
+          if constexpr (!SMALL) {
             kav[kk] = tr_operand_rows<KO8, KO32, KO40>(sK + (PAIRED ? 16 * krow_slot(64 * kk) : 64 * kk * KST) + 32 * dc +
                                                        trk);   // columns: features
           } else {
-            sbv[kk] = tr_operand_swz64(sDS[bufc] + (64 * kk) * DST, 2 * t, lane);
             // column-packed K: key block 2 kk + g of feature 32 dc + n
             kav[kk] = small_operand<W>(sK + KROW + ((2 * kk + g) * D + 32 * dc + n) * BB);
           }
@@ -596,8 +617,9 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
           // computed for every block (rows past either end are zero, so the values are
           // finite); the mask zeroes p and dS where nothing is visible
           const int qro = PAIRED ? 16 * (qrow_slot(qrow) + 288 * t) : (32 * t + qrow) * KST;
+          const int doro = DOPAIR ? 16 * ((SMALL ? krow_slot(qrow) : qrow_slot(qrow)) + 288 * t) : qro;
           const uint8_t* qp = sQb + qro + 16 * g;
-          const uint8_t* op = sDOb + qro + 16 * g;
+          const uint8_t* op = sDOb + doro + 16 * g;
           v16f st, dpt;
           if constexpr (!SMALL) {
             st = mfma32b<0, 0>(pack8b(*(const uint4*)qp, *(const uint4*)(qp + 32)),
@@ -665,13 +687,14 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
               pw[q] = cvt4_scaled_fp8(st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3], psc);
               sw[q] = cvt4_scaled_fp8(dpt[4 * q], dpt[4 * q + 1], dpt[4 * q + 2], dpt[4 * q + 3], ssc);
             } else {
-              // MXFP6 Q, K: through the builtins (the asm form raised this variant's spills from 40 to
-              // 113 registers, +28% time; it lowers the E4M3 and E2M1 ones, E2M1 -8%)
-              v2s z = __builtin_bit_cast(v2s, st[4 * q]);
+              // MXFP6 Q, K: through the builtins, each started from a zero word (the asm form raised this
+              // variant's spills from 40 to 113 registers, +28% time, and starting from a copy of the
+              // first input kept 40; the asm form lowers the E4M3 and E2M1 ones, E2M1 -8%, where the
+              // builtins spill more)
+              v2s z = {0, 0}, y = {0, 0};
               z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q], st[4 * q + 1], psc, false);
               z = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, st[4 * q + 2], st[4 * q + 3], psc, true);
               pw[q] = __builtin_bit_cast(uint32_t, z);
-              v2s y = __builtin_bit_cast(v2s, dpt[4 * q]);
               y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q], dpt[4 * q + 1], ssc, false);
               y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, dpt[4 * q + 2], dpt[4 * q + 3], ssc, true);
               sw[q] = __builtin_bit_cast(uint32_t, y);
@@ -692,7 +715,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
             pB[4 * t + q] = pw[q];
             sB[4 * t + q] = sw[q];
           }
-          if constexpr (!SMALL)
+          if constexpr (DSPAD)
             *(uint4*)(sDS[buf] + ds_row(32 * w + n) + 32 * t + 16 * g) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
           else
             *(uint4*)(sDS[buf] + (32 * w + n) * DST + 16 * ((2 * t + g) ^ (n & 3))) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
@@ -707,7 +730,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
         const uint32_t dow = sDOs[buf][g], qw = sQs[buf][g];
   #pragma unroll
         for (int dc = 0; dc < ND; ++dc) {
-          const v8i oa = tr_operand_rows<QO8, QO32, QO40>(sDOb + 32 * dc + trq);
+          const v8i oa = tr_operand_rows<DO8, DO32, DO40>(sDOb + 32 * dc + trdo);
           // Q^T: the 64 queries of feature 32 dc + n; small formats from the column-packed blocks
           // (lane half g: query block g)
           const v8i qa = SMALL ? small_operand<W>(sQb + QROW + (g * D + 32 * dc + n) * BB)
@@ -723,7 +746,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kernel(BwdArgs a) {
       } else {
         // every key of the block comes after every query of the step: dS is zero
         const uint4 z = make_uint4(0, 0, 0, 0);
-        if constexpr (!SMALL) {
+        if constexpr (DSPAD) {
           uint8_t* rowp = sDS[buf] + ds_row(32 * w + (lane >> 1)) + 32 * (lane & 1);
           *(uint4*)rowp = z;
           *(uint4*)(rowp + 16) = z;
