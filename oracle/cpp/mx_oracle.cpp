@@ -53,6 +53,7 @@ double e4m3_value(uint8_t code) {
 uint8_t e4m3_code(double y) {
   const uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
   const double a = std::fabs(y);
+  if (std::isnan(a)) return sign | 0x7F;   // outside the quantizer's contract; the format's NaN code
   if (std::isinf(a)) return sign | 0x7E;
   if (a < std::ldexp(1.0, -6)) {   // subnormal binade: multiples of 2^-9 (8 x 2^-9 is the smallest normal)
     return sign | static_cast<uint8_t>(std::nearbyint(a * 512.0));
